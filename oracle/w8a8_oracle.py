@@ -1,0 +1,412 @@
+"""Plain CPU oracle of the W8A8 INT8 linear layer -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s ``cpu_baseline``
+leg may import this module. The HIP library shares no code with it.
+
+Written with numpy only, for clarity rather than speed. Sources, by page title:
+
+* [vLLM]    "vLLM INT8 W8A8 量化实战：用 llm-compressor 制作 8 位权重与 8 位激活的推理模型"
+* [SGLang]  "[SGLang] W4A8, W8A8, W4A4: 혼합 정밀도 양자화 스킴"
+* [Kunlun]  "MiniMax-M2.7 FP8 转昆仑芯 INT8" (README of minimax-m2-kunlun-INT8)
+
+Precision. Where a float decides an integer (a quantised code, a scale that
+feeds one) the step is done in IEEE binary32 with round-to-nearest-even, the
+precision the [Kunlun] conversion formulas name (``W_fp32``). Every such step
+is one numpy float32 op, so each result is the correctly rounded binary32
+value of that op. Integer sums are exact (int64, or float64 where every
+partial sum stays below 2**53). The one floating-point *output*, the
+dequantised bf16 result, is computed in float64 from the exact integer
+accumulator and then rounded once to bf16 (round-to-nearest-even).
+
+Readings of points the pages leave open (each is also listed in the design doc):
+
+* ``round`` is round-half-to-even (numpy ``rint``); the division by a scale is a
+  true IEEE division, never a multiply by a reciprocal.
+* Per-token symmetric activation quantisation applies the per-row absmax/127
+  rule of [Kunlun] 转换关系 to each token row; an all-zero row gives q=0, s=1
+  (the same page's all-zero-row rule).
+* Asymmetric activation quantisation is the textbook affine mapping onto
+  [-128, 127] with the range widened to contain 0: s=(hi-lo)/255,
+  zp=-128-rne(lo/s), q=clamp(rne(x/s)+zp). The pages only say that the zero
+  point exists, is stored as int8 and is used as an int32 "azp" ([vLLM] 4.2).
+* The zero point is subtracted: x ~ s*(q-zp), so the integer correction is
+  acc - zp*colsum(W) ([SGLang] 핵심 코드 분석 §4).
+* requantize-with-max-scale dequantises each partition with its own scale and
+  quantises again with the largest one ([SGLang] §7); range [-128, 127].
+
+Pins (``tests/test_oracle_*.py``, run with ``-m "not gpu"``): exact rational
+brute force of every rounding decision on small rows, the half-step error
+bound, the argmax/argmin mapping, sign and power-of-two symmetries, the
+all-zero-row rule, a pure-Python integer GEMM, the dequantise-then-matmul
+identity, the OCP E4M3FN decoding against torch's float8_e4m3fn and hand
+values, and hand-computed worked examples under ``tests/golden/``.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "bf16_bits_to_f32",
+    "f64_to_bf16_bits",
+    "quant_dyn_sym",
+    "quant_dyn_asym",
+    "quant_static",
+    "quantize_act",
+    "int_gemm",
+    "colsum",
+    "azp_adj_static",
+    "corrected_acc",
+    "epilogue_bf16",
+    "scaled_mm",
+    "requant_max",
+    "e4m3fn_table",
+    "fp8_block_to_int8",
+    "grouped_scaled_mm",
+    "linear_forward",
+    "FLAG_NAN_CODE",
+    "FLAG_BAD_SCALE",
+    "FLAG_NONFINITE",
+    "MODE_DYN_SYM",
+    "MODE_DYN_ASYM",
+    "MODE_STATIC_SYM",
+    "MODE_STATIC_ASYM",
+]
+
+MODE_DYN_SYM = 0
+MODE_DYN_ASYM = 1
+MODE_STATIC_SYM = 2
+MODE_STATIC_ASYM = 3
+
+FLAG_NAN_CODE = 1   # an FP8 NaN code (0x7F / 0xFF) in the weight
+FLAG_BAD_SCALE = 2  # a scale that is NaN, +-Inf or negative
+FLAG_NONFINITE = 4  # a dequantised value that overflowed binary32
+
+_F = np.float32
+
+
+# ---------------------------------------------------------------- bf16 I/O --
+
+def bf16_bits_to_f32(bits) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float32. Exact: bf16 is the top half of binary32."""
+    b = np.asarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def f64_to_bf16_bits(y) -> np.ndarray:
+    """Round float64 values once to bf16 (round-to-nearest-even) and return the bits.
+
+    bf16 has binary32's exponent range and 8 significant bits. For a finite y,
+    write |y| = m * 2**e with m in [0.5, 1); the nearest bf16 is
+    rint(m * 2**8) * 2**(e-8) in the normal range, and a multiple of 2**-133
+    (the smallest bf16 subnormal) below 2**-126. Beyond the largest finite bf16
+    the rounding overflows to infinity.
+    """
+    y = np.asarray(y, dtype=np.float64)
+    out = np.empty(y.shape, dtype=np.float64)
+    fin = np.isfinite(y)
+    m, e = np.frexp(np.where(fin, y, 0.0))
+    quantum_exp = np.maximum(e - 8, -133)
+    r = np.rint(np.ldexp(np.where(fin, y, 0.0), -quantum_exp))  # exact scaling, RNE
+    out[...] = np.ldexp(r, quantum_exp)
+    out[~fin] = y[~fin]
+    max_bf16 = float(np.ldexp(255.0, 127 - 7))  # (2 - 2**-7) * 2**127
+    over = fin & (np.abs(out) > max_bf16)
+    out[over] = np.copysign(np.inf, y[over])
+    # binary32 holds every bf16 value exactly, so the bits are its top half.
+    f32 = out.astype(np.float32)
+    return (f32.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+# ------------------------------------------------- activation quantisation --
+
+def quant_dyn_sym(x_bits):
+    """Dynamic per-token symmetric int8 quantisation of bf16 activations [M, K].
+
+    Follows the per-row absmax rule of [Kunlun] 转换关系, applied to token rows,
+    as used by the per-token quantiser of [SGLang] 핵심 코드 분석 §3:
+        s_t = max_k |x_tk| / 127,   q = clamp(round(x / s_t), -127, 127),
+    with an all-zero row giving q = 0 and s = 1 ([Kunlun] 转换关系).
+    Returns (q int8 [M,K], s float32 [M]).
+    """
+    x = bf16_bits_to_f32(x_bits)
+    a = np.max(np.abs(x), axis=1) if x.shape[1] else np.zeros(x.shape[0], _F)
+    s = np.where(a == 0, _F(1), a / _F(127)).astype(_F)
+    r = np.rint(x / s[:, None])
+    q = np.clip(r, -127, 127).astype(np.int8)
+    return q, s
+
+
+def quant_dyn_asym(x_bits):
+    """Dynamic per-token asymmetric int8 quantisation with a zero point.
+
+    The pages state that asymmetric input quantisation is supported and that the
+    zero point is an int8 used as int32 ([vLLM] 4.2; [SGLang] §3-§4); the
+    mapping itself is the affine one over [-128, 127] with [lo, hi] widened to
+    contain zero:
+        lo = min(0, min x), hi = max(0, max x), s = (hi - lo) / 255,
+        zp = clamp(-128 - round(lo / s), -128, 127),
+        q  = clamp(round(x / s) + zp, -128, 127).
+    Row all zero (hi == lo): s = 1, zp = 0, q = 0.
+    Returns (q int8 [M,K], s float32 [M], zp int32 [M]).
+    """
+    x = bf16_bits_to_f32(x_bits)
+    M, K = x.shape
+    if K:
+        lo = np.minimum(_F(0), np.min(x, axis=1)).astype(_F)
+        hi = np.maximum(_F(0), np.max(x, axis=1)).astype(_F)
+    else:
+        lo = np.zeros(M, _F)
+        hi = np.zeros(M, _F)
+    zero_row = hi == lo
+    rng = (hi - lo).astype(_F)
+    s = np.where(zero_row, _F(1), rng / _F(255)).astype(_F)
+    zp = -128 - np.rint(lo / s).astype(np.int64)
+    zp = np.clip(zp, -128, 127)
+    zp = np.where(zero_row, 0, zp)
+    r = np.rint(x / s[:, None]).astype(np.float64)
+    q = np.clip(r + zp[:, None], -128, 127).astype(np.int8)
+    return q, s, zp.astype(np.int32)
+
+
+def quant_static(x_bits, s_in, zp_in=0, symmetric=True):
+    """Static per-tensor quantisation with a calibrated scale (and zero point).
+
+    [vLLM] 4.1 (static tensor-wise input scale) and 4.2 (input_scale /
+    input_zero_point registered only for static input):
+        q = clamp(round(x / s_in) + zp_in, qmin, qmax),
+    [-127, 127] with zp_in = 0 when symmetric, [-128, 127] otherwise.
+    The sum is exact integer arithmetic on the rounded quotient.
+    """
+    x = bf16_bits_to_f32(x_bits)
+    s = _F(s_in)
+    r = np.rint(x / s).astype(np.float64)
+    if symmetric:
+        return np.clip(r, -127, 127).astype(np.int8)
+    return np.clip(r + int(zp_in), -128, 127).astype(np.int8)
+
+
+def quantize_act(x_bits, mode, s_in=None, zp_in=None):
+    """Dispatch on the four activation modes. Returns (q, s or None, zp or None)."""
+    if mode == MODE_DYN_SYM:
+        q, s = quant_dyn_sym(x_bits)
+        return q, s, None
+    if mode == MODE_DYN_ASYM:
+        return quant_dyn_asym(x_bits)
+    if mode == MODE_STATIC_SYM:
+        return quant_static(x_bits, s_in, 0, True), None, None
+    if mode == MODE_STATIC_ASYM:
+        return quant_static(x_bits, s_in, zp_in, False), None, None
+    raise ValueError(f"unknown mode {mode}")
+
+
+# -------------------------------------------------------------- the GEMM --
+
+def int_gemm(q, w):
+    """acc[t, n] = sum_k q[t,k] * w[n,k], exact, as int64.
+
+    [SGLang] §3 (int8 x int8 matrix product) with the [vLLM] 4.2 weight layout
+    [out_features, in_features]. Computed as a float64 matrix product: every
+    product is below 2**14 in magnitude and every partial sum below
+    K * 2**14 < 2**53 for K < 2**39, so any summation order is exact.
+    """
+    q = np.asarray(q, dtype=np.int8)
+    w = np.asarray(w, dtype=np.int8)
+    assert q.shape[1] == w.shape[1]
+    acc = q.astype(np.float64) @ w.astype(np.float64).T
+    return acc.astype(np.int64)
+
+
+def colsum(w):
+    """colsum[n] = sum_k W[n, k] as int32 ([SGLang] §4: the weight sum over the
+    input dimension, which is dim 0 of the transposed [K, N] weight)."""
+    return np.asarray(w, dtype=np.int8).astype(np.int64).sum(axis=1).astype(np.int32)
+
+
+def azp_adj_static(w, zp_in):
+    """Static asymmetric input: azp_adj = input_zero_point * colsum ([SGLang] §4)."""
+    return (np.int64(zp_in) * colsum(w).astype(np.int64)).astype(np.int32)
+
+
+def corrected_acc(acc, zp=None, col_sum=None, azp_adj=None):
+    """Integer zero-point correction c = acc - zp_t*colsum_n (dynamic asym), or
+    c = acc - azp_adj_n (static asym), or c = acc ([SGLang] §4)."""
+    c = np.asarray(acc, dtype=np.int64)
+    if zp is not None:
+        c = c - np.asarray(zp, np.int64)[:, None] * np.asarray(col_sum, np.int64)[None, :]
+    elif azp_adj is not None:
+        c = c - np.asarray(azp_adj, np.int64)[None, :]
+    return c
+
+
+def epilogue_bf16(c, s_x, s_w, bias_bits=None):
+    """out = bf16(c * s_x[t] * s_w[n] + bias[n]).
+
+    [SGLang] §3: the integer product is scaled by the token scale and the
+    weight scale, the bias is added and the result is returned in the input's
+    dtype (bf16). s_x / s_w may be scalars (per-tensor) or vectors. The value
+    is formed in float64 and rounded once to bf16.
+    """
+    c = np.asarray(c, dtype=np.float64)
+    sx = np.asarray(s_x, dtype=np.float32).astype(np.float64)
+    sw = np.asarray(s_w, dtype=np.float32).astype(np.float64)
+    sx = sx.reshape(-1, 1) if sx.ndim else sx
+    sw = sw.reshape(1, -1) if sw.ndim else sw
+    y = c * sx * sw
+    if bias_bits is not None:
+        y = y + bf16_bits_to_f32(bias_bits).astype(np.float64)[None, :]
+    return f64_to_bf16_bits(y)
+
+
+def scaled_mm(q, w, s_x, s_w, zp=None, azp_adj=None, bias_bits=None):
+    """The scaled int8 GEMM with its fused epilogue ([SGLang] §3-§4).
+
+    Returns (out bf16 bits [M,N], c int64 [M,N]) where c is the corrected
+    integer accumulator.
+    """
+    acc = int_gemm(q, w)
+    cs = colsum(w) if zp is not None else None
+    c = corrected_acc(acc, zp=zp, col_sum=cs, azp_adj=azp_adj)
+    return epilogue_bf16(c, s_x, s_w, bias_bits), c
+
+
+def linear_forward(x_bits, w, s_w, mode, s_in=None, zp_in=None, bias_bits=None):
+    """quantize_act then scaled_mm, the forward of the W8A8 linear layer
+    ([SGLang] §3 apply_weights). Returns the bf16 output bits."""
+    q, s, zp = quantize_act(x_bits, mode, s_in, zp_in)
+    if mode == MODE_DYN_SYM:
+        out, _ = scaled_mm(q, w, s, s_w, bias_bits=bias_bits)
+    elif mode == MODE_DYN_ASYM:
+        out, _ = scaled_mm(q, w, s, s_w, zp=zp, bias_bits=bias_bits)
+    elif mode == MODE_STATIC_SYM:
+        out, _ = scaled_mm(q, w, _F(s_in), s_w, bias_bits=bias_bits)
+    else:
+        out, _ = scaled_mm(q, w, _F(s_in), s_w,
+                           azp_adj=azp_adj_static(w, zp_in), bias_bits=bias_bits)
+    return out
+
+
+# ------------------------------------------------------ weight preparation --
+
+def requant_max(w, part_scales, logical_widths):
+    """Requantise a fused weight with one scale per partition to the largest scale.
+
+    [SGLang] §7 (requantize_with_max_scale): the rows of partition p
+    (logical_widths gives each partition's row count) are dequantised with
+    their own scale s_p and quantised again with s_max = max_p s_p:
+        d = fp32(W * s_p),  W' = clamp(round(d / s_max), -128, 127).
+    Returns (W' int8 [N,K], s_max float32).
+    """
+    w = np.asarray(w, dtype=np.int8)
+    ps = np.asarray(part_scales, dtype=np.float32)
+    widths = [int(v) for v in logical_widths]
+    assert sum(widths) == w.shape[0] and len(widths) == ps.shape[0]
+    s_max = _F(np.max(ps))
+    out = np.empty_like(w)
+    r0 = 0
+    for p, width in enumerate(widths):
+        rows = w[r0:r0 + width].astype(np.float32)
+        d = rows * ps[p]
+        out[r0:r0 + width] = np.clip(np.rint(d / s_max), -128, 127).astype(np.int8)
+        r0 += width
+    return out, s_max
+
+
+def e4m3fn_table() -> np.ndarray:
+    """Value of every OCP FP8 E4M3FN code as float32 (NaN for 0x7F and 0xFF).
+
+    Sign bit, 4 exponent bits with bias 7, 3 mantissa bits; exponent field 0
+    encodes subnormals 2**-6 * m/8; exponent 15 with mantissa 7 is NaN and
+    there is no infinity, so the largest finite value is 1.75 * 2**8 = 448.
+    """
+    t = np.empty(256, dtype=np.float64)
+    for code in range(256):
+        sign = -1.0 if code & 0x80 else 1.0
+        e = (code >> 3) & 0xF
+        m = code & 0x7
+        if e == 0xF and m == 0x7:
+            t[code] = np.nan
+        elif e == 0:
+            t[code] = sign * (m / 8.0) * 2.0 ** (1 - 7)
+        else:
+            t[code] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return t.astype(np.float32)
+
+
+def fp8_block_to_int8(w8, scales, block=128):
+    """FP8 128x128 block-scaled weight -> per-row symmetric int8 ([Kunlun] 转换关系).
+
+        W32[i,j] = fp32(dec(W8[i,j]) * S[i//128, j//128])   (the stored "_inv"
+                   scale multiplies; it is not inverted)
+        s[i]     = fp32(max_j |W32[i,j]| / 127)
+        q[i,j]   = clamp(round(W32[i,j] / s[i]), -127, 127)
+    An all-zero row gives q = 0, s = 1. w8 is uint8 codes [N,K] or [E,N,K];
+    scales is float32 [ceil(N/128), ceil(K/128)] (or with a leading E).
+    Returns (q int8, s float32 [.., N], flags int) where flags ORs
+    FLAG_NAN_CODE, FLAG_BAD_SCALE (NaN, +-Inf or negative scale, the page's
+    "illegal scale" of 验证) and FLAG_NONFINITE. Outputs are unspecified when
+    flags is non-zero.
+    """
+    w8 = np.asarray(w8, dtype=np.uint8)
+    S = np.asarray(scales, dtype=np.float32)
+    if w8.ndim == 3:
+        qs, ss, fl = [], [], 0
+        for e in range(w8.shape[0]):
+            q, s, f = fp8_block_to_int8(w8[e], S[e], block)
+            qs.append(q)
+            ss.append(s)
+            fl |= f
+        N, K = w8.shape[1:]
+        return (np.stack(qs) if qs else np.zeros((0, N, K), np.int8),
+                np.stack(ss) if ss else np.zeros((0, N), np.float32), fl)
+    N, K = w8.shape
+    nb, kb = -(-N // block), -(-K // block)
+    assert S.shape == (nb, kb), (S.shape, (nb, kb))
+    flags = 0
+    if np.any((w8 & 0x7F) == 0x7F):
+        flags |= FLAG_NAN_CODE
+    if np.any(~np.isfinite(S) | (S < 0)):
+        flags |= FLAG_BAD_SCALE
+    dec = e4m3fn_table()[w8]
+    S_full = np.repeat(np.repeat(S, block, axis=0), block, axis=1)[:N, :K]
+    with np.errstate(invalid="ignore", over="ignore"):
+        w32 = (dec * S_full).astype(np.float32)
+    if np.any(~np.isfinite(w32) & ~np.isnan(dec) & np.isfinite(S_full)):
+        flags |= FLAG_NONFINITE
+    with np.errstate(invalid="ignore"):
+        a = np.max(np.abs(w32), axis=1) if K else np.zeros(N, np.float32)
+    s = np.where(a == 0, _F(1), a / _F(127)).astype(np.float32)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        r = np.rint(w32 / s[:, None])
+    q = np.clip(np.nan_to_num(r), -127, 127).astype(np.int8)
+    return q, s, flags
+
+
+# ---------------------------------------------------------------- MoE --
+
+def grouped_scaled_mm(xq, s_x, w, s_w, expert_offsets, row_ids=None, bias_bits=None):
+    """Grouped (MoE) scaled GEMM: for each expert e, the rows [off_e, off_e+1)
+    of the expert-sorted activation take the plain scaled GEMM with W[e], s_w[e]
+    (and bias[e]); [SGLang] 구조도 (the w8a8_int8 MoE scheme) and [Kunlun] 版本
+    (the int8 MoE method over experts w1/w2/w3).
+
+    row_ids (optional) gathers row r of the sorted order from xq[row_ids[r]]
+    and s_x[row_ids[r]]; without it xq / s_x are already in sorted order.
+    Returns (out bf16 bits [T,N], c int64 [T,N]).
+    """
+    off = np.asarray(expert_offsets, dtype=np.int64)
+    E = w.shape[0]
+    assert off.shape == (E + 1,) and off[0] == 0 and np.all(np.diff(off) >= 0)
+    T, N = int(off[-1]), w.shape[1]
+    out = np.zeros((T, N), dtype=np.uint16)
+    cc = np.zeros((T, N), dtype=np.int64)
+    for e in range(E):
+        r0, r1 = int(off[e]), int(off[e + 1])
+        if r1 == r0:
+            continue
+        rows = np.asarray(row_ids[r0:r1], np.int64) if row_ids is not None else np.arange(r0, r1)
+        b = None if bias_bits is None else bias_bits[e]
+        o, c = scaled_mm(xq[rows], w[e], np.asarray(s_x)[rows], s_w[e], bias_bits=b)
+        out[r0:r1] = o
+        cc[r0:r1] = c
+    return out, cc

@@ -1,0 +1,170 @@
+"""Pins of the oracle's integer GEMM, zero-point correction, epilogue and
+grouped (MoE) GEMM (CPU only)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from golden_io import load_golden
+from int8_w8a8_quantized_amd import synth
+
+
+def _bf16(vals):
+    return synth.f32_to_bf16_bits(np.asarray(vals, np.float32))
+
+
+def test_int_gemm_python_loops():
+    rng = np.random.default_rng(0)
+    for M, K, N in [(3, 5, 4), (1, 37, 7), (6, 64, 3)]:
+        q = rng.integers(-128, 128, (M, K), dtype=np.int8)
+        w = rng.integers(-128, 128, (N, K), dtype=np.int8)
+        acc = O.int_gemm(q, w)
+        for t in range(M):
+            for n in range(N):
+                assert int(acc[t, n]) == sum(int(q[t, k]) * int(w[n, k]) for k in range(K))
+
+
+def test_int_gemm_extremes_closed_form():
+    K = 14336
+    q = np.full((2, K), -128, np.int8)
+    q[1] = 127
+    w = np.full((2, K), -128, np.int8)
+    w[1] = 127
+    acc = O.int_gemm(q, w)
+    assert acc[0, 0] == 16384 * K and acc[0, 1] == -128 * 127 * K
+    assert acc[1, 1] == 127 * 127 * K
+
+
+def test_colsum_and_zero_point_identity():
+    rng = np.random.default_rng(1)
+    q = rng.integers(-128, 128, (9, 200), dtype=np.int8)
+    w = rng.integers(-127, 128, (11, 200), dtype=np.int8)
+    zp = rng.integers(-128, 128, 9).astype(np.int32)
+    cs = O.colsum(w)
+    assert [int(v) for v in cs] == [sum(int(a) for a in row) for row in w]
+    c = O.corrected_acc(O.int_gemm(q, w), zp=zp, col_sum=cs)
+    direct = (q.astype(np.int64) - zp[:, None]) @ w.astype(np.int64).T
+    assert np.array_equal(c, direct)
+    adj = O.azp_adj_static(w, 17)
+    assert np.array_equal(O.corrected_acc(O.int_gemm(q, w), azp_adj=adj),
+                          (q.astype(np.int64) - 17) @ w.astype(np.int64).T)
+
+
+def test_golden_gemm():
+    (g,) = load_golden("gemm_worked.txt")
+    xq = np.array(g["xq"], np.int8).reshape(2, 2)
+    w = np.array(g["w"], np.int8).reshape(2, 2)
+    sx = np.array(g["s_x"], np.float32)
+    sw = np.array(g["s_w"], np.float32)
+    zp = np.array(g["zp"], np.int32)
+    out, c = O.scaled_mm(xq, w, sx, sw)
+    assert list(c.reshape(-1)) == g["acc"]
+    assert list(O.bf16_bits_to_f32(out).reshape(-1)) == g["y_sym"]
+    out, c = O.scaled_mm(xq, w, sx, sw, zp=zp)
+    assert list(c.reshape(-1)) == g["c"]
+    assert list(O.bf16_bits_to_f32(out).reshape(-1)) == g["y_asym"]
+
+
+def test_bf16_rounding_closed_forms():
+    one = 1.0
+    cases = {one: one, one + 2 ** -8: one, one + 3 * 2 ** -8: one + 2 ** -6,
+             one + 2 ** -8 + 2 ** -30: one + 2 ** -7, -(one + 3 * 2 ** -8): -(one + 2 ** -6),
+             2.0 ** -133: 2.0 ** -133, 2.0 ** -134: 0.0, 3 * 2.0 ** -134: 2.0 ** -132,
+             1e39: float("inf"), 0.0: 0.0}
+    for y, want in cases.items():
+        got = float(O.bf16_bits_to_f32(O.f64_to_bf16_bits(np.array([y])))[0])
+        assert got == want, (y, got, want)
+
+
+def test_bf16_rounding_matches_torch_on_f32_inputs():
+    x = np.random.default_rng(2).standard_normal(100000).astype(np.float32) * np.float32(37)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.f64_to_bf16_bits(x.astype(np.float64)), ref)
+
+
+@pytest.mark.parametrize("asym,bias", [(False, False), (False, True), (True, False), (True, True)])
+def test_epilogue_equals_dequantise_then_matmul(asym, bias):
+    """x.W = (x_q - zp) . W_q . s_x . s_w (+ b): the oracle's bf16 output is the
+    bf16 rounding of the float64 dequantise-then-matmul result."""
+    rng = np.random.default_rng(3)
+    M, K, N = 7, 96, 13
+    q = rng.integers(-128, 128, (M, K), dtype=np.int8)
+    w = rng.integers(-127, 128, (N, K), dtype=np.int8)
+    sx = rng.uniform(1e-3, 1e-1, M).astype(np.float32)
+    sw = rng.uniform(1e-3, 1e-2, N).astype(np.float32)
+    zp = rng.integers(-128, 128, M).astype(np.int32) if asym else None
+    b = _bf16(rng.normal(0, 0.02, N)) if bias else None
+    out, _ = O.scaled_mm(q, w, sx, sw, zp=zp, bias_bits=b)
+    xd = (q.astype(np.float64) - (zp[:, None] if asym else 0)) * sx[:, None]
+    wd = w.astype(np.float64) * sw[:, None]
+    ref = xd @ wd.T
+    if bias:
+        ref = ref + O.bf16_bits_to_f32(b)[None, :]
+    got = O.bf16_bits_to_f32(out).astype(np.float64)
+    # one rounding to bf16: within half a bf16 ulp (2**-8 relative)
+    assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-30)
+
+
+def test_linear_forward_tracks_float_product():
+    """End to end on the tiny workload: the W8A8 result follows the unquantised
+    float64 product within the activation rounding bound."""
+    d = synth.tiny()
+    out = O.linear_forward(d["x"], d["w"], d["s_w"], O.MODE_DYN_SYM)
+    xf = O.bf16_bits_to_f32(d["x"]).astype(np.float64)
+    wd = d["w"].astype(np.float64) * d["s_w"][:, None]
+    ref = xf @ wd.T
+    _, s = O.quant_dyn_sym(d["x"])
+    # |sum_k (x - s q)_k W_nk| <= s/2 * sum_k |W_nk| (+ output rounding)
+    bound = 0.5001 * s[:, None] * (np.abs(wd).sum(axis=1))[None, :]
+    got = O.bf16_bits_to_f32(out).astype(np.float64)
+    assert np.all(np.abs(got - ref) <= bound + np.abs(ref) * 2.0 ** -8)
+
+
+def test_static_linear_forward_identity():
+    rng = np.random.default_rng(4)
+    x = _bf16(rng.normal(0.3, 1.0, (5, 64)))
+    w = rng.integers(-127, 128, (6, 64), dtype=np.int8)
+    s_in, zp_in = np.float32(0.03), 9
+    out = O.linear_forward(x, w, np.float32(0.004), O.MODE_STATIC_ASYM, s_in, zp_in)
+    q = O.quant_static(x, s_in, zp_in, symmetric=False)
+    ref = ((q.astype(np.float64) - zp_in) * float(s_in)) @ (w.astype(np.float64) * float(np.float32(0.004))).T
+    got = O.bf16_bits_to_f32(out).astype(np.float64)
+    assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-30)
+
+
+def test_grouped_against_per_row_brute_force():
+    rng = np.random.default_rng(5)
+    E, K, N, M = 5, 32, 6, 9
+    counts = np.array([3, 0, 7, 1, 0])
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    T = int(off[-1])
+    xq = rng.integers(-128, 128, (M, K), dtype=np.int8)
+    sx = rng.uniform(0.01, 0.1, M).astype(np.float32)
+    row_ids = rng.integers(0, M, T).astype(np.int32)
+    w = rng.integers(-127, 128, (E, N, K), dtype=np.int8)
+    sw = rng.uniform(1e-3, 1e-2, (E, N)).astype(np.float32)
+    b = _bf16(rng.normal(0, 0.02, (E, N)))
+    out, c = O.grouped_scaled_mm(xq, sx, w, sw, off, row_ids=row_ids, bias_bits=b)
+    for r in range(T):
+        e = int(np.searchsorted(off, r, side="right") - 1)
+        t = int(row_ids[r])
+        for n in range(N):
+            acc = sum(int(xq[t, k]) * int(w[e, n, k]) for k in range(K))
+            assert c[r, n] == acc
+            y = acc * float(sx[t]) * float(sw[e, n]) + float(O.bf16_bits_to_f32(b[e, n]))
+            assert abs(float(O.bf16_bits_to_f32(out[r, n])) - y) <= abs(y) * 2.0 ** -8 + 1e-12
+    # without row_ids the rows are read in place
+    xs = xq[row_ids]
+    out2, c2 = O.grouped_scaled_mm(xs, sx[row_ids], w, sw, off, bias_bits=b)
+    assert np.array_equal(out2, out) and np.array_equal(c2, c)
+
+
+def test_moe_routing_generator_is_a_valid_grouping():
+    row_ids, off = synth.moe_routing(np.random.default_rng(0), 64, 8, 2)
+    assert off[0] == 0 and off[-1] == 128 and np.all(np.diff(off) >= 0)
+    # each token appears exactly top-k times, in distinct experts
+    assert np.array_equal(np.bincount(row_ids, minlength=64), np.full(64, 2))
+    for e in range(8):
+        seg = row_ids[off[e]:off[e + 1]]
+        assert np.all(np.diff(seg) > 0)
