@@ -1,0 +1,247 @@
+/*
+ * w8a8.h -- C ABI of libw8a8.so, the W8A8 INT8 linear layer for AMD MI355X (gfx950).
+ *
+ * The layer, as the three source pages describe it:
+ *   [vLLM]   "vLLM INT8 W8A8 量化实战：用 llm-compressor 制作 8 位权重与 8 位激活的推理模型"
+ *   [SGLang] "[SGLang] W4A8, W8A8, W4A4: 혼합 정밀도 양자화 스킴"
+ *   [Kunlun] "MiniMax-M2.7 FP8 转昆仑芯 INT8"
+ * quantises bf16 activations to int8 (per token and dynamic, symmetric or with
+ * a zero point, or with a static per-tensor scale), multiplies them with int8
+ * weights into exact int32 sums, and applies token scale, weight scale,
+ * zero-point correction and bias in a fused epilogue that writes bf16
+ * ([SGLang] 핵심 코드 분석 §3-§4). Load-time preparation (column sums,
+ * requantise to the max per-tensor scale, FP8 block -> per-row int8) and an
+ * MoE grouped GEMM complete it.
+ *
+ * Conventions for every call:
+ *  - Pointers are device pointers unless marked "host". Every buffer is owned
+ *    by the caller; the library allocates no device memory and keeps no state
+ *    besides a per-device property cache.
+ *  - "stream" is a hipStream_t (NULL = the null stream). Work is enqueued
+ *    asynchronously on it; nothing synchronises.
+ *  - Matrices are row-major; ld* are row strides in elements.
+ *  - bf16 values travel as their uint16_t bit patterns.
+ *  - Shape, null-pointer, alignment and range problems are found on the host
+ *    and returned before anything is enqueued (W8A8_ERR_INVALID_ARG); a
+ *    combination the layer does not define returns W8A8_ERR_NOT_IMPLEMENTED
+ *    (the [vLLM] 4.3 behaviour for an unmatched scheme); a failed launch
+ *    returns W8A8_ERR_HIP. Data-dependent problems (an illegal scale, an FP8
+ *    NaN code) are OR-ed into a caller's device err_flag word, to be read
+ *    after synchronising; the other outputs are then unspecified.
+ *  - Empty problems (a zero M, N, E or T) are legal no-ops.
+ *  - The calls are reentrant; w8a8_last_error() is per host thread.
+ *  - NaN or infinite activations are outside the contract.
+ */
+#ifndef W8A8_H
+#define W8A8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum w8a8_status {
+  W8A8_OK = 0,
+  W8A8_ERR_INVALID_ARG = 1,
+  W8A8_ERR_NOT_IMPLEMENTED = 2,
+  W8A8_ERR_UNSUPPORTED_DEVICE = 3,
+  W8A8_ERR_HIP = 4
+} w8a8_status;
+
+/* Quantisation strategies ([SGLang] 설계 근거: TENSOR/CHANNEL/BLOCK/TOKEN/GROUP). */
+enum {
+  W8A8_STRATEGY_TENSOR = 0,
+  W8A8_STRATEGY_CHANNEL = 1,
+  W8A8_STRATEGY_TOKEN = 2,
+  W8A8_STRATEGY_BLOCK = 3,
+  W8A8_STRATEGY_GROUP = 4
+};
+
+/* Activation quantisation modes of w8a8_quantize_act. */
+enum {
+  W8A8_QUANT_DYN_SYM = 0,     /* per token, s = absmax/127, codes [-127,127]        */
+  W8A8_QUANT_DYN_ASYM = 1,    /* per token, zero point, codes [-128,127]            */
+  W8A8_QUANT_STATIC_SYM = 2,  /* one calibrated s_in, codes [-127,127]              */
+  W8A8_QUANT_STATIC_ASYM = 3  /* one calibrated s_in and zp_in, codes [-128,127]    */
+};
+
+/* Zero-point correction applied by the GEMM epilogue. */
+enum {
+  W8A8_AZP_NONE = 0,
+  W8A8_AZP_PER_TOKEN = 1,  /* c = acc - zp[t] * colsum[n]   (dynamic asymmetric) */
+  W8A8_AZP_STATIC = 2      /* c = acc - azp_adj[n]          (static asymmetric)  */
+};
+
+/* Output element type of the GEMMs. */
+enum {
+  W8A8_OUT_BF16 = 0, /* bf16(c * s_x * s_w + bias), round to nearest even            */
+  W8A8_OUT_I32 = 1   /* the corrected integer c itself (exact; for checking)        */
+};
+
+/* err_flag bits. */
+enum {
+  W8A8_FLAG_NAN_CODE = 1,  /* an FP8 NaN code (0x7F or 0xFF) in a weight              */
+  W8A8_FLAG_BAD_SCALE = 2, /* a scale that is NaN, infinite or negative (or not > 0
+                              where the call says so)                              */
+  W8A8_FLAG_NONFINITE = 4  /* a dequantised weight overflowed float32               */
+};
+
+/* Largest K any call accepts: |acc - zp*colsum| <= 2*K*128*127 stays below 2^31. */
+#define W8A8_MAX_K 65536
+/* Largest number of partitions of a fused weight in w8a8_prepare_requant_max. */
+#define W8A8_MAX_PARTITIONS 16
+
+/* The quantisation scheme of one linear layer, as its checkpoint declares it
+ * ([vLLM] 4.1: bit widths, strategy, dynamic flag and symmetry of the weight
+ * and of the input). */
+typedef struct w8a8_scheme {
+  int32_t weight_bits;      /* must be 8                                   */
+  int32_t input_bits;       /* must be 8                                   */
+  int32_t weight_strategy;  /* W8A8_STRATEGY_TENSOR or _CHANNEL            */
+  int32_t input_strategy;   /* _TENSOR (static) or _TOKEN (dynamic)        */
+  int32_t weight_symmetric; /* must be 1                                   */
+  int32_t input_symmetric;  /* 0 or 1                                      */
+  int32_t weight_dynamic;   /* must be 0                                   */
+  int32_t input_dynamic;    /* 0 with _TENSOR input, 1 with _TOKEN input   */
+} w8a8_scheme;
+
+/* Check that `device` is a gfx950 GPU and cache its properties. Every other
+ * call performs the same check lazily on the current device; this one lets a
+ * caller fail early. (The analogue of the minimum-capability gate of
+ * [vLLM] 一.) Returns W8A8_ERR_UNSUPPORTED_DEVICE for any other GPU. */
+w8a8_status w8a8_init(int device);
+
+/* Validate a scheme against the combinations the layer defines ([vLLM] 4.1
+ * table: both 8-bit; weight per-tensor or per-channel, static and symmetric;
+ * input either static per-tensor or dynamic per-token, symmetric or not).
+ * On success writes the activation mode (W8A8_QUANT_*) to *quant_mode and the
+ * kernel variant flags to *is_channelwise (both nullable). Anything else
+ * returns W8A8_ERR_NOT_IMPLEMENTED and w8a8_last_error() names the fields. */
+w8a8_status w8a8_check_scheme(const w8a8_scheme* scheme, int32_t* quant_mode,
+                              int32_t* is_channelwise);
+
+/* Quantise bf16 activations x [M,K] (row stride ldx) to int8 xq [M,K]
+ * (row stride ldq). [SGLang] 핵심 코드 분석 §3 (per-token quantiser) with the
+ * per-row rule of [Kunlun] 转换关系; [vLLM] 4.1-4.2 for the static modes.
+ *   DYN_SYM:     s_x[t] = max|x_t|/127, xq = clamp(rne(x/s_x[t]), -127, 127);
+ *                an all-zero row gives s_x = 1, xq = 0.
+ *   DYN_ASYM:    lo = min(0, min x_t), hi = max(0, max x_t),
+ *                s_x[t] = (hi-lo)/255, zp[t] = clamp(-128 - rne(lo/s), -128, 127),
+ *                xq = clamp(rne(x/s) + zp[t], -128, 127); all-zero row: 1, 0, 0.
+ *   STATIC_SYM:  xq = clamp(rne(x / *s_in), -127, 127).
+ *   STATIC_ASYM: xq = clamp(rne(x / *s_in) + *zp_in, -128, 127).
+ * Every float step is one IEEE binary32 operation (true division, round to
+ * nearest even), so the codes are exactly determined.
+ * s_x: float [M], written in the dynamic modes (else ignored, may be NULL).
+ * zp: int32 [M], written in DYN_ASYM (else may be NULL).
+ * s_in / zp_in: device scalars read in the static modes (else may be NULL).
+ * Requires K % 16 == 0, K <= W8A8_MAX_K, x and xq 16-byte aligned,
+ * ldx % 8 == 0, ldq % 16 == 0, ldx >= K, ldq >= K. */
+w8a8_status w8a8_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                              int32_t mode, const float* s_in, const int32_t* zp_in,
+                              int8_t* xq, int64_t ldq, float* s_x, int32_t* zp,
+                              void* stream);
+
+/* Column sums of an int8 weight W [N,K] (row stride ldw):
+ * out[n] = sum_k W[n,k], or zp_in * sum_k W[n,k] when zp_in (a device int32
+ * scalar) is given -- the azp_adj of [SGLang] 핵심 코드 분석 §4 for the static
+ * asymmetric scheme. Run it after any requantisation of W.
+ * Requires K % 16 == 0, K <= W8A8_MAX_K, W 16-byte aligned, ldw % 16 == 0. */
+w8a8_status w8a8_prepare_colsum(const int8_t* W, int64_t N, int64_t K, int64_t ldw,
+                                const int32_t* zp_in, int32_t* out, void* stream);
+
+/* Requantise, in place, a fused weight W [N,K] whose P row partitions
+ * (host array logical_widths [P], summing to N) each carry one per-tensor
+ * scale (device part_scales [P]) to the single largest scale
+ * ([SGLang] 핵심 코드 분석 §7, requantize_with_max_scale):
+ *   s_max = max_p part_scales[p];  for the rows of partition p:
+ *   W' = clamp(rne(fp32(W * s_p) / s_max), -128, 127).
+ * Writes s_max to the device scalar *s_max. A scale that is not finite and
+ * > 0 sets W8A8_FLAG_BAD_SCALE in *err_flag (device int32, nullable; the
+ * call only ORs bits into it). 1 <= P <= W8A8_MAX_PARTITIONS; W 16-byte
+ * aligned, ldw % 16 == 0, K % 16 == 0. */
+w8a8_status w8a8_prepare_requant_max(int8_t* W, int64_t N, int64_t K, int64_t ldw,
+                                     const float* part_scales,
+                                     const int64_t* logical_widths /* host */, int32_t P,
+                                     float* s_max, int32_t* err_flag, void* stream);
+
+/* Convert E FP8 E4M3FN weights W8 [E,N,K] (OCP encoding) with float block
+ * scales S [E, ceil(N/128), ceil(K/128)] to per-row symmetric int8
+ * ([Kunlun] 转换关系):
+ *   W32 = fp32(dec(W8[i,j]) * S[i/128, j/128])   (the scale multiplies)
+ *   s[e,i] = fp32(max_j |W32[i,j]| / 127);  Wq = clamp(rne(W32 / s), -127, 127)
+ * and an all-zero row gives Wq = 0, s = 1. Wq int8 [E,N,K], s float [E,N].
+ * err_flag (device int32, required) receives W8A8_FLAG_NAN_CODE,
+ * W8A8_FLAG_BAD_SCALE (NaN, infinite or negative block scale; zero is legal)
+ * and W8A8_FLAG_NONFINITE bits. Requires K % 16 == 0, K <= W8A8_MAX_K and
+ * 16-byte aligned W8 and Wq; rows are dense (row stride K). */
+w8a8_status w8a8_prepare_fp8_block_to_int8(const uint8_t* W8, const float* S, int64_t E,
+                                           int64_t N, int64_t K, int8_t* Wq, float* s,
+                                           int32_t* err_flag, void* stream);
+
+/* Bytes of workspace w8a8_scaled_mm_int8 needs for this shape (0 when none).
+ * The caller allocates it, zero-fills it once, and may reuse it for every
+ * later call on the same stream: each call leaves it zero again. */
+size_t w8a8_scaled_mm_workspace_size(int64_t M, int64_t N, int64_t K);
+
+/* The scaled int8 GEMM with its fused epilogue ([SGLang] 핵심 코드 분석 §3-§4):
+ *   acc[t,n] = sum_k xq[t,k] * Wq[n,k]        (exact int32)
+ *   c = acc - zp[t]*colsum[n]   (azp_mode W8A8_AZP_PER_TOKEN)
+ *     = acc - azp_adj[n]        (W8A8_AZP_STATIC)
+ *     = acc                     (W8A8_AZP_NONE)
+ *   out[t,n] = bf16(c * s_x[t or 0] * s_w[n or 0] + bias[n])   (W8A8_OUT_BF16)
+ *            = c                                               (W8A8_OUT_I32)
+ * xq int8 [M,K] (ldx), Wq int8 [N,K] (ldw; the [vLLM] 4.2 layout
+ * [out_features, in_features]); s_x float [M] if s_x_per_token else [1];
+ * s_w float [N] if s_w_per_channel else [1]; zp int32 [M] and colsum int32 [N]
+ * (PER_TOKEN), or azp_adj int32 [N] (STATIC) -- pass it as `colsum`;
+ * bias bf16 [N] or NULL; out bf16 or int32 [M,N] (ldo).
+ * workspace: see w8a8_scaled_mm_workspace_size (NULL when that is 0).
+ * Requires K % 16 == 0, 1 <= K <= W8A8_MAX_K, xq/Wq/out 16-byte aligned,
+ * ldx % 16 == 0, ldw % 16 == 0, ld* >= the row length. */
+w8a8_status w8a8_scaled_mm_int8(const int8_t* xq, int64_t M, int64_t K, int64_t ldx,
+                                const int8_t* Wq, int64_t N, int64_t ldw,
+                                const float* s_x, int32_t s_x_per_token,
+                                const float* s_w, int32_t s_w_per_channel,
+                                const int32_t* zp, const int32_t* colsum, int32_t azp_mode,
+                                const uint16_t* bias, void* out, int32_t out_dtype,
+                                int64_t ldo, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/* Grouped (MoE) scaled GEMM: the rows of the expert-sorted activation are
+ * split by expert_offsets (device int32 [E+1], non-decreasing, [0] == 0,
+ * [E] == T); rows [off[e], off[e+1]) take the symmetric scaled GEMM above
+ * with Wq[e] (int8 [E,N,K], dense) and s_w[e] (float [E,N]) and bias[e]
+ * (bf16 [E,N] or NULL). The int8 MoE scheme of [SGLang] 구조도 and the int8
+ * MoE method of [Kunlun] 版本.
+ * row_ids (int32 [T], nullable): sorted row r reads activation row
+ * xq[row_ids[r]] and scale s_x[row_ids[r]] of an xq [M_src,K] (ldx);
+ * without it xq is [T,K] in sorted order, s_x is [T] and M_src is ignored.
+ * out bf16 or int32 [T,N] (ldo), in sorted order. An empty expert is legal.
+ * expert_offsets and row_ids live on the device and are not checked on the
+ * host; the kernel clamps offsets into [0,T] and treats a row id outside
+ * [0,M_src) as an all-zero row, so bad values give wrong rows, never an
+ * access outside the buffers.
+ * Requires K % 16 == 0, 1 <= K <= W8A8_MAX_K, xq/Wq/out 16-byte aligned,
+ * ldx % 16 == 0, ldo >= N. */
+w8a8_status w8a8_grouped_scaled_mm_int8(const int8_t* xq, int64_t ldx, int64_t M_src,
+                                        const int32_t* row_ids,
+                                        const int32_t* expert_offsets, int64_t T, int64_t E,
+                                        int64_t K, int64_t N, const int8_t* Wq,
+                                        const float* s_x, const float* s_w,
+                                        const uint16_t* bias, void* out, int32_t out_dtype,
+                                        int64_t ldo, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* w8a8_status_string(w8a8_status status);
+
+/* Message of the last failed call on this host thread ("" if none). */
+const char* w8a8_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W8A8_H */

@@ -1,0 +1,342 @@
+// The C ABI of libw8a8 (declared in include/w8a8.h): host-side validation,
+// scheme checking, kernel dispatch and error reporting. No device memory is
+// allocated here; all buffers belong to the caller.
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "launch.h"
+#include "w8a8.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+w8a8_status fail(w8a8_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+w8a8_status ok() {
+  g_last_error.clear();
+  return W8A8_OK;
+}
+
+w8a8_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(W8A8_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Per-device arch check: 0 = not yet checked, 1 = gfx950, 2 = other.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch[kMaxDevices];
+
+w8a8_status check_device(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(W8A8_ERR_UNSUPPORTED_DEVICE, "device %d out of range", dev);
+  int st = g_arch[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    hipError_t e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_status(e, "hipGetDeviceProperties");
+    st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_arch[dev].store(st, std::memory_order_release);
+    if (st == 2)
+      return fail(W8A8_ERR_UNSUPPORTED_DEVICE, "device %d is %s; this library is built for gfx950 (MI355X)",
+                  dev, prop.gcnArchName);
+  }
+  if (st == 2) return fail(W8A8_ERR_UNSUPPORTED_DEVICE, "device %d is not gfx950 (MI355X)", dev);
+  return W8A8_OK;
+}
+
+w8a8_status check_current_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  return check_device(dev);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define W8A8_REQUIRE(cond, ...) \
+  do {                          \
+    if (!(cond)) return fail(W8A8_ERR_INVALID_ARG, __VA_ARGS__); \
+  } while (0)
+
+w8a8_status check_k(int64_t K) {
+  W8A8_REQUIRE(K >= 1 && K <= W8A8_MAX_K, "K=%lld outside [1, %d]", (long long)K, W8A8_MAX_K);
+  W8A8_REQUIRE(K % 16 == 0, "K=%lld is not a multiple of 16", (long long)K);
+  return W8A8_OK;
+}
+
+// Sizes stay below 2^26 so that every launch's workgroup count times its
+// workgroup size fits the 32-bit grid of the dispatch packet.
+constexpr int64_t kMaxDim = int64_t(1) << 26;
+
+w8a8_status check_dim(int64_t v, const char* name) {
+  W8A8_REQUIRE(v >= 0 && v < kMaxDim, "%s=%lld outside [0, 2^26)", name, (long long)v);
+  return W8A8_OK;
+}
+
+// Output tiles of the 128x128 MFMA GEMM (grouped: plus one partial tile per expert).
+w8a8_status check_tiles(int64_t rows, int64_t extra, int64_t N) {
+  const int64_t t = ((rows + 127) / 128 + extra) * ((N + 127) / 128);
+  W8A8_REQUIRE(t < (int64_t(1) << 24), "problem needs %lld output tiles (limit 2^24)", (long long)t);
+  return W8A8_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+w8a8_status w8a8_init(int device) {
+  w8a8_status st = check_device(device);
+  return st == W8A8_OK ? ok() : st;
+}
+
+w8a8_status w8a8_check_scheme(const w8a8_scheme* s, int32_t* quant_mode, int32_t* is_channelwise) {
+  W8A8_REQUIRE(s != nullptr, "scheme is NULL");
+  std::string bad;
+  auto note = [&](const char* what, int v) {
+    char b[96];
+    std::snprintf(b, sizeof b, "%s%s=%d", bad.empty() ? "" : ", ", what, v);
+    bad += b;
+  };
+  if (s->weight_bits != 8) note("weight_bits", s->weight_bits);
+  if (s->input_bits != 8) note("input_bits", s->input_bits);
+  if (s->weight_strategy != W8A8_STRATEGY_TENSOR && s->weight_strategy != W8A8_STRATEGY_CHANNEL)
+    note("weight_strategy", s->weight_strategy);
+  if (s->weight_symmetric != 1) note("weight_symmetric", s->weight_symmetric);
+  if (s->weight_dynamic != 0) note("weight_dynamic", s->weight_dynamic);
+  if (s->input_symmetric != 0 && s->input_symmetric != 1) note("input_symmetric", s->input_symmetric);
+  const bool static_tensor = s->input_strategy == W8A8_STRATEGY_TENSOR && s->input_dynamic == 0;
+  const bool dynamic_token = s->input_strategy == W8A8_STRATEGY_TOKEN && s->input_dynamic == 1;
+  if (!static_tensor && !dynamic_token) {
+    note("input_strategy", s->input_strategy);
+    note("input_dynamic", s->input_dynamic);
+  }
+  if (!bad.empty())
+    return fail(W8A8_ERR_NOT_IMPLEMENTED,
+                "no W8A8 INT8 scheme matches (8-bit static symmetric tensor/channel weights with "
+                "static per-tensor or dynamic per-token 8-bit input): %s",
+                bad.c_str());
+  if (quant_mode)
+    *quant_mode = dynamic_token ? (s->input_symmetric ? W8A8_QUANT_DYN_SYM : W8A8_QUANT_DYN_ASYM)
+                                : (s->input_symmetric ? W8A8_QUANT_STATIC_SYM : W8A8_QUANT_STATIC_ASYM);
+  if (is_channelwise) *is_channelwise = s->weight_strategy == W8A8_STRATEGY_CHANNEL;
+  return ok();
+}
+
+w8a8_status w8a8_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int32_t mode,
+                              const float* s_in, const int32_t* zp_in, int8_t* xq, int64_t ldq,
+                              float* s_x, int32_t* zp, void* stream) {
+  w8a8_status st;
+  if ((st = check_dim(M, "M")) != W8A8_OK) return st;
+  if ((st = check_k(K)) != W8A8_OK) return st;
+  W8A8_REQUIRE(mode >= W8A8_QUANT_DYN_SYM && mode <= W8A8_QUANT_STATIC_ASYM, "unknown mode %d", mode);
+  if (M == 0) return ok();
+  W8A8_REQUIRE(x && xq, "x and xq must not be NULL");
+  W8A8_REQUIRE(aligned16(x) && aligned16(xq), "x and xq must be 16-byte aligned");
+  W8A8_REQUIRE(ldx >= K && ldx % 8 == 0, "ldx=%lld must be >= K and a multiple of 8", (long long)ldx);
+  W8A8_REQUIRE(ldq >= K && ldq % 16 == 0, "ldq=%lld must be >= K and a multiple of 16", (long long)ldq);
+  if (mode == W8A8_QUANT_DYN_SYM || mode == W8A8_QUANT_DYN_ASYM)
+    W8A8_REQUIRE(s_x != nullptr, "s_x must not be NULL in a dynamic mode");
+  if (mode == W8A8_QUANT_DYN_ASYM) W8A8_REQUIRE(zp != nullptr, "zp must not be NULL in DYN_ASYM");
+  if (mode == W8A8_QUANT_STATIC_SYM || mode == W8A8_QUANT_STATIC_ASYM)
+    W8A8_REQUIRE(s_in != nullptr, "s_in must not be NULL in a static mode");
+  if (mode == W8A8_QUANT_STATIC_ASYM) W8A8_REQUIRE(zp_in != nullptr, "zp_in must not be NULL in STATIC_ASYM");
+  if ((st = check_current_device()) != W8A8_OK) return st;
+  return hip_status(w8a8::launch_quantize_act(x, M, K, ldx, mode, s_in, zp_in, xq, ldq, s_x, zp,
+                                              static_cast<hipStream_t>(stream)),
+                    "quantize_act launch");
+}
+
+w8a8_status w8a8_prepare_colsum(const int8_t* W, int64_t N, int64_t K, int64_t ldw,
+                                const int32_t* zp_in, int32_t* out, void* stream) {
+  w8a8_status st;
+  if ((st = check_dim(N, "N")) != W8A8_OK) return st;
+  if ((st = check_k(K)) != W8A8_OK) return st;
+  if (N == 0) return ok();
+  W8A8_REQUIRE(W && out, "W and out must not be NULL");
+  W8A8_REQUIRE(aligned16(W), "W must be 16-byte aligned");
+  W8A8_REQUIRE(ldw >= K && ldw % 16 == 0, "ldw=%lld must be >= K and a multiple of 16", (long long)ldw);
+  if ((st = check_current_device()) != W8A8_OK) return st;
+  return hip_status(w8a8::launch_colsum(W, N, K, ldw, zp_in, out, static_cast<hipStream_t>(stream)),
+                    "colsum launch");
+}
+
+w8a8_status w8a8_prepare_requant_max(int8_t* W, int64_t N, int64_t K, int64_t ldw,
+                                     const float* part_scales, const int64_t* logical_widths,
+                                     int32_t P, float* s_max, int32_t* err_flag, void* stream) {
+  w8a8_status st;
+  if ((st = check_dim(N, "N")) != W8A8_OK) return st;
+  if ((st = check_k(K)) != W8A8_OK) return st;
+  W8A8_REQUIRE(P >= 1 && P <= W8A8_MAX_PARTITIONS, "P=%d outside [1, %d]", P, W8A8_MAX_PARTITIONS);
+  W8A8_REQUIRE(part_scales && logical_widths && s_max, "part_scales, logical_widths and s_max must not be NULL");
+  w8a8::RequantParts parts{};
+  parts.P = P;
+  int64_t sum = 0;
+  for (int p = 0; p < P; ++p) {
+    W8A8_REQUIRE(logical_widths[p] >= 0, "logical_widths[%d]=%lld is negative", p, (long long)logical_widths[p]);
+    parts.row_start[p] = sum;
+    sum += logical_widths[p];
+  }
+  parts.row_start[P] = sum;
+  W8A8_REQUIRE(sum == N, "logical widths sum to %lld, not N=%lld", (long long)sum, (long long)N);
+  W8A8_REQUIRE(N * (K / 16) < (int64_t(1) << 31), "N*K=%lld too large for one launch", (long long)(N * K));
+  if (N > 0) {
+    W8A8_REQUIRE(W != nullptr, "W must not be NULL");
+    W8A8_REQUIRE(aligned16(W), "W must be 16-byte aligned");
+    W8A8_REQUIRE(ldw >= K && ldw % 16 == 0, "ldw=%lld must be >= K and a multiple of 16", (long long)ldw);
+  }
+  if ((st = check_current_device()) != W8A8_OK) return st;
+  return hip_status(w8a8::launch_requant_max(W, N, K, ldw, part_scales, parts, s_max, err_flag,
+                                             static_cast<hipStream_t>(stream)),
+                    "requant_max launch");
+}
+
+w8a8_status w8a8_prepare_fp8_block_to_int8(const uint8_t* W8, const float* S, int64_t E, int64_t N,
+                                           int64_t K, int8_t* Wq, float* s, int32_t* err_flag,
+                                           void* stream) {
+  w8a8_status st;
+  if ((st = check_dim(E, "E")) != W8A8_OK) return st;
+  if ((st = check_dim(N, "N")) != W8A8_OK) return st;
+  if ((st = check_k(K)) != W8A8_OK) return st;
+  if (E == 0 || N == 0) return ok();
+  W8A8_REQUIRE(W8 && S && Wq && s && err_flag, "W8, S, Wq, s and err_flag must not be NULL");
+  W8A8_REQUIRE(aligned16(W8) && aligned16(Wq), "W8 and Wq must be 16-byte aligned");
+  W8A8_REQUIRE(E * N < kMaxDim, "E*N=%lld rows exceed 2^26", (long long)(E * N));
+  if ((st = check_current_device()) != W8A8_OK) return st;
+  return hip_status(w8a8::launch_fp8_block_to_int8(W8, S, E, N, K, Wq, s, err_flag,
+                                                   static_cast<hipStream_t>(stream)),
+                    "fp8_block_to_int8 launch");
+}
+
+size_t w8a8_scaled_mm_workspace_size(int64_t M, int64_t N, int64_t K) {
+  (void)M;
+  (void)N;
+  (void)K;
+  return 0;
+}
+
+static w8a8_status check_gemm_common(const int8_t* xq, int64_t ldx, const int8_t* Wq, int64_t K,
+                                     const void* out, int32_t out_dtype, int64_t ldo, int64_t N) {
+  W8A8_REQUIRE(xq && Wq && out, "xq, Wq and out must not be NULL");
+  W8A8_REQUIRE(aligned16(xq) && aligned16(Wq) && aligned16(out), "xq, Wq and out must be 16-byte aligned");
+  W8A8_REQUIRE(ldx >= K && ldx % 16 == 0, "ldx=%lld must be >= K and a multiple of 16", (long long)ldx);
+  W8A8_REQUIRE(ldo >= N, "ldo=%lld must be >= N", (long long)ldo);
+  W8A8_REQUIRE(out_dtype == W8A8_OUT_BF16 || out_dtype == W8A8_OUT_I32, "unknown out_dtype %d", out_dtype);
+  return W8A8_OK;
+}
+
+w8a8_status w8a8_scaled_mm_int8(const int8_t* xq, int64_t M, int64_t K, int64_t ldx, const int8_t* Wq,
+                                int64_t N, int64_t ldw, const float* s_x, int32_t s_x_per_token,
+                                const float* s_w, int32_t s_w_per_channel, const int32_t* zp,
+                                const int32_t* colsum, int32_t azp_mode, const uint16_t* bias, void* out,
+                                int32_t out_dtype, int64_t ldo, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  w8a8_status st;
+  if ((st = check_dim(M, "M")) != W8A8_OK) return st;
+  if ((st = check_dim(N, "N")) != W8A8_OK) return st;
+  if ((st = check_k(K)) != W8A8_OK) return st;
+  W8A8_REQUIRE(azp_mode >= W8A8_AZP_NONE && azp_mode <= W8A8_AZP_STATIC, "unknown azp_mode %d", azp_mode);
+  if (M == 0 || N == 0) return ok();
+  if ((st = check_gemm_common(xq, ldx, Wq, K, out, out_dtype, ldo, N)) != W8A8_OK) return st;
+  W8A8_REQUIRE(ldw >= K && ldw % 16 == 0, "ldw=%lld must be >= K and a multiple of 16", (long long)ldw);
+  W8A8_REQUIRE(s_x && s_w, "s_x and s_w must not be NULL");
+  if (azp_mode == W8A8_AZP_PER_TOKEN) W8A8_REQUIRE(zp && colsum, "AZP_PER_TOKEN needs zp and colsum");
+  if (azp_mode == W8A8_AZP_STATIC) W8A8_REQUIRE(colsum, "AZP_STATIC needs azp_adj (passed as colsum)");
+  if ((st = check_tiles(M, 0, N)) != W8A8_OK) return st;
+  if ((st = check_current_device()) != W8A8_OK) return st;
+  w8a8::GemmArgs a{};
+  a.A = xq;
+  a.lda = ldx;
+  a.B = Wq;
+  a.ldb = ldw;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.s_x = s_x;
+  a.sx_per_token = s_x_per_token != 0;
+  a.s_w = s_w;
+  a.sw_per_channel = s_w_per_channel != 0;
+  a.zp = zp;
+  a.colsum = colsum;
+  a.azp_mode = azp_mode;
+  a.bias = bias;
+  a.out = out;
+  a.out_i32 = out_dtype == W8A8_OUT_I32;
+  a.ldo = ldo;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = (M <= 64) ? w8a8::launch_decode_mm(a, s) : w8a8::launch_scaled_mm(a, s);
+  return hip_status(e, "scaled_mm launch");
+}
+
+w8a8_status w8a8_grouped_scaled_mm_int8(const int8_t* xq, int64_t ldx, int64_t M_src, const int32_t* row_ids,
+                                        const int32_t* expert_offsets, int64_t T, int64_t E, int64_t K,
+                                        int64_t N, const int8_t* Wq, const float* s_x, const float* s_w,
+                                        const uint16_t* bias, void* out, int32_t out_dtype, int64_t ldo,
+                                        void* stream) {
+  w8a8_status st;
+  if ((st = check_dim(T, "T")) != W8A8_OK) return st;
+  if ((st = check_dim(E, "E")) != W8A8_OK) return st;
+  if ((st = check_dim(N, "N")) != W8A8_OK) return st;
+  if ((st = check_k(K)) != W8A8_OK) return st;
+  if (T == 0 || E == 0 || N == 0) return ok();
+  if ((st = check_gemm_common(xq, ldx, Wq, K, out, out_dtype, ldo, N)) != W8A8_OK) return st;
+  W8A8_REQUIRE(expert_offsets && s_x && s_w, "expert_offsets, s_x and s_w must not be NULL");
+  if (row_ids) {
+    if ((st = check_dim(M_src, "M_src")) != W8A8_OK) return st;
+    W8A8_REQUIRE(M_src >= 1, "M_src must be >= 1 with row_ids");
+  }
+  if ((st = check_tiles(T, E, N)) != W8A8_OK) return st;
+  if ((st = check_current_device()) != W8A8_OK) return st;
+  w8a8::GemmArgs a{};
+  a.A = xq;
+  a.lda = ldx;
+  a.B = Wq;
+  a.ldb = K;
+  a.M = T;
+  a.N = N;
+  a.K = K;
+  a.s_x = s_x;
+  a.sx_per_token = 1;
+  a.s_w = s_w;
+  a.sw_per_channel = 1;
+  a.azp_mode = W8A8_AZP_NONE;
+  a.bias = bias;
+  a.out = out;
+  a.out_i32 = out_dtype == W8A8_OUT_I32;
+  a.ldo = ldo;
+  a.row_ids = row_ids;
+  a.expert_offsets = expert_offsets;
+  a.E = E;
+  a.M_src = row_ids ? M_src : T;
+  return hip_status(w8a8::launch_grouped_mm(a, static_cast<hipStream_t>(stream)), "grouped_mm launch");
+}
+
+const char* w8a8_status_string(w8a8_status s) {
+  switch (s) {
+    case W8A8_OK: return "W8A8_OK";
+    case W8A8_ERR_INVALID_ARG: return "W8A8_ERR_INVALID_ARG";
+    case W8A8_ERR_NOT_IMPLEMENTED: return "W8A8_ERR_NOT_IMPLEMENTED";
+    case W8A8_ERR_UNSUPPORTED_DEVICE: return "W8A8_ERR_UNSUPPORTED_DEVICE";
+    case W8A8_ERR_HIP: return "W8A8_ERR_HIP";
+  }
+  return "W8A8_UNKNOWN_STATUS";
+}
+
+const char* w8a8_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

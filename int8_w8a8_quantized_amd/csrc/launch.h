@@ -1,0 +1,59 @@
+// Host-side launchers of the libw8a8 kernels. They assume the arguments were
+// validated by the C ABI layer (api.cpp) and return the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w8a8 {
+
+hipError_t launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int mode,
+                               const float* s_in, const int32_t* zp_in, int8_t* xq, int64_t ldq,
+                               float* s_x, int32_t* zp, hipStream_t stream);
+
+hipError_t launch_colsum(const int8_t* W, int64_t N, int64_t K, int64_t ldw, const int32_t* zp_in,
+                         int32_t* out, hipStream_t stream);
+
+struct RequantParts {
+  int32_t P;
+  int64_t row_start[17];  // prefix sums of the logical widths, row_start[P] == N
+};
+
+hipError_t launch_requant_max(int8_t* W, int64_t N, int64_t K, int64_t ldw,
+                              const float* part_scales, const RequantParts& parts, float* s_max,
+                              int32_t* err_flag, hipStream_t stream);
+
+hipError_t launch_fp8_block_to_int8(const uint8_t* W8, const float* S, int64_t E, int64_t N,
+                                    int64_t K, int8_t* Wq, float* s, int32_t* err_flag,
+                                    hipStream_t stream);
+
+// Everything the GEMM kernels read besides the two operands' base pointers.
+struct GemmArgs {
+  const int8_t* A;  // activations xq
+  int64_t lda;
+  const int8_t* B;  // weights Wq [N,K] (or [E,N,K])
+  int64_t ldb;
+  int64_t M, N, K;
+  const float* s_x;
+  int32_t sx_per_token;
+  const float* s_w;
+  int32_t sw_per_channel;
+  const int32_t* zp;      // [M] per-token zero points (AZP_PER_TOKEN)
+  const int32_t* colsum;  // [N] colsum (PER_TOKEN) or azp_adj (STATIC)
+  int32_t azp_mode;
+  const uint16_t* bias;
+  void* out;
+  int32_t out_i32;
+  int64_t ldo;
+  // grouped (MoE) extras
+  const int32_t* row_ids;
+  const int32_t* expert_offsets;
+  int64_t E;
+  int64_t M_src;
+};
+
+hipError_t launch_scaled_mm(const GemmArgs& a, hipStream_t stream);  // MFMA tiles, any M
+hipError_t launch_decode_mm(const GemmArgs& a, hipStream_t stream);  // M <= 64, weight streaming
+hipError_t launch_grouped_mm(const GemmArgs& a, hipStream_t stream);
+
+}  // namespace w8a8

@@ -1,0 +1,284 @@
+// Load-time weight preparation kernels.
+//
+//  * colsum / azp_adj: the int32 sum of each weight row over the input dim,
+//    times the static input zero point when one is given
+//    ("[SGLang] W4A8, W8A8, W4A4: 혼합 정밀도 양자화 스킴", 핵심 코드 분석 §4).
+//  * requantise a fused weight whose partitions carry their own per-tensor
+//    scales to the largest of them (same page, §7, requantize_with_max_scale).
+//  * FP8 E4M3FN with 128x128 block scales -> per-row absmax/127 int8
+//    ("MiniMax-M2.7 FP8 转昆仑芯 INT8", 转换关系): the block scale multiplies the
+//    decoded value, an all-zero row gives q = 0 and s = 1.
+//
+// All three stream the weight once from HBM with 16-byte loads; one wave owns
+// one row where a row reduction is needed.
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace w8a8 {
+
+// ------------------------------------------------------------------ colsum
+
+__global__ __launch_bounds__(256) void colsum_kernel(const int8_t* __restrict__ W, int64_t N,
+                                                     int64_t K, int64_t ldw,
+                                                     const int32_t* __restrict__ zp_in,
+                                                     int32_t* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n >= N) return;
+  const int8_t* row = W + n * ldw;
+  int acc = 0;
+  for (int64_t j = lane; j < (K >> 4); j += 64) acc = sum_i8x16(ld16(row + j * 16), acc);
+  acc = wave_sum(acc);
+  if (lane == 0) out[n] = zp_in ? (*zp_in) * acc : acc;
+}
+
+hipError_t launch_colsum(const int8_t* W, int64_t N, int64_t K, int64_t ldw, const int32_t* zp_in,
+                         int32_t* out, hipStream_t stream) {
+  hipLaunchKernelGGL(colsum_kernel, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, stream, W, N, K,
+                     ldw, zp_in, out);
+  return hipGetLastError();
+}
+
+// --------------------------------------------------------- requant to max
+
+__device__ __forceinline__ bool legal_positive(float s) { return s > 0.0f && s <= 3.402823466e38f; }
+
+// Each thread owns 16 consecutive bytes of one row; the partition of the row
+// picks its scale. d = fp32(w * s_p), w' = clamp(rint(d / s_max), -128, 127).
+__global__ __launch_bounds__(256) void requant_max_kernel(int8_t* __restrict__ W, int64_t N,
+                                                          int64_t K, int64_t ldw,
+                                                          const float* __restrict__ part_scales,
+                                                          RequantParts parts,
+                                                          float* __restrict__ s_max_out,
+                                                          int32_t* __restrict__ err_flag) {
+  float s_max = part_scales[0];
+  for (int p = 1; p < parts.P; ++p) s_max = fmaxf(s_max, part_scales[p]);
+  const int64_t chunks_per_row = K >> 4;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx == 0) {
+    *s_max_out = s_max;
+    bool bad = false;
+    for (int p = 0; p < parts.P; ++p) bad |= !legal_positive(part_scales[p]);
+    if (bad && err_flag) atomicOr(err_flag, (int)2 /* W8A8_FLAG_BAD_SCALE */);
+  }
+  if (idx >= N * chunks_per_row) return;
+  const int64_t n = idx / chunks_per_row;
+  const int64_t j = idx - n * chunks_per_row;
+  int p = 0;
+  while (p + 1 < parts.P && n >= parts.row_start[p + 1]) ++p;
+  const float sp = part_scales[p];
+  int8_t* ptr = W + n * ldw + j * 16;
+  uint4 v = ld16(ptr);
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int q[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int8_t c = (int8_t)((w[i] >> (8 * b)) & 0xFF);
+      const float d = (float)c * sp;
+      float r = rne(d / s_max);
+      r = fminf(fmaxf(r, -128.0f), 127.0f);
+      q[b] = (int)r;
+    }
+    w[i] = pack4(q[0], q[1], q[2], q[3]);
+  }
+  st16(ptr, make_uint4(w[0], w[1], w[2], w[3]));
+}
+
+hipError_t launch_requant_max(int8_t* W, int64_t N, int64_t K, int64_t ldw,
+                              const float* part_scales, const RequantParts& parts, float* s_max,
+                              int32_t* err_flag, hipStream_t stream) {
+  const int64_t total = N * (K >> 4);
+  const int64_t blocks = total > 0 ? (total + 255) / 256 : 1;  // one block writes s_max
+  hipLaunchKernelGGL(requant_max_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, W, N, K,
+                     ldw, part_scales, parts, s_max, err_flag);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------- FP8 -> int8 rows
+
+// OCP E4M3FN code -> float, exact: the 7 magnitude bits placed at float bit 20
+// read as 2^(e-127)(1+m/8) for e > 0 and as the subnormal m * 2^-129 for
+// e == 0; scaling by 2^120 gives 2^(e-7)(1+m/8) and m * 2^-9, the format's
+// normal and subnormal values. NaN codes (magnitude 0x7F) decode to 480 here
+// and are reported through the flag instead.
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+  return __uint_as_float(((c & 0x7Fu) << 20) | ((c & 0x80u) << 24)) * 0x1p120f;
+}
+
+// A word holds a NaN code in some byte iff that byte's low 7 bits are all ones.
+__device__ __forceinline__ bool has_nan_code(uint32_t w) {
+  return (((w & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u) != 0;
+}
+
+__device__ __forceinline__ bool legal_block_scale(float s) {
+  return s >= 0.0f && s <= 3.402823466e38f;  // NaN, +-Inf and negatives fail; -0 passes
+}
+
+// One chunk = 16 codes of one row. Decodes and scales them into w32[16].
+__device__ __forceinline__ void decode16(uint4 v, float scale, float* w32) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) w32[i * 4 + b] = e4m3_decode((w[i] >> (8 * b)) & 0xFFu) * scale;
+}
+
+__device__ __forceinline__ uint4 encode16(const float* w32, float s) {
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int q[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      float r = rne(w32[i * 4 + b] / s);
+      r = fminf(fmaxf(r, -127.0f), 127.0f);  // NaN (flagged rows only) -> -127
+      q[b] = (int)r;
+    }
+    o[i] = pack4(q[0], q[1], q[2], q[3]);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// Flags of one row, computed after its absmax: a NaN code, an illegal scale
+// among the row's blocks, and (only if the absmax is not finite) a scan for
+// a non-NaN code whose product with a finite scale overflowed.
+struct RowCtx {
+  const uint8_t* codes;
+  const float* srow;  // block scales of this row's block-row
+  int64_t K;
+};
+
+__device__ int row_flags_slow(RowCtx r, int lane) {
+  int f = 0;
+  for (int64_t j = lane; j < (r.K >> 4); j += 64) {
+    const uint4 v = ld16(r.codes + j * 16);
+    const float sc = r.srow[(j * 16) >> 7];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    for (int i = 0; i < 4; ++i)
+      for (int b = 0; b < 4; ++b) {
+        const uint32_t c = (w[i] >> (8 * b)) & 0xFFu;
+        if ((c & 0x7Fu) == 0x7Fu || !(fabsf(sc) <= 3.402823466e38f)) continue;
+        const float d = e4m3_decode(c) * sc;
+        if (!(fabsf(d) <= 3.402823466e38f)) f |= 4;  // W8A8_FLAG_NONFINITE
+      }
+  }
+  return f;
+}
+
+// CH = 16-code chunks per lane kept in registers; rows with K <= CH*1024.
+template <int CH>
+__global__ __launch_bounds__(256) void fp8_rows_kernel(const uint8_t* __restrict__ W8,
+                                                       const float* __restrict__ S, int64_t E,
+                                                       int64_t N, int64_t K, int8_t* __restrict__ Wq,
+                                                       float* __restrict__ s_out,
+                                                       int32_t* __restrict__ err_flag) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // over E*N rows
+  if (row >= E * N) return;
+  const int64_t e = row / N, i = row - e * N;
+  const int64_t nb = (N + 127) >> 7, kb = (K + 127) >> 7;
+  const float* srow = S + (e * nb + (i >> 7)) * kb;
+  const uint8_t* codes = W8 + row * K;
+  const int64_t nchunk = K >> 4;
+  float w32[CH][16];
+  bool nan_code = false, bad_scale = false;
+  float amax = 0.0f;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int64_t j = (int64_t)c * 64 + lane;
+    if (j < nchunk) {
+      const uint4 v = ld16(codes + j * 16);
+      const float sc = srow[(j * 16) >> 7];
+      nan_code |= has_nan_code(v.x) | has_nan_code(v.y) | has_nan_code(v.z) | has_nan_code(v.w);
+      bad_scale |= !legal_block_scale(sc);
+      decode16(v, sc, w32[c]);
+#pragma unroll
+      for (int b = 0; b < 16; ++b) amax = fmaxf(amax, fabsf(w32[c][b]));
+    } else {
+#pragma unroll
+      for (int b = 0; b < 16; ++b) w32[c][b] = 0.0f;
+    }
+  }
+  amax = wave_max(amax);
+  const int any_nan = wave_or((int)nan_code), any_bad = wave_or((int)bad_scale);
+  int flags = (any_nan ? 1 : 0) | (any_bad ? 2 : 0);
+  if (!(amax <= 3.402823466e38f)) flags |= wave_or(row_flags_slow(RowCtx{codes, srow, K}, lane));
+  const float s = (amax == 0.0f) ? 1.0f : amax / 127.0f;
+  int8_t* orow = Wq + row * K;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int64_t j = (int64_t)c * 64 + lane;
+    if (j < nchunk) st16(orow + j * 16, encode16(w32[c], s));
+  }
+  if (lane == 0) {
+    s_out[row] = s;
+    if (flags) atomicOr(err_flag, flags);
+  }
+}
+
+// Any K: pass 1 for the absmax and flags, pass 2 re-reads, decodes and writes.
+__global__ __launch_bounds__(256) void fp8_rows_loop_kernel(const uint8_t* __restrict__ W8,
+                                                            const float* __restrict__ S, int64_t E,
+                                                            int64_t N, int64_t K,
+                                                            int8_t* __restrict__ Wq,
+                                                            float* __restrict__ s_out,
+                                                            int32_t* __restrict__ err_flag) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= E * N) return;
+  const int64_t e = row / N, i = row - e * N;
+  const int64_t nb = (N + 127) >> 7, kb = (K + 127) >> 7;
+  const float* srow = S + (e * nb + (i >> 7)) * kb;
+  const uint8_t* codes = W8 + row * K;
+  const int64_t nchunk = K >> 4;
+  bool nan_code = false, bad_scale = false;
+  float amax = 0.0f;
+  float w32[16];
+  for (int64_t j = lane; j < nchunk; j += 64) {
+    const uint4 v = ld16(codes + j * 16);
+    const float sc = srow[(j * 16) >> 7];
+    nan_code |= has_nan_code(v.x) | has_nan_code(v.y) | has_nan_code(v.z) | has_nan_code(v.w);
+    bad_scale |= !legal_block_scale(sc);
+    decode16(v, sc, w32);
+    for (int b = 0; b < 16; ++b) amax = fmaxf(amax, fabsf(w32[b]));
+  }
+  amax = wave_max(amax);
+  const int any_nan = wave_or((int)nan_code), any_bad = wave_or((int)bad_scale);
+  int flags = (any_nan ? 1 : 0) | (any_bad ? 2 : 0);
+  if (!(amax <= 3.402823466e38f)) flags |= wave_or(row_flags_slow(RowCtx{codes, srow, K}, lane));
+  const float s = (amax == 0.0f) ? 1.0f : amax / 127.0f;
+  int8_t* orow = Wq + row * K;
+  for (int64_t j = lane; j < nchunk; j += 64) {
+    decode16(ld16(codes + j * 16), srow[(j * 16) >> 7], w32);
+    st16(orow + j * 16, encode16(w32, s));
+  }
+  if (lane == 0) {
+    s_out[row] = s;
+    if (flags) atomicOr(err_flag, flags);
+  }
+}
+
+hipError_t launch_fp8_block_to_int8(const uint8_t* W8, const float* S, int64_t E, int64_t N,
+                                    int64_t K, int8_t* Wq, float* s, int32_t* err_flag,
+                                    hipStream_t stream) {
+  const int64_t rows = E * N;
+  const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+  const int64_t per_lane = ((K >> 4) + 63) / 64;
+  if (per_lane <= 1)
+    hipLaunchKernelGGL(fp8_rows_kernel<1>, grid, block, 0, stream, W8, S, E, N, K, Wq, s, err_flag);
+  else if (per_lane <= 2)
+    hipLaunchKernelGGL(fp8_rows_kernel<2>, grid, block, 0, stream, W8, S, E, N, K, Wq, s, err_flag);
+  else if (per_lane <= 3)
+    hipLaunchKernelGGL(fp8_rows_kernel<3>, grid, block, 0, stream, W8, S, E, N, K, Wq, s, err_flag);
+  else if (per_lane <= 4)
+    hipLaunchKernelGGL(fp8_rows_kernel<4>, grid, block, 0, stream, W8, S, E, N, K, Wq, s, err_flag);
+  else
+    hipLaunchKernelGGL(fp8_rows_loop_kernel, grid, block, 0, stream, W8, S, E, N, K, Wq, s,
+                       err_flag);
+  return hipGetLastError();
+}
+
+}  // namespace w8a8

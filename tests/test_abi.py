@@ -1,0 +1,127 @@
+"""The C ABI on the host (CPU only): the library loads, exports every function
+the header declares, validates schemes, and rejects bad arguments before any
+device work. No call here reaches a kernel."""
+
+import ctypes
+
+import pytest
+
+from int8_w8a8_quantized_amd import lib as W
+
+
+@pytest.fixture(scope="module")
+def L():
+    return W.load()
+
+
+def test_exports_every_declared_function(L):
+    names = W.header_functions()
+    assert len(names) == 11, names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    assert W.status_string(W.OK) == "W8A8_OK"
+    assert W.status_string(W.ERR_NOT_IMPLEMENTED) == "W8A8_ERR_NOT_IMPLEMENTED"
+    assert W.status_string(99) == "W8A8_UNKNOWN_STATUS"
+
+
+@pytest.mark.parametrize("wstrat,istrat,idyn,isym,mode,chan", [
+    (W.STRATEGY_CHANNEL, W.STRATEGY_TOKEN, 1, 1, W.QUANT_DYN_SYM, True),
+    (W.STRATEGY_CHANNEL, W.STRATEGY_TOKEN, 1, 0, W.QUANT_DYN_ASYM, True),
+    (W.STRATEGY_TENSOR, W.STRATEGY_TOKEN, 1, 1, W.QUANT_DYN_SYM, False),
+    (W.STRATEGY_TENSOR, W.STRATEGY_TENSOR, 0, 0, W.QUANT_STATIC_ASYM, False),
+    (W.STRATEGY_CHANNEL, W.STRATEGY_TENSOR, 0, 1, W.QUANT_STATIC_SYM, True),
+])
+def test_legal_schemes(wstrat, istrat, idyn, isym, mode, chan):
+    """The dispatch table of "vLLM INT8 W8A8 量化实战" 4.1: 8-bit weights
+    (tensor or channel, static, symmetric) with static per-tensor or dynamic
+    per-token 8-bit input, symmetric or not."""
+    assert W.check_scheme(weight_strategy=wstrat, input_strategy=istrat, input_dynamic=idyn,
+                          input_symmetric=isym) == (mode, chan)
+
+
+@pytest.mark.parametrize("kw,field", [
+    (dict(weight_bits=4), "weight_bits"),
+    (dict(input_bits=16), "input_bits"),
+    (dict(weight_strategy=W.STRATEGY_BLOCK), "weight_strategy"),
+    (dict(weight_strategy=W.STRATEGY_GROUP), "weight_strategy"),
+    (dict(weight_symmetric=0), "weight_symmetric"),
+    (dict(weight_dynamic=1), "weight_dynamic"),
+    (dict(input_strategy=W.STRATEGY_TOKEN, input_dynamic=0), "input_dynamic"),
+    (dict(input_strategy=W.STRATEGY_TENSOR, input_dynamic=1), "input_strategy"),
+    (dict(input_strategy=W.STRATEGY_CHANNEL), "input_strategy"),
+])
+def test_illegal_schemes_raise_not_implemented(kw, field):
+    with pytest.raises(NotImplementedError, match=field):
+        W.check_scheme(**kw)
+
+
+FAKE = 1 << 20  # a 16-byte aligned address that is never dereferenced
+
+
+def test_quantize_act_rejects_before_device_work(L):
+    def q(M=4, K=64, ldx=64, mode=0, x=FAKE, xq=FAKE, ldq=64, s_x=FAKE, zp=FAKE, s_in=None, zp_in=None):
+        return L.w8a8_quantize_act(x, M, K, ldx, mode, s_in, zp_in, xq, ldq, s_x, zp, None)
+    assert q(K=40) == W.ERR_INVALID_ARG            # K % 16
+    assert q(K=0) == W.ERR_INVALID_ARG
+    assert q(K=W.MAX_K + 16, ldx=W.MAX_K + 16, ldq=W.MAX_K + 16) == W.ERR_INVALID_ARG
+    assert q(M=-1) == W.ERR_INVALID_ARG
+    assert q(mode=7) == W.ERR_INVALID_ARG
+    assert q(x=None) == W.ERR_INVALID_ARG
+    assert q(x=FAKE + 8) == W.ERR_INVALID_ARG      # alignment
+    assert q(ldx=60) == W.ERR_INVALID_ARG
+    assert q(ldq=72) == W.ERR_INVALID_ARG          # ldq % 16
+    assert q(s_x=None) == W.ERR_INVALID_ARG
+    assert q(mode=W.QUANT_DYN_ASYM, zp=None) == W.ERR_INVALID_ARG
+    assert q(mode=W.QUANT_STATIC_SYM) == W.ERR_INVALID_ARG   # s_in missing
+    assert q(mode=W.QUANT_STATIC_ASYM, s_in=FAKE) == W.ERR_INVALID_ARG  # zp_in missing
+    assert "ldq" in W.last_error() or "zp_in" in W.last_error()
+    assert q(M=0) == W.OK                           # empty problem: nothing to do
+
+
+def test_gemm_rejects_before_device_work(L):
+    def mm(M=8, K=64, N=32, ldx=64, ldw=64, ldo=32, xq=FAKE, wq=FAKE, out=FAKE, sx=FAKE, sw=FAKE,
+           zp=None, cs=None, azp=0, dt=0):
+        return L.w8a8_scaled_mm_int8(xq, M, K, ldx, wq, N, ldw, sx, 1, sw, 1, zp, cs, azp, None, out,
+                                     dt, ldo, None, 0, None)
+    assert mm(K=24) == W.ERR_INVALID_ARG
+    assert mm(ldx=48) == W.ERR_INVALID_ARG
+    assert mm(ldw=72) == W.ERR_INVALID_ARG
+    assert mm(ldo=20) == W.ERR_INVALID_ARG
+    assert mm(out=FAKE + 4) == W.ERR_INVALID_ARG
+    assert mm(azp=1) == W.ERR_INVALID_ARG          # per-token AZP needs zp and colsum
+    assert mm(azp=2) == W.ERR_INVALID_ARG          # static AZP needs azp_adj
+    assert mm(azp=5) == W.ERR_INVALID_ARG
+    assert mm(dt=3) == W.ERR_INVALID_ARG
+    assert mm(sw=None) == W.ERR_INVALID_ARG
+    assert mm(M=1 << 26) == W.ERR_INVALID_ARG
+    assert mm(M=0) == W.OK and mm(N=0) == W.OK
+    assert W.scaled_mm_workspace_size(64, 4096, 4096) == 0
+
+
+def test_grouped_rejects_before_device_work(L):
+    def g(T=16, E=4, K=64, N=32, rows=FAKE, msrc=8, off=FAKE, ldo=32):
+        return L.w8a8_grouped_scaled_mm_int8(FAKE, 64, msrc, rows, off, T, E, K, N, FAKE, FAKE, FAKE,
+                                             None, FAKE, 0, ldo, None)
+    assert g(K=8) == W.ERR_INVALID_ARG
+    assert g(off=None) == W.ERR_INVALID_ARG
+    assert g(msrc=0) == W.ERR_INVALID_ARG
+    assert g(ldo=16) == W.ERR_INVALID_ARG
+    assert g(T=0) == W.OK and g(E=0) == W.OK
+
+
+def test_prepare_rejects_before_device_work(L):
+    widths = (ctypes.c_int64 * 3)(4096, 1024, 1024)
+    assert L.w8a8_prepare_requant_max(FAKE, 6000, 64, 64, FAKE, widths, 3, FAKE, None, None) == W.ERR_INVALID_ARG
+    assert "sum" in W.last_error()
+    assert L.w8a8_prepare_requant_max(FAKE, 6144, 64, 64, FAKE, widths, 0, FAKE, None, None) == W.ERR_INVALID_ARG
+    assert L.w8a8_prepare_requant_max(FAKE, 6144, 64, 64, FAKE, widths, 17, FAKE, None, None) == W.ERR_INVALID_ARG
+    neg = (ctypes.c_int64 * 2)(-1, 6145)
+    assert L.w8a8_prepare_requant_max(FAKE, 6144, 64, 64, FAKE, neg, 2, FAKE, None, None) == W.ERR_INVALID_ARG
+    assert L.w8a8_prepare_fp8_block_to_int8(FAKE, FAKE, 2, 64, 72, FAKE, FAKE, FAKE, None) == W.ERR_INVALID_ARG
+    assert L.w8a8_prepare_fp8_block_to_int8(FAKE, FAKE, 2, 64, 64, FAKE, FAKE, None, None) == W.ERR_INVALID_ARG
+    assert L.w8a8_prepare_fp8_block_to_int8(FAKE, FAKE, 0, 64, 64, FAKE, FAKE, FAKE, None) == W.OK
+    assert L.w8a8_prepare_colsum(FAKE, 16, 48, 40, None, FAKE, None) == W.ERR_INVALID_ARG
+    assert L.w8a8_prepare_colsum(FAKE, 0, 48, 48, None, FAKE, None) == W.OK

@@ -1,0 +1,122 @@
+"""GPU parity of w8a8_scaled_mm_int8: the corrected int32 accumulator
+bit-exact (W8A8_OUT_I32) and the bf16 output within 1e-2 relative, on the
+decode (M <= 64) and the MFMA tile paths, with ragged M, N and K, every
+zero-point mode, per-token / per-tensor scales and bias."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from gpu_util import assert_bf16_close, assert_equal, bf16_bits, host, note, to_dev
+from int8_w8a8_quantized_amd import lib as W
+from int8_w8a8_quantized_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(M, K, N, seed=0, full_range=True):
+    rng = synth.rng_for(901, M, K, N, seed)
+    lo = -128 if full_range else -127
+    return dict(
+        xq=rng.integers(lo, 128, (M, K), dtype=np.int8),
+        w=rng.integers(lo, 128, (N, K), dtype=np.int8),
+        sx=rng.uniform(1e-3, 5e-2, M).astype(np.float32),
+        sw=rng.uniform(1e-3, 1e-2, N).astype(np.float32),
+        zp=rng.integers(-128, 128, M).astype(np.int32),
+        bias=synth.bias_bits(rng, N),
+        zin=int(rng.integers(-128, 128)),
+    )
+
+
+def _run(d, azp, per_token=True, per_channel=True, bias=False, out_dtype=W.OUT_BF16, ldo=None):
+    M, K = d["xq"].shape
+    N = d["w"].shape[0]
+    note(f"scaled_mm M={M} K={K} N={N} azp={azp} pt={per_token} pc={per_channel} bias={bias} out={out_dtype}")
+    xq, w = to_dev(d["xq"]), to_dev(d["w"])
+    sx = to_dev(d["sx"] if per_token else d["sx"][:1])
+    sw = to_dev(d["sw"] if per_channel else d["sw"][:1])
+    zp = colsum = None
+    if azp == W.AZP_PER_TOKEN:
+        zp = to_dev(d["zp"])
+        colsum = to_dev(O.colsum(d["w"]))
+    elif azp == W.AZP_STATIC:
+        colsum = to_dev(O.azp_adj_static(d["w"], d["zin"]))
+    b = to_dev(d["bias"]) if bias else None
+    out = None
+    if ldo is not None:
+        dt = torch.bfloat16 if out_dtype == W.OUT_BF16 else torch.int32
+        out = torch.zeros((M, ldo), dtype=dt, device="cuda:0")[:, :N]
+    got = W.scaled_mm_int8(xq, w, sx, sw, zp=zp, colsum=colsum, azp_mode=azp, bias=b,
+                           out_dtype=out_dtype, out=out)
+    torch.cuda.synchronize()
+    acc = O.int_gemm(d["xq"], d["w"])
+    if azp == W.AZP_PER_TOKEN:
+        c = O.corrected_acc(acc, zp=d["zp"], col_sum=O.colsum(d["w"]))
+    elif azp == W.AZP_STATIC:
+        c = O.corrected_acc(acc, azp_adj=O.azp_adj_static(d["w"], d["zin"]))
+    else:
+        c = acc
+    if out_dtype == W.OUT_I32:
+        assert_equal(host(got), c.astype(np.int32), "int32 accumulator")
+    else:
+        want = O.epilogue_bf16(c, d["sx"] if per_token else d["sx"][0],
+                               d["sw"] if per_channel else d["sw"][0], d["bias"] if bias else None)
+        assert_bf16_close(bf16_bits(got), want)
+
+
+SHAPES = [(1, 256, 512), (7, 272, 520), (16, 256, 512), (33, 1040, 100), (64, 4096, 96),
+          (65, 272, 130), (128, 512, 256), (200, 1296, 333), (257, 4112, 129), (1, 64, 1), (3, 16, 17)]
+
+
+@pytest.mark.parametrize("M,K,N", SHAPES)
+@pytest.mark.parametrize("azp", [W.AZP_NONE, W.AZP_PER_TOKEN, W.AZP_STATIC])
+def test_i32_exact(M, K, N, azp):
+    _run(_inputs(M, K, N), azp, out_dtype=W.OUT_I32)
+
+
+@pytest.mark.parametrize("M,K,N", SHAPES)
+def test_bf16_epilogue_variants(M, K, N):
+    d = _inputs(M, K, N, seed=1)
+    _run(d, W.AZP_NONE, bias=True)
+    _run(d, W.AZP_PER_TOKEN, per_channel=False)
+    _run(d, W.AZP_STATIC, per_token=False, bias=True)
+
+
+def test_strided_output():
+    d = _inputs(70, 512, 200, seed=2)
+    _run(d, W.AZP_PER_TOKEN, ldo=264, out_dtype=W.OUT_I32)
+    _run(d, W.AZP_NONE, ldo=208, bias=True)
+    d = _inputs(9, 512, 200, seed=3)
+    _run(d, W.AZP_NONE, ldo=264, out_dtype=W.OUT_I32)
+
+
+def test_extreme_values_exact():
+    """All -128 against all -128 over K = 14336: the largest sums, still exact."""
+    M, K, N = 70, 14336, 40
+    d = _inputs(M, K, N, seed=4)
+    d["xq"][:] = -128
+    d["w"][:] = -128
+    d["w"][1::2] = 127
+    _run(d, W.AZP_NONE, out_dtype=W.OUT_I32)
+    d["xq"] = d["xq"][:5].copy()
+    d["sx"], d["zp"] = d["sx"][:5], d["zp"][:5]
+    _run(d, W.AZP_PER_TOKEN, out_dtype=W.OUT_I32)
+
+
+def test_deterministic_repeat():
+    d = _inputs(64, 4096, 1000, seed=5)
+    xq, w = to_dev(d["xq"]), to_dev(d["w"])
+    sx, sw = to_dev(d["sx"]), to_dev(d["sw"])
+    a = W.scaled_mm_int8(xq, w, sx, sw, out_dtype=W.OUT_I32)
+    b = W.scaled_mm_int8(xq, w, sx, sw, out_dtype=W.OUT_I32)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_empty():
+    xq = torch.empty((0, 64), dtype=torch.int8, device="cuda:0")
+    w = torch.zeros((8, 64), dtype=torch.int8, device="cuda:0")
+    s = torch.ones(8, dtype=torch.float32, device="cuda:0")
+    out = W.scaled_mm_int8(xq, w, s[:1], s)
+    assert out.shape == (0, 8)

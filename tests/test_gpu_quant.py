@@ -1,0 +1,101 @@
+"""GPU parity of w8a8_quantize_act against the oracle: bit-exact codes,
+scales and zero points."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from gpu_util import assert_equal, host, note, to_dev
+from int8_w8a8_quantized_amd import lib as W
+from int8_w8a8_quantized_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _x(M, K, mean=0.0, outliers=0, seed=0):
+    return synth.activations(synth.rng_for(900, M, K, seed), M, K, mean, outliers, 40.0)
+
+
+def _check(x_bits, mode, s_in=None, zp_in=None, ldx=None, ldq=None):
+    M, K = x_bits.shape
+    note(f"quantize_act mode={mode} M={M} K={K} ldx={ldx} ldq={ldq}")
+    if ldx is not None:
+        buf = np.zeros((M, ldx), np.uint16)
+        buf[:, :K] = x_bits
+        xd = to_dev(buf)[:, :K]
+    else:
+        xd = to_dev(x_bits)
+    xq = None
+    if ldq is not None:
+        xq = torch.full((M, ldq), 99, dtype=torch.int8, device=xd.device)[:, :K]
+    sin = None if s_in is None else torch.tensor([s_in], dtype=torch.float32, device=xd.device)
+    zin = None if zp_in is None else torch.tensor([zp_in], dtype=torch.int32, device=xd.device)
+    q, s, zp = W.quantize_act(xd, mode, sin, zin, xq=xq)
+    torch.cuda.synchronize()
+    rq, rs, rzp = O.quantize_act(x_bits, mode, None if s_in is None else np.float32(s_in), zp_in)
+    assert_equal(host(q), rq, "codes")
+    if rs is not None:
+        assert_equal(host(s).view(np.uint32), rs.view(np.uint32), "scales")
+    if rzp is not None:
+        assert_equal(host(zp), rzp, "zero points")
+    if ldq is not None:  # padding columns untouched
+        full = host(xq.as_strided((M, ldq), (ldq, 1)))
+        assert np.all(full[:, K:] == 99)
+
+
+MODES = [W.QUANT_DYN_SYM, W.QUANT_DYN_ASYM]
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("M,K", [(1, 16), (3, 48), (16, 256), (5, 512), (7, 528), (4, 4096),
+                                 (2, 14336), (9, 8208), (3, 16384), (2, 16400), (2, 40960)])
+def test_dynamic_shapes(mode, M, K):
+    _check(_x(M, K, 0.3 if mode == W.QUANT_DYN_ASYM else 0.0, min(3, K)), mode)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_many_rows_ragged(mode):
+    _check(_x(1027, 1536, 0.3, 4, seed=1), mode)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_strided(mode):
+    _check(_x(37, 272, 0.1, 2, seed=2), mode, ldx=288, ldq=304)
+
+
+def test_edge_rows():
+    """All-zero rows (incl. -0.0), a single nonzero, one-signed rows, tiny
+    subnormal-range values, exact ties, and huge values."""
+    K = 64
+    rows = np.zeros((10, K), np.uint16)
+    rows[1, :] = 0x8000
+    rows[2, 17] = synth.f32_to_bf16_bits(np.array([-3.5], np.float32))[0]
+    rows[3] = synth.f32_to_bf16_bits(np.abs(np.random.default_rng(0).standard_normal(K)).astype(np.float32))
+    rows[4] = rows[3] ^ np.uint16(0x8000)
+    rows[5] = np.arange(K, dtype=np.uint16) + 1                      # bf16 subnormals
+    rows[6] = synth.f32_to_bf16_bits(np.linspace(-127, 127, K).astype(np.float32) / 2)
+    rows[7] = synth.f32_to_bf16_bits(np.float32(1e30) * np.random.default_rng(1).standard_normal(K).astype(np.float32))
+    rows[8, :32] = synth.f32_to_bf16_bits((np.arange(32) + 0.5).astype(np.float32))
+    rows[8, 32] = synth.f32_to_bf16_bits(np.array([127.0], np.float32))[0]
+    rows[9] = synth.f32_to_bf16_bits(np.float32(2.0 ** -120) * np.random.default_rng(2).standard_normal(K).astype(np.float32))
+    for mode in MODES:
+        _check(rows, mode)
+
+
+@pytest.mark.parametrize("symmetric", [True, False])
+def test_static(symmetric):
+    x = _x(129, 4096, 0.3, 20, seed=3)
+    mode = W.QUANT_STATIC_SYM if symmetric else W.QUANT_STATIC_ASYM
+    _check(x, mode, s_in=0.0213, zp_in=None if symmetric else -17)
+
+
+def test_static_workload():
+    d = synth.static_qkv()
+    _check(d["x"], W.QUANT_STATIC_ASYM, s_in=float(d["s_in"]), zp_in=int(d["zp_in"]))
+
+
+def test_empty():
+    xd = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda:0")
+    q, s, _ = W.quantize_act(xd, W.QUANT_DYN_SYM)
+    assert q.shape == (0, 64)
