@@ -102,6 +102,8 @@ def main():
                                s_x=torch.empty(M, dtype=torch.float32, device=dev),
                                out=torch.empty((M, N), dtype=torch.bfloat16, device=dev))
     step_bytes = sum(gemm_bytes(M, K, N, bias=True) + quant_bytes(M, K) for (M, K, N) in shapes)
+    ws_bytes = max(W.scaled_mm_workspace_size(M, N, K) for (M, K, N) in shapes)
+    workspace = torch.zeros(max(1, ws_bytes // 4), dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
 
     call = [0]
@@ -117,7 +119,8 @@ def main():
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
-            W.scaled_mm_int8(a["xq"], w, a["s_x"], wv["s_w"], bias=wv["bias"], out=a["out"])
+            W.scaled_mm_int8(a["xq"], w, a["s_x"], wv["s_w"], bias=wv["bias"], out=a["out"],
+                             workspace=workspace)
             if events:
                 e1.record(stream)
                 ev_log.append(((M, K, N), e0, e1))

@@ -52,6 +52,12 @@ __device__ __forceinline__ int wave_or(int v) {
 // 16-byte global load / store.
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+// 16-byte load of data read exactly once (non-temporal: do not keep it in cache).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ldnt16(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 // Sum of the four signed bytes of each of the four words (v_dot4_i32_i8 with ones).
 __device__ __forceinline__ int sum_i8x16(uint4 v, int acc) {

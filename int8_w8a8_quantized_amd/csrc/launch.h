@@ -53,7 +53,12 @@ struct GemmArgs {
 };
 
 hipError_t launch_scaled_mm(const GemmArgs& a, hipStream_t stream);  // MFMA tiles, any M
-hipError_t launch_decode_mm(const GemmArgs& a, hipStream_t stream);  // M <= 64, weight streaming
+// M <= 64: weight streaming, split over K through the workspace when one of
+// decode_workspace_bytes(M, N) bytes is given (zero on entry, zero on exit).
+hipError_t launch_decode_mm(const GemmArgs& a, void* workspace, size_t ws_bytes, int num_cus,
+                            hipStream_t stream);
+size_t decode_workspace_bytes(int64_t M, int64_t N);
+constexpr int64_t kDecodeMaxM = 64;
 hipError_t launch_grouped_mm(const GemmArgs& a, hipStream_t stream);
 
 }  // namespace w8a8

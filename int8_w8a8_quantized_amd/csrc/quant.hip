@@ -8,19 +8,26 @@
 // (§3-§4) and "vLLM INT8 W8A8 量化实战" (4.2) describe; static: one calibrated
 // scale (and zero point) for the whole tensor ("vLLM INT8 W8A8 量化实战" 4.1).
 //
-// One wave owns one row. The row is read once with 16-byte loads (8 bf16 per
-// lane per chunk, consecutive lanes on consecutive chunks so each wave
-// instruction moves 1 KiB of contiguous HBM) and kept in registers while the
-// wave reduces its absmax (or min and max) with cross-lane shuffles; the codes
-// are then written as 8-byte stores, again contiguous across the wave. HBM
-// traffic is the algorithmic 2 B read + 1 B written per element. Rows longer
-// than the register budget take a two-pass variant that re-reads the row
-// (an L2 hit: one row is at most 128 KiB).
+// Layout: TPR threads own one row (TPR = 64, 256 or 1024; several rows share a
+// 256-thread workgroup when TPR = 64). The row is read once with 16-byte
+// loads (8 bf16 per chunk, consecutive threads on consecutive chunks, so a
+// wave instruction moves 1 KiB of contiguous HBM), held in registers (CH
+// chunks per thread) while the extremes are reduced across lanes with
+// shuffles and across the row's waves through LDS, then written as 8-byte
+// code stores. HBM traffic is the algorithmic 2 B read + 1 B written per
+// element. Small batches use wide rows (more threads per row, fewer chunks
+// per thread) to cut latency; large batches use narrow rows and many waves.
 //
-// Every float step is one IEEE binary32 operation: the absmax and min/max are
-// exact, the scale is a true division by 127 (or 255), and each code is
-// rint(x / s) with a true division and round-half-to-even, so the codes equal
-// the exactly defined ones bit for bit.
+// Exactness: the absmax / min / max are exact, the scale is one IEEE binary32
+// division, and each code is rint(fl(x / s)) with round-half-to-even. The
+// per-element division is replaced by t = fl(x * r) with r = fl(1 / s), which
+// is provably enough except near a rounding boundary: |t - fl(x/s)| <
+// |t| * 2^-22 whenever 1/s is a normal number (two roundings of relative
+// size 2^-24 in t, one in fl(x/s)), so if the distance from t to the nearest
+// half-integer exceeds |t| * 2^-22 both round to the same integer. Elements
+// that fail that test (about 1 in 16000), and rows whose scale is outside
+// (2^-100, 2^100), take the true division. Quotients of magnitude >= 1024
+// saturate every mode's clamp whichever way they round.
 
 #include "device_common.h"
 #include "launch.h"
@@ -30,31 +37,65 @@ namespace w8a8 {
 enum { kDynSym = 0, kDynAsym = 1, kStaticSym = 2, kStaticAsym = 3 };
 
 struct RowParams {
-  float s;
-  int zp;
+  float s;     // scale
+  float r;     // fl(1/s)
+  int zp;      // zero point (0 for symmetric modes)
+  bool fast;   // 1/s is comfortably normal: the multiply-and-check path applies
 };
 
-// Code of one element. Symmetric: clamp(rint(x/s), -127, 127). Asymmetric:
-// clamp(rint(x/s) + zp, -128, 127); the quotient is clamped to +-512 before the
-// integer add, which cannot change the result since |zp| <= 128.
-template <int MODE>
-__device__ __forceinline__ int code_of(float x, RowParams p) {
-  float r = rne(x / p.s);
-  if (MODE == kDynSym || MODE == kStaticSym) {
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
-    return (int)r;
-  }
-  r = fminf(fmaxf(r, -512.0f), 512.0f);
-  return clampi((int)r + p.zp, -128, 127);
+__device__ __forceinline__ RowParams finish_params(float s, int zp) {
+  RowParams p;
+  p.s = s;
+  p.zp = zp;
+  p.fast = s > 0x1p-100f && s < 0x1p100f;
+  p.r = 1.0f / s;
+  return p;
+}
+
+// rint(fl(x / s)) via the multiply when it provably agrees; flags the rest.
+__device__ __forceinline__ float quot_round(float x, const RowParams& p, bool& fix) {
+  const float t = x * p.r;
+  const float f = t - floorf(t);
+  const float at = fabsf(t);
+  const bool ok = p.fast && (fabsf(f - 0.5f) > at * 0x1p-22f || at >= 1024.0f);
+  fix = !ok;
+  return rne(t);
 }
 
 template <int MODE>
-__device__ __forceinline__ uint2 codes8(uint4 v, RowParams p) {
+__device__ __forceinline__ int finish_code(float rq, int zp) {
+  if (MODE == kDynSym || MODE == kStaticSym) return (int)fminf(fmaxf(rq, -127.0f), 127.0f);
+  return clampi((int)fminf(fmaxf(rq, -512.0f), 512.0f) + zp, -128, 127);
+}
+
+// Codes of one 16-byte chunk (8 bf16) as 8 bytes.
+template <int MODE>
+__device__ __forceinline__ uint2 codes8(uint4 v, const RowParams& p) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float xs[8], rq[8];
+  uint32_t fix = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    xs[2 * i] = bf16_lo(w[i]);
+    xs[2 * i + 1] = bf16_hi(w[i]);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    bool f;
+    rq[e] = quot_round(xs[e], p, f);
+    fix |= (uint32_t)f << e;
+  }
+  if (__builtin_expect(fix != 0, 0)) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if ((fix >> e) & 1u) rq[e] = rne(xs[e] / p.s);
+  }
+  int q[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) q[e] = finish_code<MODE>(rq[e], p.zp);
   uint2 o;
-  o.x = pack4(code_of<MODE>(bf16_lo(v.x), p), code_of<MODE>(bf16_hi(v.x), p),
-              code_of<MODE>(bf16_lo(v.y), p), code_of<MODE>(bf16_hi(v.y), p));
-  o.y = pack4(code_of<MODE>(bf16_lo(v.z), p), code_of<MODE>(bf16_hi(v.z), p),
-              code_of<MODE>(bf16_lo(v.w), p), code_of<MODE>(bf16_hi(v.w), p));
+  o.x = pack4(q[0], q[1], q[2], q[3]);
+  o.y = pack4(q[4], q[5], q[6], q[7]);
   return o;
 }
 
@@ -68,52 +109,44 @@ __device__ __forceinline__ void minmax8(uint4 v, float& lo, float& hi) {
   }
 }
 
-// Row parameters from the wave-reduced extremes. lo <= 0 <= hi always, since
-// both start at 0 (the asymmetric range is widened to contain zero; for the
+// Row parameters from the reduced extremes. lo <= 0 <= hi always, since both
+// start at 0 (the asymmetric range is widened to contain zero; for the
 // symmetric mode absmax = max(hi, -lo)).
 template <int MODE>
 __device__ __forceinline__ RowParams row_params(float lo, float hi, const float* s_in,
                                                 const int32_t* zp_in) {
-  RowParams p;
   if (MODE == kDynSym) {
-    float a = fmaxf(hi, -lo);
-    p.s = (a == 0.0f) ? 1.0f : a / 127.0f;
-    p.zp = 0;
-  } else if (MODE == kDynAsym) {
-    if (hi == lo) {
-      p.s = 1.0f;
-      p.zp = 0;
-    } else {
-      p.s = (hi - lo) / 255.0f;
-      float z = fminf(fmaxf(rne(lo / p.s), -512.0f), 512.0f);
-      p.zp = clampi(-128 - (int)z, -128, 127);
-    }
-  } else {
-    p.s = *s_in;
-    p.zp = (MODE == kStaticAsym) ? *zp_in : 0;
+    const float a = fmaxf(hi, -lo);
+    return finish_params((a == 0.0f) ? 1.0f : a / 127.0f, 0);
   }
-  return p;
+  if (MODE == kDynAsym) {
+    if (hi == lo) return finish_params(1.0f, 0);
+    const float s = (hi - lo) / 255.0f;
+    const float z = fminf(fmaxf(rne(lo / s), -512.0f), 512.0f);
+    return finish_params(s, clampi(-128 - (int)z, -128, 127));
+  }
+  return finish_params(*s_in, (MODE == kStaticAsym) ? *zp_in : 0);
 }
 
-// CH = 16-byte chunks per lane held in registers; rows with K <= CH*512.
-template <int MODE, int CH>
-__global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ x,
-                                                         int64_t M, int64_t K, int64_t ldx,
-                                                         const float* __restrict__ s_in,
-                                                         const int32_t* __restrict__ zp_in,
-                                                         int8_t* __restrict__ xq, int64_t ldq,
-                                                         float* __restrict__ s_x,
-                                                         int32_t* __restrict__ zp) {
-  const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= M) return;
+template <int MODE, int TPR, int CH>
+__global__ __launch_bounds__(TPR < 256 ? 256 : TPR) void quant_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
+    const float* __restrict__ s_in, const int32_t* __restrict__ zp_in, int8_t* __restrict__ xq,
+    int64_t ldq, float* __restrict__ s_x, int32_t* __restrict__ zp) {
+  constexpr int BLOCK = TPR < 256 ? 256 : TPR;
+  constexpr int RPB = BLOCK / TPR;           // rows per workgroup
+  constexpr int WPR = TPR / 64;              // waves per row
+  const int sub = threadIdx.x % TPR;
+  const int64_t t = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+  const bool row_ok = t < M;
+  if (WPR == 1 && !row_ok) return;           // nothing below synchronises in that case
   const int64_t nchunk = K >> 3;
-  const uint16_t* row = x + t * ldx;
+  const uint16_t* row = x + (row_ok ? t : 0) * ldx;
   uint4 v[CH];
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
-    const int64_t j = (int64_t)c * 64 + lane;
-    v[c] = (j < nchunk) ? ld16(row + j * 8) : make_uint4(0, 0, 0, 0);
+    const int64_t j = (int64_t)c * TPR + sub;
+    v[c] = (row_ok && j < nchunk) ? ld16(row + j * 8) : make_uint4(0, 0, 0, 0);
   }
   RowParams p;
   if (MODE == kDynSym || MODE == kDynAsym) {
@@ -122,75 +155,77 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
     for (int c = 0; c < CH; ++c) minmax8(v[c], lo, hi);
     lo = wave_min(lo);
     hi = wave_max(hi);
+    if (WPR > 1) {
+      __shared__ float red_lo[WPR > 1 ? WPR : 1], red_hi[WPR > 1 ? WPR : 1];
+      const int wv = sub >> 6;
+      if ((threadIdx.x & 63) == 0) {
+        red_lo[wv] = lo;
+        red_hi[wv] = hi;
+      }
+      __syncthreads();
+      lo = red_lo[0];
+      hi = red_hi[0];
+#pragma unroll
+      for (int i = 1; i < WPR; ++i) {
+        lo = fminf(lo, red_lo[i]);
+        hi = fmaxf(hi, red_hi[i]);
+      }
+    }
+    if (!row_ok) return;
     p = row_params<MODE>(lo, hi, s_in, zp_in);
-    if (lane == 0) {
+    if (sub == 0) {
       s_x[t] = p.s;
       if (MODE == kDynAsym) zp[t] = p.zp;
     }
   } else {
+    if (!row_ok) return;
     p = row_params<MODE>(0.0f, 0.0f, s_in, zp_in);
   }
   int8_t* orow = xq + t * ldq;
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
-    const int64_t j = (int64_t)c * 64 + lane;
+    const int64_t j = (int64_t)c * TPR + sub;
     if (j < nchunk) *reinterpret_cast<uint2*>(orow + j * 8) = codes8<MODE>(v[c], p);
   }
 }
 
-// Any K: a first pass for the extremes, a second that re-reads and writes.
-template <int MODE>
-__global__ __launch_bounds__(256) void quant_rows_loop_kernel(const uint16_t* __restrict__ x,
-                                                              int64_t M, int64_t K, int64_t ldx,
-                                                              const float* __restrict__ s_in,
-                                                              const int32_t* __restrict__ zp_in,
-                                                              int8_t* __restrict__ xq, int64_t ldq,
-                                                              float* __restrict__ s_x,
-                                                              int32_t* __restrict__ zp) {
-  const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= M) return;
-  const int64_t nchunk = K >> 3;
-  const uint16_t* row = x + t * ldx;
-  RowParams p;
-  if (MODE == kDynSym || MODE == kDynAsym) {
-    float lo = 0.0f, hi = 0.0f;
-    for (int64_t j = lane; j < nchunk; j += 64) minmax8(ld16(row + j * 8), lo, hi);
-    lo = wave_min(lo);
-    hi = wave_max(hi);
-    p = row_params<MODE>(lo, hi, s_in, zp_in);
-    if (lane == 0) {
-      s_x[t] = p.s;
-      if (MODE == kDynAsym) zp[t] = p.zp;
-    }
-  } else {
-    p = row_params<MODE>(0.0f, 0.0f, s_in, zp_in);
-  }
-  int8_t* orow = xq + t * ldq;
-  for (int64_t j = lane; j < nchunk; j += 64)
-    *reinterpret_cast<uint2*>(orow + j * 8) = codes8<MODE>(ld16(row + j * 8), p);
+template <int MODE, int TPR>
+static void launch_tpr(int ch, dim3 grid, hipStream_t stream, const uint16_t* x, int64_t M,
+                       int64_t K, int64_t ldx, const float* s_in, const int32_t* zp_in, int8_t* xq,
+                       int64_t ldq, float* s_x, int32_t* zp) {
+  constexpr int BLOCK = TPR < 256 ? 256 : TPR;
+#define W8A8_Q(CHV)                                                                           \
+  hipLaunchKernelGGL((quant_kernel<MODE, TPR, CHV>), grid, dim3(BLOCK), 0, stream, x, M, K, ldx, \
+                     s_in, zp_in, xq, ldq, s_x, zp)
+  if (ch <= 1) W8A8_Q(1);
+  else if (ch <= 2) W8A8_Q(2);
+  else if (ch <= 4) W8A8_Q(4);
+  else W8A8_Q(8);
+#undef W8A8_Q
 }
 
 template <int MODE>
 static hipError_t launch_mode(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                               const float* s_in, const int32_t* zp_in, int8_t* xq, int64_t ldq,
                               float* s_x, int32_t* zp, hipStream_t stream) {
-  const dim3 grid((unsigned)((M + 3) / 4)), block(256);
-  const int64_t per_lane = (K / 8 + 63) / 64;  // 16-byte chunks per lane
-#define W8A8_QLAUNCH(CHV)                                                                       \
-  hipLaunchKernelGGL((quant_rows_kernel<MODE, CHV>), grid, block, 0, stream, x, M, K, ldx, s_in, \
-                     zp_in, xq, ldq, s_x, zp)
-  if (per_lane <= 1) W8A8_QLAUNCH(1);
-  else if (per_lane <= 2) W8A8_QLAUNCH(2);
-  else if (per_lane <= 4) W8A8_QLAUNCH(4);
-  else if (per_lane <= 8) W8A8_QLAUNCH(8);
-  else if (per_lane <= 16) W8A8_QLAUNCH(16);
-  else if (per_lane <= 28) W8A8_QLAUNCH(28);
-  else if (per_lane <= 32) W8A8_QLAUNCH(32);
+  const int64_t nchunk = K / 8;
+  // Threads per row: wide rows for small batches (latency), narrow for large.
+  int tpr;
+  if (M <= 256)
+    tpr = nchunk <= 64 ? 64 : (nchunk <= 512 ? 256 : 1024);
   else
-    hipLaunchKernelGGL((quant_rows_loop_kernel<MODE>), grid, block, 0, stream, x, M, K, ldx, s_in,
-                       zp_in, xq, ldq, s_x, zp);
-#undef W8A8_QLAUNCH
+    tpr = nchunk <= 512 ? 64 : (nchunk <= 2048 ? 256 : 1024);
+  const int ch = (int)((nchunk + tpr - 1) / tpr);  // <= 8 since K <= 65536
+  if (tpr == 64) {
+    launch_tpr<MODE, 64>(ch, dim3((unsigned)((M + 3) / 4)), stream, x, M, K, ldx, s_in, zp_in, xq,
+                         ldq, s_x, zp);
+  } else if (tpr == 256) {
+    launch_tpr<MODE, 256>(ch, dim3((unsigned)M), stream, x, M, K, ldx, s_in, zp_in, xq, ldq, s_x,
+                          zp);
+  } else {
+    launch_tpr<MODE, 1024>(ch, dim3((unsigned)M), stream, x, M, K, ldx, s_in, zp_in, xq, ldq, s_x,
+                           zp);
+  }
   return hipGetLastError();
 }
 

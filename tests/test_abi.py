@@ -98,7 +98,10 @@ def test_gemm_rejects_before_device_work(L):
     assert mm(sw=None) == W.ERR_INVALID_ARG
     assert mm(M=1 << 26) == W.ERR_INVALID_ARG
     assert mm(M=0) == W.OK and mm(N=0) == W.OK
-    assert W.scaled_mm_workspace_size(64, 4096, 4096) == 0
+    # decode (M <= 64): int32 sums [M, N] + one counter per 64 weight rows, 256-byte rounded
+    assert W.scaled_mm_workspace_size(64, 4096, 4096) == (64 * 4096 + 64) * 4
+    assert W.scaled_mm_workspace_size(1, 100, 4096) == 512
+    assert W.scaled_mm_workspace_size(65, 4096, 4096) == 0
 
 
 def test_grouped_rejects_before_device_work(L):

@@ -120,3 +120,27 @@ def test_empty():
     s = torch.ones(8, dtype=torch.float32, device="cuda:0")
     out = W.scaled_mm_int8(xq, w, s[:1], s)
     assert out.shape == (0, 8)
+
+
+def test_decode_split_workspace_is_left_zero():
+    """The split-K decode path adds partial sums into a caller workspace and
+    must leave it all-zero after every call, whatever the shape sequence."""
+    ws = torch.zeros(W.scaled_mm_workspace_size(64, 4096, 14336) // 4, dtype=torch.int32,
+                     device="cuda:0")
+    for i, (M, K, N) in enumerate([(1, 14336, 4096), (64, 4096, 200), (17, 14336, 96),
+                                   (64, 14336, 4096), (3, 272, 64), (48, 8192, 1000)]):
+        d = _inputs(M, K, N, seed=10 + i)
+        note(f"split workspace M={M} K={K} N={N}")
+        got = W.scaled_mm_int8(to_dev(d["xq"]), to_dev(d["w"]), to_dev(d["sx"]), to_dev(d["sw"]),
+                               out_dtype=W.OUT_I32, workspace=ws)
+        torch.cuda.synchronize()
+        assert_equal(host(got), O.int_gemm(d["xq"], d["w"]).astype(np.int32), "split-K int32")
+        assert int(torch.count_nonzero(ws)) == 0
+
+
+def test_decode_without_workspace():
+    d = _inputs(9, 8192, 256, seed=20)
+    got = W.scaled_mm_int8(to_dev(d["xq"]), to_dev(d["w"]), to_dev(d["sx"]), to_dev(d["sw"]),
+                           out_dtype=W.OUT_I32, workspace=False)
+    torch.cuda.synchronize()
+    assert_equal(host(got), O.int_gemm(d["xq"], d["w"]).astype(np.int32), "unsplit int32")
