@@ -6,17 +6,24 @@ Headline workload: the decode-shaped Llama-3-8B-like linears -- M in
 (4096, 28672) gate_up, (14336, 4096) down} -- with dynamic per-token
 symmetric activation quantisation, per-channel int8 weights and a bf16 bias.
 One step runs the whole hot path on all 16 shapes: w8a8_quantize_act then
-w8a8_scaled_mm_int8 for each. The weights rotate through enough copies
-(>= 1 GiB) that no call finds its weight in the 256 MB Infinity Cache, so the
-figure is HBM bandwidth. Inputs are seeded synthetic data already resident
-in HBM when timing starts.
+w8a8_scaled_mm_int8 for each. Every call reads its own copy of the weight,
+and each shape's copies add up to >= 1 GiB, so no call finds its weight in
+the 256 MB Infinity Cache and the figure is HBM bandwidth. Inputs are seeded
+synthetic data already resident in HBM when timing starts.
 
-value = algorithmic bytes of one step / step time (GB/s); the same line
-carries the dominant kernel's roofline (HIP events around each of its
-launches on the launch stream) and the CPU oracle timed on a bounded sample.
-Prefill-shaped GEMMs (M in {2048, 8192}) are reported in "prefill" as TOPS.
+Steps are captured once as HIP graphs (one graph per step of the weight
+rotation) and replayed, so the timed region holds GPU work only, not the
+host's per-call launch cost.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-prefill]
+value = algorithmic bytes of one step / step time (GB/s). The same line
+carries the dominant kernel's roofline -- its average launch duration taken
+with HIP events on the launch stream around a graph of back-to-back launches
+-- and the CPU oracle timed on a bounded sample. The other workloads (prefill
+TOPS, the static per-tensor scheme, the MoE grouped GEMM and the FP8 weight
+conversion) are reported in their own sections, each kernel against its own
+roofline.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-prefill] [--no-extra]
 """
 
 from __future__ import annotations
@@ -33,7 +40,8 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA, TOPS
-ROTATE_BYTES = 1 << 30       # weight bytes cycled between reuses of one copy
+ROTATE_BYTES = 1 << 30       # weight bytes cycled between reuses of one copy, per shape
+GRAPH_STEPS = 16             # distinct step graphs (weight-rotation period)
 
 
 def gemm_bytes(M, K, N, bias=False, asym=False):
@@ -51,15 +59,52 @@ def quant_bytes(M, K, asym=False):
     return 3 * M * K + 4 * M + (4 * M if asym else 0)
 
 
+def grouped_bytes(E, T, K, N, rows_read):
+    return E * N * K + rows_read * K + 4 * T + 4 * E * N + 2 * T * N + 4 * (E + 1)
+
+
+def fp8_convert_bytes(E, N, K):
+    return 2 * E * N * K + 4 * E * (-(-N // 128)) * (-(-K // 128)) + 4 * E * N
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-prefill", action="store_true", help="skip the prefill TOPS section")
-    p.add_argument("--prefill-steps", type=int, default=5)
+    p.add_argument("--no-extra", action="store_true", help="skip the static / MoE / FP8 sections")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="minimum CPU time of the oracle sample")
     return p.parse_args()
+
+
+class Timer:
+    """HIP events on one stream around a region of already-enqueued work."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+
+    def graph_us(self, graph, launches, reps=3):
+        """Average microseconds per launch of a graph holding `launches` launches."""
+        torch = self.torch
+        graph.replay()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
+        for _ in range(reps):
+            graph.replay()
+        e1.record(self.stream)
+        e1.synchronize()
+        return 1e3 * e0.elapsed_time(e1) / (reps * launches)
+
+
+def capture(torch, fn):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
 
 
 def main():
@@ -77,7 +122,6 @@ def main():
 
     W.init(0)
     dev = "cuda:0"
-    stream = torch.cuda.current_stream()
 
     def to_dev(a):
         a = np.ascontiguousarray(a)
@@ -85,20 +129,24 @@ def main():
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(a).to(dev)
 
+    # Graph capture runs on a side stream; all timing happens on this one.
+    stream = torch.cuda.Stream()
+    torch.cuda.set_stream(stream)
+    timer = Timer(torch, stream)
+
     # ---------------------------------------------------------------- inputs
     shapes = [(M, K, N) for M in synth.DECODE_M for (K, N) in synth.DECODE_KN]
-    weights = {}
+    pools = {}
     for (K, N) in synth.DECODE_KN:
         d = synth.decode(64, K, N)
-        weights[(K, N)] = dict(w=to_dev(d["w"]), s_w=to_dev(d["s_w"]), bias=to_dev(d["bias"]))
-    set_bytes = sum(K * N for (K, N) in synth.DECODE_KN)
-    copies = max(2, -(-ROTATE_BYTES // set_bytes))
-    rot = {kn: [v["w"]] + [v["w"].clone() for _ in range(copies - 1)] for kn, v in weights.items()}
+        w0 = to_dev(d["w"])
+        n_copies = max(2, -(-ROTATE_BYTES // (K * N)))
+        pools[(K, N)] = dict(w=[w0] + [w0.clone() for _ in range(n_copies - 1)],
+                             s_w=to_dev(d["s_w"]), bias=to_dev(d["bias"]))
     acts = {}
     for (M, K, N) in shapes:
         d = synth.decode(M, K, N)
-        x = to_dev(d["x"])
-        acts[(M, K, N)] = dict(x=x, xq=torch.empty((M, K), dtype=torch.int8, device=dev),
+        acts[(M, K, N)] = dict(x=to_dev(d["x"]), xq=torch.empty((M, K), dtype=torch.int8, device=dev),
                                s_x=torch.empty(M, dtype=torch.float32, device=dev),
                                out=torch.empty((M, N), dtype=torch.bfloat16, device=dev))
     step_bytes = sum(gemm_bytes(M, K, N, bias=True) + quant_bytes(M, K) for (M, K, N) in shapes)
@@ -106,68 +154,81 @@ def main():
     workspace = torch.zeros(max(1, ws_bytes // 4), dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
 
-    call = [0]
-    ev_log = []
+    def gemm(shape, copy):
+        M, K, N = shape
+        a, p = acts[shape], pools[(K, N)]
+        W.scaled_mm_int8(a["xq"], p["w"][copy % len(p["w"])], a["s_x"], p["s_w"], bias=p["bias"],
+                         out=a["out"], workspace=workspace)
 
-    def step(events=False):
-        for (M, K, N) in shapes:
-            a = acts[(M, K, N)]
-            wv = weights[(K, N)]
-            w = rot[(K, N)][call[0] % copies]
-            W.quantize_act(a["x"], W.QUANT_DYN_SYM, xq=a["xq"], s_x=a["s_x"])
-            if events:
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-            W.scaled_mm_int8(a["xq"], w, a["s_x"], wv["s_w"], bias=wv["bias"], out=a["out"],
-                             workspace=workspace)
-            if events:
-                e1.record(stream)
-                ev_log.append(((M, K, N), e0, e1))
-        call[0] += 1
+    def quant(shape):
+        a = acts[shape]
+        W.quantize_act(a["x"], W.QUANT_DYN_SYM, xq=a["xq"], s_x=a["s_x"])
 
-    for _ in range(args.warmup):
-        step()
+    def step(s):
+        # call j of a (K, N) pair in step s reads weight copy 4*s + j of its pool
+        j_of = {}
+        for shape in shapes:
+            kn = shape[1:]
+            j = j_of.get(kn, 0)
+            j_of[kn] = j + 1
+            quant(shape)
+            gemm(shape, 4 * s + j)
+
+    for s in range(2):   # eager warm-up (also checks every call returns OK)
+        step(s)
+    torch.cuda.synchronize()
+    graphs = [capture(torch, lambda s=s: step(s)) for s in range(GRAPH_STEPS)]
+    torch.cuda.synchronize()
+
+    # ------------------------------------------------------ timed region
+    for i in range(args.warmup):
+        graphs[i % GRAPH_STEPS].replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        graphs[i % GRAPH_STEPS].replay()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = 1e3 * elapsed / args.steps
     value = step_bytes / (elapsed / args.steps) / 1e9
 
-    # Per-launch GEMM durations with HIP events on the launch stream, over a
-    # second pass of the same steps (the events sit between launches, so this
-    # pass is kept out of the headline timing).
-    ev_log.clear()
-    for _ in range(args.steps):
-        step(events=True)
-    torch.cuda.synchronize()
-    per_kernel = {}
-    for (M, K, N), e0, e1 in ev_log:
-        kname = "gemv_i8_kernel<MF=%d>" % (1 if M <= 16 else 2 if M <= 32 else 3 if M <= 48 else 4)
-        ms = e0.elapsed_time(e1)
-        agg = per_kernel.setdefault(kname, dict(launches=0, ms=0.0, bytes=0))
+    # ---------------------------------------- per-kernel launch durations
+    # One graph per shape of back-to-back launches over that shape's weight
+    # copies; HIP events on the launch stream around its replays.
+    per_shape, per_kernel = {}, {}
+    for shape in shapes:
+        M, K, N = shape
+        n = len(pools[(K, N)]["w"])
+        R = n * max(1, -(-64 // n))
+        g = capture(torch, lambda: [gemm(shape, c) for c in range(R)])
+        us = timer.graph_us(g, R)
+        gq = capture(torch, lambda: [quant(shape) for _ in range(32)])
+        qus = timer.graph_us(gq, 32)
+        del g, gq
+        kname = W.scaled_mm_kernel_name(M, N, K)
+        b = gemm_bytes(M, K, N, bias=True)
+        per_shape[f"{M}x{K}x{N}"] = {"kernel": kname, "gemm_us": round(us, 3),
+                                     "GBs": round(b / (us * 1e-6) / 1e9, 1),
+                                     "quant_us": round(qus, 3)}
+        agg = per_kernel.setdefault(kname, dict(launches=0, us=0.0, bytes=0))
         agg["launches"] += 1
-        agg["ms"] += ms
-        agg["bytes"] += gemm_bytes(M, K, N, bias=True)
-    dom_name, dom = max(per_kernel.items(), key=lambda kv: kv[1]["ms"])
-    avg_us = 1e3 * dom["ms"] / dom["launches"]
-    achieved = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
+        agg["us"] += us
+        agg["bytes"] += b
+        qname = "quant_kernel (dynamic symmetric)"
+        agg = per_kernel.setdefault(qname, dict(launches=0, us=0.0, bytes=0))
+        agg["launches"] += 1
+        agg["us"] += qus
+        agg["bytes"] += quant_bytes(M, K)
+    dom_name, dom = max(per_kernel.items(), key=lambda kv: kv[1]["us"])
+    avg_us = dom["us"] / dom["launches"]
+    achieved = dom["bytes"] / (dom["us"] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                 "kernel": dom_name, "avg_launch_us": round(avg_us, 3),
                 "bytes_per_launch": int(dom["bytes"] / dom["launches"])}
-    kernels = {k: {"launches_per_step": v["launches"] // args.steps,
-                   "avg_us": round(1e3 * v["ms"] / v["launches"], 3),
-                   "GBs": round(v["bytes"] / (v["ms"] * 1e-3) / 1e9, 1)} for k, v in per_kernel.items()}
-    per_shape = {}
-    for (M, K, N), e0, e1 in ev_log:
-        per_shape.setdefault(f"{M}x{K}x{N}", []).append(e0.elapsed_time(e1))
-    shapes_out = {k: {"us": round(1e3 * float(np.median(v)), 2),
-                      "GBs": round(gemm_bytes(*map(int, k.split("x")), bias=True) / (np.median(v) * 1e-3) / 1e9, 1)}
-                  for k, v in per_shape.items()}
+    kernels = {k: {"launches_per_step": v["launches"], "avg_us": round(v["us"] / v["launches"], 3),
+                   "GBs": round(v["bytes"] / (v["us"] * 1e-6) / 1e9, 1)} for k, v in per_kernel.items()}
+    del graphs
 
     # ------------------------------------------------------------ prefill TOPS
     prefill = None
@@ -181,53 +242,30 @@ def main():
                 xq, s_x, zp = W.quantize_act(x, W.QUANT_DYN_ASYM)
                 cs = W.prepare_colsum(w)
                 out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-                for _ in range(2):
-                    W.scaled_mm_int8(xq, w, s_x, s_w, zp=zp, colsum=cs, azp_mode=W.AZP_PER_TOKEN, out=out)
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                for _ in range(args.prefill_steps):
-                    W.scaled_mm_int8(xq, w, s_x, s_w, zp=zp, colsum=cs, azp_mode=W.AZP_PER_TOKEN, out=out)
-                e1.record(stream)
-                q0 = torch.cuda.Event(enable_timing=True)
-                q1 = torch.cuda.Event(enable_timing=True)
-                q0.record(stream)
-                for _ in range(args.prefill_steps):
-                    W.quantize_act(x, W.QUANT_DYN_ASYM, xq=xq, s_x=s_x, zp=zp)
-                q1.record(stream)
-                torch.cuda.synchronize()
-                us = 1e3 * e0.elapsed_time(e1) / args.prefill_steps
-                qus = 1e3 * q0.elapsed_time(q1) / args.prefill_steps
+                R = 5
+                g = capture(torch, lambda: [W.scaled_mm_int8(xq, w, s_x, s_w, zp=zp, colsum=cs,
+                                                             azp_mode=W.AZP_PER_TOKEN, out=out)
+                                            for _ in range(R)])
+                us = timer.graph_us(g, R)
+                gq = capture(torch, lambda: [W.quantize_act(x, W.QUANT_DYN_ASYM, xq=xq, s_x=s_x, zp=zp)
+                                             for _ in range(R)])
+                qus = timer.graph_us(gq, R)
+                del g, gq
                 tops = 2.0 * M * N * K / (us * 1e-6) / 1e12
-                prefill[f"{M}x{K}x{N}"] = {"gemm_us": round(us, 1), "TOPS": round(tops, 1),
+                prefill[f"{M}x{K}x{N}"] = {"kernel": W.scaled_mm_kernel_name(M, N, K),
+                                           "gemm_us": round(us, 1), "TOPS": round(tops, 1),
                                            "frac": round(tops / INT8_PEAK_TOPS, 4),
                                            "quant_us": round(qus, 1),
                                            "quant_GBs": round(quant_bytes(M, K, True) / (qus * 1e-6) / 1e9, 1)}
                 del x, w, xq, out
         torch.cuda.synchronize()
 
+    extra = None if args.no_extra else extra_sections(torch, np, W, synth, to_dev, timer, dev)
+
     # ------------------------------------------------------------- CPU oracle
     cpu = None
     if not args.no_cpu:
-        import oracle as O
-        try:
-            from threadpoolctl import threadpool_info
-            blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-        except Exception:  # pragma: no cover
-            blas_threads = None
-        sample = [(M, K, N) for (M, K, N) in shapes if M in (1, 64)]
-        t0 = time.perf_counter()
-        nbytes = 0
-        for (M, K, N) in sample:
-            d = synth.decode(M, K, N)
-            O.linear_forward(d["x"], d["w"], d["s_w"], O.MODE_DYN_SYM, bias_bits=d["bias"])
-            nbytes += gemm_bytes(M, K, N, bias=True) + quant_bytes(M, K)
-        cpu_s = time.perf_counter() - t0
-        cpu = {"value": round(nbytes / cpu_s / 1e9, 3), "unit": "GB/s",
-               "cores": blas_threads or len(os.sched_getaffinity(0)), "kind": "oracle",
-               "sample": "oracle linear_forward (quantize + GEMM + epilogue) on the 8 decode shapes "
-                         "with M in {1, 64}, once each; input generation excluded",
-               "seconds": round(cpu_s, 2), "host_cpus": len(os.sched_getaffinity(0))}
+        cpu = cpu_baseline(np, synth, shapes, args.cpu_seconds)
 
     line = {
         "metric": "INT8 scaled-GEMM TOPS (prefill) and GB/s (decode), % of MI355X roofline",
@@ -241,19 +279,140 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "int8",
-        "data": "synthetic (seeded), resident in HBM; weights rotated over >=1 GiB",
+        "data": "synthetic (seeded), resident in HBM; each shape's weight rotated over >= 1 GiB of copies",
         "config": {"workload": "decode: M in {1,8,32,64} x (K,N) in {(4096,6144),(4096,4096),"
                                "(4096,28672),(14336,4096)}; dynamic per-token symmetric quant + "
                                "scaled int8 GEMM with bf16 bias",
-                   "shapes": len(shapes), "weight_copies": copies, "parallelism": "single GPU"},
+                   "shapes": len(shapes), "step_bytes": step_bytes, "timing": "HIP graph replay",
+                   "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kernels,
-        "decode_shapes": shapes_out,
+        "decode_shapes": per_shape,
         "prefill": prefill,
+        "extra": extra,
     }
     print(json.dumps(line))
     return 0
+
+
+def extra_sections(torch, np, W, synth, to_dev, timer, dev):
+    """The static per-tensor scheme, the MoE grouped GEMM and the FP8 weight
+    conversion, each timed as a graph of back-to-back launches."""
+    out = {}
+
+    # Static per-tensor scheme: fused QKV, M=512, K=4096, N=6144.
+    d = synth.static_qkv()
+    M, K = d["x"].shape
+    N = d["w"].shape[0]
+    x, w = to_dev(d["x"]), to_dev(d["w"])
+    ps = to_dev(d["part_scales"])
+    s_in = to_dev(np.array([d["s_in"]], np.float32))
+    zp_in = to_dev(np.array([d["zp_in"]], np.int32))
+    s_max = W.prepare_requant_max(w, ps, d["widths"])
+    adj = W.prepare_colsum(w, zp_in=zp_in)
+    xq = torch.empty((M, K), dtype=torch.int8, device=dev)
+    o = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    one = torch.ones(1, dtype=torch.float32, device=dev)
+    R = 20
+    g = capture(torch, lambda: [W.quantize_act(x, W.QUANT_STATIC_ASYM, s_in=s_in, zp_in=zp_in, xq=xq)
+                                for _ in range(R)])
+    qus = timer.graph_us(g, R)
+    g = capture(torch, lambda: [W.scaled_mm_int8(xq, w, s_in, s_max, colsum=adj, azp_mode=W.AZP_STATIC,
+                                                 out=o) for _ in range(R)])
+    us = timer.graph_us(g, R)
+    del g
+    tops = 2.0 * M * N * K / (us * 1e-6) / 1e12
+    gb = gemm_bytes(M, K, N, asym=True)
+    out["static_qkv_512x4096x6144"] = {
+        "kernel": W.scaled_mm_kernel_name(M, N, K), "gemm_us": round(us, 2), "TOPS": round(tops, 1),
+        "mfma_frac": round(tops / INT8_PEAK_TOPS, 4), "GBs": round(gb / (us * 1e-6) / 1e9, 1),
+        "hbm_frac": round(gb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "quant_us": round(qus, 2)}
+    del x, w, xq, o, one
+
+    # MoE: FP8 -> int8 conversion of the expert weights, then the two grouped GEMMs.
+    m = synth.moe()
+    E = synth.MOE_E
+    T = m["row_ids"].shape[0]
+    rows = to_dev(m["row_ids"])
+    offs = to_dev(m["offsets"])
+    conv = {}
+    qw = {}
+    for name in ("w13", "w2"):
+        codes, S = to_dev(m[name + "_fp8"]), to_dev(m[name + "_scales"])
+        _, Nn, Kk = codes.shape
+        Wq, s, flag = W.prepare_fp8_block_to_int8(codes, S)
+        g = capture(torch, lambda: [W.prepare_fp8_block_to_int8(codes, S, Wq=Wq, s=s, err_flag=flag)
+                                    for _ in range(3)])
+        us = timer.graph_us(g, 3)
+        del g
+        b = fp8_convert_bytes(E, Nn, Kk)
+        conv[f"{name}_{E}x{Nn}x{Kk}"] = {"us": round(us, 1), "GBs": round(b / (us * 1e-6) / 1e9, 1),
+                                         "hbm_frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        qw[name] = (Wq, s)
+        del codes, S
+    out["fp8_block_to_int8"] = conv
+
+    x13 = to_dev(m["x13"])
+    x2 = to_dev(m["x2"])
+    xq13, sx13, _ = W.quantize_act(x13, W.QUANT_DYN_SYM)
+    xq2, sx2, _ = W.quantize_act(x2, W.QUANT_DYN_SYM)
+    moe = {}
+    for name, xq_, sx_, rid, Kk in (("w13", xq13, sx13, rows, synth.MOE_HIDDEN),
+                                     ("w2", xq2, sx2, None, synth.MOE_INTER)):
+        Wq, s = qw[name]
+        Nn = Wq.shape[1]
+        o = torch.empty((T, Nn), dtype=torch.bfloat16, device=dev)
+        R = 5
+        g = capture(torch, lambda: [W.grouped_scaled_mm_int8(xq_, offs, Wq, sx_, s, row_ids=rid, T=T, out=o)
+                                    for _ in range(R)])
+        us = timer.graph_us(g, R)
+        del g
+        tops = 2.0 * T * Nn * Kk / (us * 1e-6) / 1e12
+        b = grouped_bytes(E, T, Kk, Nn, T)
+        moe[f"{name}_T{T}_K{Kk}_N{Nn}"] = {
+            "gemm_us": round(us, 1), "TOPS": round(tops, 1), "mfma_frac": round(tops / INT8_PEAK_TOPS, 4),
+            "GBs": round(b / (us * 1e-6) / 1e9, 1), "hbm_frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        del o
+    R = 5
+    g = capture(torch, lambda: [W.quantize_act(x2, W.QUANT_DYN_SYM, xq=xq2, s_x=sx2) for _ in range(R)])
+    qus = timer.graph_us(g, R)
+    del g
+    moe["quant_w2_input_32768x1536"] = {"us": round(qus, 1),
+                                         "GBs": round(quant_bytes(T, 1536) / (qus * 1e-6) / 1e9, 1)}
+    out["moe_grouped"] = moe
+    torch.cuda.synchronize()
+    return out
+
+
+def cpu_baseline(np, synth, shapes, min_seconds):
+    """The oracle, as written, on the decode workload: whole steps (all 16
+    shapes, quantise + GEMM + epilogue) until at least min_seconds of CPU
+    time have passed. Input generation is outside the timing."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = None
+    data = {s: synth.decode(*s) for s in shapes}
+    nbytes = 0
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        for (M, K, N) in shapes:
+            d = data[(M, K, N)]
+            O.linear_forward(d["x"], d["w"], d["s_w"], O.MODE_DYN_SYM, bias_bits=d["bias"])
+            nbytes += gemm_bytes(M, K, N, bias=True) + quant_bytes(M, K)
+        steps += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    cpu_s = time.perf_counter() - t0
+    return {"value": round(nbytes / cpu_s / 1e9, 3), "unit": "GB/s",
+            "cores": blas_threads or len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"{steps} whole decode step(s) of the oracle (all 16 shapes: quantise + GEMM + "
+                      f"epilogue); input generation excluded",
+            "seconds": round(cpu_s, 2), "host_cpus": len(os.sched_getaffinity(0))}
 
 
 if __name__ == "__main__":

@@ -234,6 +234,11 @@ w8a8_status w8a8_grouped_scaled_mm_int8(const int8_t* xq, int64_t ldx, int64_t M
                                         const uint16_t* bias, void* out, int32_t out_dtype,
                                         int64_t ldo, void* stream);
 
+/* Name of the kernel template instance that w8a8_scaled_mm_int8 launches
+ * for an M x N x K problem (static storage; "" for an empty or invalid
+ * shape). Profilers list kernels by these names; no device is touched. */
+const char* w8a8_scaled_mm_kernel_name(int64_t M, int64_t N, int64_t K);
+
 /* Human-readable name of a status code (static storage). */
 const char* w8a8_status_string(w8a8_status status);
 

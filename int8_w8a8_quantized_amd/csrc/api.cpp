@@ -333,6 +333,11 @@ w8a8_status w8a8_grouped_scaled_mm_int8(const int8_t* xq, int64_t ldx, int64_t M
   return hip_status(w8a8::launch_grouped_mm(a, static_cast<hipStream_t>(stream)), "grouped_mm launch");
 }
 
+const char* w8a8_scaled_mm_kernel_name(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0) return "";
+  return (M <= w8a8::kDecodeMaxM) ? w8a8::decode_kernel_name(M) : w8a8::scaled_mm_kernel_name(M, N, K);
+}
+
 const char* w8a8_status_string(w8a8_status s) {
   switch (s) {
     case W8A8_OK: return "W8A8_OK";

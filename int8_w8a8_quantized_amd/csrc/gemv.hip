@@ -170,6 +170,13 @@ size_t decode_workspace_bytes(int64_t M, int64_t N) {
   return (b + 255) & ~size_t(255);
 }
 
+const char* decode_kernel_name(int64_t M) {
+  if (M <= 16) return "gemv_i8_kernel<1, 4>";
+  if (M <= 32) return "gemv_i8_kernel<2, 4>";
+  if (M <= 48) return "gemv_i8_kernel<3, 2>";
+  return "gemv_i8_kernel<4, 2>";
+}
+
 hipError_t launch_decode_mm(const GemmArgs& a, void* workspace, size_t ws_bytes, int num_cus,
                             hipStream_t stream) {
   const int64_t tiles = (a.N + kTN - 1) / kTN;

@@ -58,6 +58,9 @@ hipError_t launch_scaled_mm(const GemmArgs& a, hipStream_t stream);  // MFMA til
 hipError_t launch_decode_mm(const GemmArgs& a, void* workspace, size_t ws_bytes, int num_cus,
                             hipStream_t stream);
 size_t decode_workspace_bytes(int64_t M, int64_t N);
+// Name of the kernel instance launch_decode_mm / launch_scaled_mm runs for a shape.
+const char* decode_kernel_name(int64_t M);
+const char* scaled_mm_kernel_name(int64_t M, int64_t N, int64_t K);
 constexpr int64_t kDecodeMaxM = 64;
 hipError_t launch_grouped_mm(const GemmArgs& a, hipStream_t stream);
 

@@ -54,6 +54,7 @@ _SIGS = {
                                    _p, _p, _i32, _p, _p, _i32, _i64, _p, ctypes.c_size_t, _p]),
     "w8a8_grouped_scaled_mm_int8": (_i32, [_p, _i64, _i64, _p, _p, _i64, _i64, _i64, _i64, _p,
                                            _p, _p, _p, _p, _i32, _i64, _p]),
+    "w8a8_scaled_mm_kernel_name": (ctypes.c_char_p, [_i64, _i64, _i64]),
     "w8a8_status_string": (ctypes.c_char_p, [_i32]),
     "w8a8_last_error": (ctypes.c_char_p, []),
 }
@@ -194,6 +195,11 @@ def prepare_fp8_block_to_int8(W8, S, Wq=None, s=None, err_flag=None):
 
 def scaled_mm_workspace_size(M: int, N: int, K: int) -> int:
     return int(load().w8a8_scaled_mm_workspace_size(M, N, K))
+
+
+def scaled_mm_kernel_name(M: int, N: int, K: int) -> str:
+    """Name of the kernel instance scaled_mm_int8 launches for this shape."""
+    return load().w8a8_scaled_mm_kernel_name(M, N, K).decode()
 
 
 _ws_cache = {}
