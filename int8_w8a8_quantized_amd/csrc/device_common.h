@@ -24,6 +24,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// Two floats -> two bf16 packed in one word (low half = a), round to nearest
+// even, by gfx950's v_cvt_pk_bf16_f32 (quiet NaN stays NaN).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
 // Round to nearest integer, ties to even (v_rndne_f32).
 __device__ __forceinline__ float rne(float v) { return __builtin_rintf(v); }
 

@@ -6,56 +6,74 @@
 // (4.2), with the scale / zero-point / bias epilogue of the same page (§3-§4)
 // fused into the store.
 //
-// Both operands are K-contiguous ("NT"). A workgroup of 4 waves owns a
-// BM x BN output tile and walks K in BK-byte steps: each thread moves 16-byte
-// chunks of the A and B tiles from HBM into registers, then into LDS (rows
-// padded by 16 bytes so the 16-byte fragment reads of a wave hit distinct
-// banks), double-buffered so the global loads of step k+1 are in flight while
-// the MFMAs of step k run. Each wave computes a (BM/2) x (BN/2) sub-tile as a
-// grid of 16x16 int32 accumulators with v_mfma_i32_16x16x64_i8.
+// Both operands are K-contiguous ("NT"). A workgroup of 4 waves (2 x 2) owns
+// a BM x BN output tile; each wave computes a (BM/2) x (BN/2) sub-tile as a
+// grid of 32x32 int32 accumulators with v_mfma_i32_32x32x32_i8 (the form that
+// runs at the full int8 rate on gfx950). At 256 x 256 a wave holds 128 x 128
+// accumulators (256 AGPRs), so every 16-byte fragment read from LDS feeds
+// four MFMAs.
 //
-// Tile order: workgroup ids are spread round-robin over the 8 XCDs, so the
-// linear id is first remapped to give each XCD a contiguous range of tiles,
-// which are then walked in groups of 8 tile-rows so that neighbouring
-// workgroups share A and B tiles in that XCD's L2.
+// Main kernel (K a multiple of 64): tiles travel HBM -> LDS with the gfx950
+// direct-to-LDS load (global_load_lds_dwordx4: each lane's 16 bytes land at
+// the wave's LDS base + 16 * lane, no registers involved) into a ring of NS
+// LDS stages of BK = 128 (or 64) bytes of K, so NS - 1 K steps are in flight
+// while the MFMAs of another run. One wave instruction fills 64 / (BK / 16)
+// rows of BK bytes; the 16-byte chunks of row r sit at a chunk position
+// XOR-swizzled by bits of r (swz), which makes the MFMA fragment reads (32
+// rows x one chunk per wave) hit distinct banks whether the LDS serves 8 or
+// 16 lanes of a 16-byte read per cycle. Rows past the end of the matrix
+// load a valid row instead; they only feed outputs the epilogue never
+// stores. One barrier per K step both publishes the stage that just landed
+// and retires the stage the next load overwrites, and the step's
+// instructions are ordered explicitly (sched_group_barrier) so that LDS
+// reads and the next stage's loads slot in between MFMAs.
 //
-// The grouped variant maps each workgroup to (expert, m-tile of that
-// expert's row range, n-tile) by scanning expert_offsets; rows may be
-// gathered through row_ids in the A load.
+// General kernel (any K that is a multiple of 16): the same tile and
+// epilogue, with tiles staged through registers (zero-filled past K) into two
+// padded LDS buffers.
+//
+// Tile order: workgroups are dealt round-robin to the 8 XCDs, so the linear
+// id is first remapped to give each XCD a contiguous range of tiles, which
+// are then walked in groups of 8 tile-rows so that the workgroups running
+// together on one XCD share A and B tiles in its L2. The grouped variant maps
+// each workgroup to (expert, m-tile of that expert's row range, n-tile) by
+// scanning expert_offsets; rows may be gathered through row_ids.
+
+#include <type_traits>
 
 #include "gemm_common.h"
 
 namespace w8a8 {
 
-template <int BM, int BN, int BK, bool GROUPED>
-__global__ __launch_bounds__(256) void gemm_i8_kernel(GemmArgs a, int tiles_m, int tiles_n) {
-  constexpr int NT = 256;
-  constexpr int WM = 2, WN = 2;
-  constexpr int STRIDE = BK + 16;
-  constexpr int TM = BM / WM, TN = BN / WN;
-  constexpr int FM = TM / 16, FN = TN / 16;
-  constexpr int KC = BK / 16;
-  constexpr int A_PER_T = BM * KC / NT, B_PER_T = BN * KC / NT;
-  static_assert(BM * KC % NT == 0 && BN * KC % NT == 0, "tile / thread mismatch");
-  static_assert(BK % 64 == 0, "BK is a multiple of the MFMA k");
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(1))) void* global_void_ptr;
 
-  __shared__ __attribute__((aligned(16))) int8_t smem[2 * (BM + BN) * STRIDE];
+// Linear workgroup id -> logical tile id such that XCD x (which receives
+// workgroups x, x+8, x+16, ...) processes a contiguous range of tiles.
+__device__ __forceinline__ int xcd_remap(int pid, int nwg) {
+  constexpr int kXcds = 8;
+  const int xcd = pid % kXcds, local = pid / kXcds;
+  const int base = nwg / kXcds, extra = nwg % kXcds;
+  return xcd * base + min(xcd, extra) + local;
+}
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
+struct TileLoc {
+  int64_t row_begin, row_end;  // output rows [row_begin, min(row_begin + BM, row_end))
+  int64_t n_begin;
+  int64_t expert;              // -1: no work for this workgroup
+};
 
-  // ---- which tile
-  int tn;
-  int64_t row_begin, row_end;
-  const int8_t* B = a.B;
-  const float* sw = a.s_w;
-  const uint16_t* bias = a.bias;
+template <int BM, int BN, bool GROUPED>
+__device__ __forceinline__ TileLoc locate_tile(const GemmArgs& a, int tiles_m, int tiles_n) {
+  TileLoc t;
+  const int pid = xcd_remap(blockIdx.x, gridDim.x);
   if (GROUPED) {
-    const int mt = blockIdx.x / tiles_n;
-    tn = blockIdx.x % tiles_n;
+    const int mt = pid / tiles_n;
+    t.n_begin = (int64_t)(pid % tiles_n) * BN;
+    t.expert = -1;
+    t.row_begin = t.row_end = 0;
     const int64_t T = a.M;
-    int64_t cum = 0, e_found = -1;
-    int64_t prev = 0;
+    int64_t cum = 0, prev = 0;
     for (int64_t e = 0; e < a.E; ++e) {
       int64_t s0 = a.expert_offsets[e], s1 = a.expert_offsets[e + 1];
       s0 = min(max(s0, prev), T);
@@ -63,32 +81,343 @@ __global__ __launch_bounds__(256) void gemm_i8_kernel(GemmArgs a, int tiles_m, i
       prev = s0;
       const int64_t t_e = (s1 - s0 + BM - 1) / BM;
       if (mt < cum + t_e) {
-        e_found = e;
-        row_begin = s0 + (int64_t)(mt - cum) * BM;
-        row_end = s1;
+        t.expert = e;
+        t.row_begin = s0 + (int64_t)(mt - cum) * BM;
+        t.row_end = s1;
         break;
       }
       cum += t_e;
     }
-    if (e_found < 0) return;
-    B += e_found * a.N * a.ldb;
-    sw += e_found * a.N;
-    if (bias) bias += e_found * a.N;
   } else {
-    int pid = blockIdx.x;
-    const int nwg = gridDim.x;
-    if ((nwg & 7) == 0) pid = (pid & 7) * (nwg >> 3) + (pid >> 3);
     constexpr int GM = 8;
     const int group = pid / (GM * tiles_n);
     const int first_m = group * GM;
     const int gsz = min(tiles_m - first_m, GM);
     const int in_group = pid % (GM * tiles_n);
-    const int tm = first_m + in_group % gsz;
-    tn = in_group / gsz;
-    row_begin = (int64_t)tm * BM;
-    row_end = a.M;
+    t.row_begin = (int64_t)(first_m + in_group % gsz) * BM;
+    t.row_end = a.M;
+    t.n_begin = (int64_t)(in_group / gsz) * BN;
+    t.expert = 0;
   }
-  const int64_t n_begin = (int64_t)tn * BN;
+  return t;
+}
+
+// Source row of output row gr (gathered through row_ids in the grouped GEMM),
+// or -1 for a row id outside [0, M_src): such a row counts as all zeros. The
+// loads then read row 0 instead (a valid address) and the epilogue discards
+// the sums.
+template <bool GROUPED>
+__device__ __forceinline__ int64_t source_row(const GemmArgs& a, int64_t gr) {
+  if (GROUPED && a.row_ids) {
+    const int64_t s = a.row_ids[gr];
+    return (s >= 0 && s < a.M_src) ? s : -1;
+  }
+  return gr;
+}
+
+// The fused epilogue, one 32-row slab of the wave's sub-tile at a time: the
+// slab's accumulators go to LDS in MFMA layout (lane = column), come back
+// row-contiguous (4 consecutive columns per lane), get the zero-point
+// correction, scales and bias, and leave as 8-byte bf16 (or 16-byte int32)
+// stores that cover whole row segments. The tile's per-row parameters
+// (source row, token scale, zero point) are fetched once into LDS first, so
+// the row passes wait on no global load. `smem` must hold
+// epilogue_lds_bytes<BM, BN>() bytes and be free: the caller has passed a
+// barrier after its last read.
+template <int BM, int BN>
+constexpr int epilogue_lds_bytes() {
+  return 4 * 32 * (BN / 2 + 8) * 4 + BM * 12;
+}
+
+template <int BM, int BN, bool GROUPED>
+__device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const TileLoc& t, const float* sw,
+                                              const uint16_t* bias, int8_t* smem,
+                                              i32x16 (&acc)[BM / 64][BN / 64]) {
+  constexpr int TM = BM / 2, TN = BN / 2, FM = TM / 32, FN = TN / 32;
+  constexpr int CSTRIDE = TN + 8;  // int32 words; rows 4 apart land 32 banks apart
+  constexpr int LANES_PER_ROW = TN / 4;
+  constexpr int ROWS_PER_PASS = 64 / LANES_PER_ROW;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int frag_row = lane & 31;
+  int32_t* slab = reinterpret_cast<int32_t*>(smem) + wave * 32 * CSTRIDE;
+  const int c4 = (lane * 4) % TN;  // first of this lane's 4 columns
+  const int lrow = (lane * 4) / TN;  // row of this lane within a pass
+  const int64_t col0 = t.n_begin + wn * TN + c4;
+  float csw[4], cbias[4];
+  int ccorr[4];
+  bool cok[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const EpiCol c = load_col(a, col0 + q, sw, bias);
+    csw[q] = c.sw;
+    cbias[q] = c.bias;
+    ccorr[q] = c.corr;
+    cok[q] = c.ok;
+  }
+  const bool vec_store = cok[3] && (a.ldo % 4 == 0);
+
+  // per-row parameters of the tile: source row (-1: all-zero row, or past the
+  // end), token scale, zero point
+  int* row_src = reinterpret_cast<int*>(smem + 4 * 32 * CSTRIDE * 4);
+  float* row_sx = reinterpret_cast<float*>(row_src + BM);
+  int* row_zp = row_src + 2 * BM;
+  for (int r = threadIdx.x; r < BM; r += 256) {
+    const int64_t gr = t.row_begin + r;
+    const int64_t src = gr < t.row_end ? source_row<GROUPED>(a, gr) : -1;
+    const int64_t s0 = src > 0 ? src : 0;
+    row_src[r] = (int)src;
+    row_sx[r] = a.sx_per_token ? a.s_x[s0] : a.s_x[0];
+    row_zp[r] = (a.azp_mode == 1) ? a.zp[s0] : 0;
+  }
+
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        slab[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * CSTRIDE + j * 32 + frag_row] = acc[i][j][r];
+    __syncthreads();
+#pragma unroll 4
+    for (int p = 0; p < 32 / ROWS_PER_PASS; ++p) {
+      const int lr = p * ROWS_PER_PASS + lrow;
+      const int4 v = *reinterpret_cast<const int4*>(slab + lr * CSTRIDE + c4);
+      const int tr = wm * TM + i * 32 + lr;  // row within the tile
+      const int64_t gr = t.row_begin + tr;
+      if (gr >= t.row_end) continue;
+      int c[4] = {v.x, v.y, v.z, v.w};
+      if (row_src[tr] < 0) c[0] = c[1] = c[2] = c[3] = 0;
+      if (a.azp_mode == 1) {
+        const int zp = row_zp[tr];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) c[q] -= zp * ccorr[q];
+      } else if (a.azp_mode == 2) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) c[q] -= ccorr[q];
+      }
+      if (a.out_i32) {
+        int32_t* o = reinterpret_cast<int32_t*>(a.out) + gr * a.ldo + col0;
+        if (vec_store) {
+          *reinterpret_cast<int4*>(o) = make_int4(c[0], c[1], c[2], c[3]);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (cok[q]) o[q] = c[q];
+        }
+      } else {
+        const float sx = row_sx[tr];
+        float y[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          y[q] = (float)c[q] * sx * csw[q];
+          if (a.bias) y[q] += cbias[q];
+        }
+        const uint32_t h01 = pack_bf16x2(y[0], y[1]), h23 = pack_bf16x2(y[2], y[3]);
+        uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + gr * a.ldo + col0;
+        if (vec_store) {
+          *reinterpret_cast<uint2*>(o) = make_uint2(h01, h23);
+        } else {
+          const uint16_t h[4] = {(uint16_t)h01, (uint16_t)(h01 >> 16), (uint16_t)h23,
+                                 (uint16_t)(h23 >> 16)};
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (cok[q]) o[q] = h[q];
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Workgroup barrier without the memory fence __syncthreads() carries (which
+// would wait for every load in flight, including the prefetched stages). The
+// ordering the direct-to-LDS ring needs is explicit: each wave waits for its
+// own loads of the stage with s_waitcnt vmcnt before the barrier, and the
+// "memory" clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void barrier_no_fence() { __asm__ volatile("s_barrier" ::: "memory"); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// ---------------------------------------------------------------- main kernel
+// Chunk position of logical 16-byte chunk c in tile row r (CH chunks per
+// row): distinct banks for the fragment reads of 8 consecutive rows (32-bank
+// view) and of 16 consecutive rows (64-bank view). Depends on bits 0-4 of r
+// only, so rows 32 apart (the MFMA blocks of one wave) share it.
+template <int CH>
+__device__ __forceinline__ int swz(int r) {
+  return CH == 4 ? (((r >> 1) ^ (r >> 3)) & 3) : ((r ^ ((r >> 3) & 3)) & 7);
+}
+
+template <int BM, int BN, int BK, int NS, bool GROUPED>
+__global__ __launch_bounds__(256) void gemm_i8_dma_kernel(GemmArgs a, int tiles_m, int tiles_n) {
+  constexpr int STAGE = (BM + BN) * BK;
+  constexpr int TM = BM / 2, TN = BN / 2, FM = TM / 32, FN = TN / 32;
+  constexpr int CH = BK / 16;                 // 16-byte chunks per tile row
+  constexpr int RPI = 64 / CH;                // tile rows per 1-KiB load instruction
+  constexpr int AI = BM / RPI / 4, BI = BN / RPI / 4;  // load instructions per wave per stage
+  constexpr int PER_STAGE = AI + BI;
+  constexpr int KS = BK / 32;                 // MFMA k slices per stage
+  static_assert(CH == 4 || CH == 8, "BK is 64 or 128");
+  static_assert(BM % (4 * RPI) == 0 && BN % (4 * RPI) == 0, "tile / load mismatch");
+  static_assert(NS >= 2 && (NS - 2) * PER_STAGE <= 63, "stages / vmcnt range");
+  static_assert(epilogue_lds_bytes<BM, BN>() <= NS * STAGE, "epilogue does not fit the LDS");
+
+  __shared__ __attribute__((aligned(1024))) int8_t smem[NS * STAGE];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  const TileLoc t = locate_tile<BM, BN, GROUPED>(a, tiles_m, tiles_n);
+  if (t.expert < 0) return;
+  const int8_t* B = a.B + t.expert * a.N * a.ldb;
+  const float* sw = a.s_w + (GROUPED ? t.expert * a.N : 0);
+  const uint16_t* bias = (GROUPED && a.bias) ? a.bias + t.expert * a.N : a.bias;
+
+  // ---- per-lane DMA sources: instruction q of this wave fills tile rows
+  // (wave*AI + q)*RPI .. +RPI-1; lane l writes row +l/CH, physical chunk
+  // l%CH, which holds logical chunk (l%CH) ^ swz(row).
+  const int lrow = lane / CH, pch = lane % CH;
+  const int8_t* a_src[AI];
+#pragma unroll
+  for (int q = 0; q < AI; ++q) {
+    const int r = (wave * AI + q) * RPI + lrow;
+    const int64_t gr = min(t.row_begin + r, t.row_end - 1);
+    const int64_t src = source_row<GROUPED>(a, gr);
+    a_src[q] = a.A + (src > 0 ? src : 0) * a.lda + (pch ^ swz<CH>(r)) * 16;
+  }
+  const int8_t* b_src[BI];
+#pragma unroll
+  for (int q = 0; q < BI; ++q) {
+    const int r = (wave * BI + q) * RPI + lrow;
+    const int64_t n = min(t.n_begin + r, a.N - 1);
+    b_src[q] = B + n * a.ldb + (pch ^ swz<CH>(r)) * 16;
+  }
+  // Loads K step kt_src into LDS stage kt_dst % NS.
+  auto issue = [&](int kt_src, int kt_dst) __attribute__((always_inline)) {
+    int8_t* st = smem + (kt_dst % NS) * STAGE;
+    const int64_t k0 = (int64_t)kt_src * BK;
+#pragma unroll
+    for (int q = 0; q < AI; ++q)
+      __builtin_amdgcn_global_load_lds((global_void_ptr)(a_src[q] + k0),
+                                       (lds_void_ptr)(st + (wave * AI + q) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int q = 0; q < BI; ++q)
+      __builtin_amdgcn_global_load_lds((global_void_ptr)(b_src[q] + k0),
+                                       (lds_void_ptr)(st + BM * BK + (wave * BI + q) * 1024), 16, 0,
+                                       0);
+  };
+
+  // ---- fragment reads: lane reads tile row (.. + lane%32), logical chunk
+  // 2*ks + lane/32 of the BK-byte row; rows 32 apart share swz().
+  const int fr = lane & 31;
+  const int fsw = swz<CH>(fr);
+  const int a_base = wm * TM * BK + fr * BK, b_base = BM * BK + wn * TN * BK + fr * BK;
+  i32x4 fa[2][FM], fb[2][FN];
+  auto read_frags = [&](const int8_t* st, int ks, int slot) __attribute__((always_inline)) {
+    const int off = ((2 * ks + (lane >> 5)) ^ fsw) * 16;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      fa[slot][i] = *reinterpret_cast<const i32x4*>(st + a_base + i * 32 * BK + off);
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      fb[slot][j] = *reinterpret_cast<const i32x4*>(st + b_base + j * 32 * BK + off);
+  };
+
+  i32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+
+  const int nk = (int)(a.K / BK);
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s) issue(min(s, nk - 1), s);
+
+  for (int kt = 0; kt < nk; ++kt) {
+    // This wave's loads of stage kt are done once at most the NS - 2 stages
+    // issued after it remain outstanding (every step issues exactly one
+    // stage, so the count is the same each time).
+    wait_vmcnt<(NS - 2) * PER_STAGE>();
+    barrier_no_fence();  // every wave's part of stage kt has landed; stage kt-1 is retired
+    const int8_t* st = smem + (kt % NS) * STAGE;
+    read_frags(st, 0, 0);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      if (s + 1 < KS) read_frags(st, s + 1, (s + 1) & 1);
+      // The next stage's loads go out among the first slice's MFMAs, after
+      // its fragment reads (the compiler keeps LDS reads and these LDS-writing
+      // loads in program order). Past the last stage they reload it into a
+      // retired buffer (same addresses, never read), which keeps the step
+      // one straight-line block.
+      if (s == 0) issue(min(kt + NS - 1, nk - 1), kt + NS - 1);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x32(fa[s & 1][i], fb[s & 1][j], acc[i][j]);
+    }
+    // Instruction order for the step (left to the compiler, the fragment
+    // reads sink next to their MFMAs and every read's latency is exposed):
+    // the first slice's reads, then for each slice its MFMAs with one of the
+    // next slice's reads after each of the first MFMAs; in the first slice
+    // the next stage's global loads follow, spread over its last MFMAs.
+    constexpr int NR = FM + FN, NM = FM * FN;
+    static_assert(NM >= NR, "more fragment reads than MFMAs in a slice");
+    constexpr int FREE = NM - NR;  // MFMA slots of the first slice without a read
+    constexpr int VPS = FREE > 0 ? (PER_STAGE + FREE - 1) / FREE : 0;  // loads per slot
+    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int nr = (s + 1 < KS) ? NR : 0;
+#pragma unroll
+      for (int q = 0; q < NM; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (q < nr) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (s == 0 && q >= NR) {
+#pragma unroll
+          for (int v = 0; v < VPS; ++v)
+            if ((q - NR) * VPS + v < PER_STAGE) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+        }
+      }
+      if (s == 0 && FREE == 0) {
+#pragma unroll
+        for (int v = 0; v < PER_STAGE; ++v) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+      }
+    }
+  }
+  __syncthreads();
+  epilogue_tile<BM, BN, GROUPED>(a, t, sw, bias, smem, acc);
+}
+
+// ------------------------------------------------------------- general kernel
+template <int BM, int BN, bool GROUPED>
+__global__ __launch_bounds__(256) void gemm_i8_kernel(GemmArgs a, int tiles_m, int tiles_n) {
+  constexpr int NT = 256, BK = 64;
+  constexpr int STRIDE = BK + 16;
+  constexpr int STAGE = (BM + BN) * STRIDE;
+  constexpr int TM = BM / 2, TN = BN / 2;
+  constexpr int FM = TM / 32, FN = TN / 32;
+  constexpr int KC = BK / 16;
+  constexpr int A_PER_T = BM * KC / NT, B_PER_T = BN * KC / NT;
+  static_assert(BM * KC % NT == 0 && BN * KC % NT == 0, "tile / thread mismatch");
+  static_assert(epilogue_lds_bytes<BM, BN>() <= 2 * STAGE, "epilogue does not fit the LDS");
+
+  __shared__ __attribute__((aligned(16))) int8_t smem[2 * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  const TileLoc t = locate_tile<BM, BN, GROUPED>(a, tiles_m, tiles_n);
+  if (t.expert < 0) return;
+  const int8_t* B = a.B + t.expert * a.N * a.ldb;
+  const float* sw = a.s_w + (GROUPED ? t.expert * a.N : 0);
+  const uint16_t* bias = (GROUPED && a.bias) ? a.bias + t.expert * a.N : a.bias;
 
   // ---- per-thread global source pointers (fixed over K)
   const int8_t* a_src[A_PER_T];
@@ -97,16 +426,10 @@ __global__ __launch_bounds__(256) void gemm_i8_kernel(GemmArgs a, int tiles_m, i
 #pragma unroll
   for (int i = 0; i < A_PER_T; ++i) {
     const int c = tid + i * NT, r = c / KC, kc = c % KC;
-    const int64_t gr = row_begin + r;
-    bool ok = gr < row_end;
-    int64_t src = ok ? gr : 0;
-    if (GROUPED && a.row_ids) {
-      src = ok ? (int64_t)a.row_ids[gr] : 0;
-      ok = ok && src >= 0 && src < a.M_src;
-      if (!ok) src = 0;
-    }
-    a_src[i] = a.A + src * a.lda + kc * 16;
-    a_ok[i] = ok;
+    const int64_t gr = t.row_begin + r;
+    const int64_t src = gr < t.row_end ? source_row<GROUPED>(a, gr) : -1;
+    a_ok[i] = src >= 0;
+    a_src[i] = a.A + (a_ok[i] ? src : 0) * a.lda + kc * 16;
     a_kc[i] = kc * 16;
     a_lds[i] = r * STRIDE + kc * 16;
   }
@@ -116,37 +439,50 @@ __global__ __launch_bounds__(256) void gemm_i8_kernel(GemmArgs a, int tiles_m, i
 #pragma unroll
   for (int i = 0; i < B_PER_T; ++i) {
     const int c = tid + i * NT, r = c / KC, kc = c % KC;
-    const int64_t n = n_begin + r;
+    const int64_t n = t.n_begin + r;
     b_ok[i] = n < a.N;
     b_src[i] = B + (b_ok[i] ? n : 0) * a.ldb + kc * 16;
     b_kc[i] = kc * 16;
     b_lds[i] = BM * STRIDE + r * STRIDE + kc * 16;
   }
 
-  uint4 ra[A_PER_T], rb[B_PER_T];
-  auto load_tile = [&](int64_t k0) {
+  // Loads are branch-free: an out-of-range chunk reads a valid address and is
+  // replaced by zeros (the K tail must be zero in both operands).
+  u32x4 ra[A_PER_T], rb[B_PER_T];
+  auto load_tile = [&](int64_t k0) __attribute__((always_inline)) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int i = 0; i < A_PER_T; ++i)
-      ra[i] = (a_ok[i] && k0 + a_kc[i] < a.K) ? ld16(a_src[i] + k0) : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < A_PER_T; ++i) {
+      const bool ok = a_ok[i] && k0 + a_kc[i] < a.K;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(a_src[i] + (ok ? k0 : 0));
+      ra[i] = ok ? v : z;
+    }
 #pragma unroll
-    for (int i = 0; i < B_PER_T; ++i)
-      rb[i] = (b_ok[i] && k0 + b_kc[i] < a.K) ? ld16(b_src[i] + k0) : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < B_PER_T; ++i) {
+      const bool ok = b_ok[i] && k0 + b_kc[i] < a.K;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(b_src[i] + (ok ? k0 : 0));
+      rb[i] = ok ? v : z;
+    }
   };
-  auto store_tile = [&](int buf) {
-    int8_t* base = smem + buf * (BM + BN) * STRIDE;
+  auto store_tile = [&](int buf) __attribute__((always_inline)) {
+    int8_t* base = smem + buf * STAGE;
 #pragma unroll
-    for (int i = 0; i < A_PER_T; ++i) *reinterpret_cast<uint4*>(base + a_lds[i]) = ra[i];
+    for (int i = 0; i < A_PER_T; ++i) *reinterpret_cast<u32x4*>(base + a_lds[i]) = ra[i];
 #pragma unroll
-    for (int i = 0; i < B_PER_T; ++i) *reinterpret_cast<uint4*>(base + b_lds[i]) = rb[i];
+    for (int i = 0; i < B_PER_T; ++i) *reinterpret_cast<u32x4*>(base + b_lds[i]) = rb[i];
   };
 
-  i32x4 acc[FM][FN];
+  i32x16 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
-  const int frag_row = lane & 15, frag_k = (lane >> 4) * 16;
+  const int frag_row = lane & 31, frag_k = (lane >> 5) * 16;
+  const int a_frag = (wm * TM + frag_row) * STRIDE + frag_k;
+  const int b_frag = BM * STRIDE + (wn * TN + frag_row) * STRIDE + frag_k;
   const int64_t nk = (a.K + BK - 1) / BK;
 
   load_tile(0);
@@ -155,75 +491,130 @@ __global__ __launch_bounds__(256) void gemm_i8_kernel(GemmArgs a, int tiles_m, i
   for (int64_t kt = 0; kt < nk; ++kt) {
     const bool more = kt + 1 < nk;
     if (more) load_tile((kt + 1) * BK);
-    const int8_t* base = smem + (kt & 1) * (BM + BN) * STRIDE;
+    const int8_t* base = smem + (kt & 1) * STAGE;
 #pragma unroll
-    for (int ks = 0; ks < BK; ks += 64) {
+    for (int ks = 0; ks < BK; ks += 32) {
       i32x4 af[FM], bf[FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i)
-        af[i] = as_i32x4(*reinterpret_cast<const uint4*>(
-            base + (wm * TM + i * 16 + frag_row) * STRIDE + ks + frag_k));
+        af[i] = *reinterpret_cast<const i32x4*>(base + a_frag + i * 32 * STRIDE + ks);
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        bf[j] = as_i32x4(*reinterpret_cast<const uint4*>(
-            base + BM * STRIDE + (wn * TN + j * 16 + frag_row) * STRIDE + ks + frag_k));
+        bf[j] = *reinterpret_cast<const i32x4*>(base + b_frag + j * 32 * STRIDE + ks);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma16x16x64(af[i], bf[j], acc[i][j]);
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x32(af[i], bf[j], acc[i][j]);
     }
     if (more) store_tile((kt + 1) & 1);
     __syncthreads();
   }
-
-  // ---- fused epilogue
-  EpiCol cols[FN];
-#pragma unroll
-  for (int j = 0; j < FN; ++j) cols[j] = load_col(a, n_begin + wn * TN + j * 16 + frag_row, sw, bias);
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t gr = row_begin + wm * TM + i * 16 + (lane >> 4) * 4 + r;
-      EpiRow er;
-      er.ok = gr < row_end;
-      er.out_row = gr;
-      int64_t src = er.ok ? gr : 0;
-      if (GROUPED && a.row_ids) {
-        src = er.ok ? (int64_t)a.row_ids[gr] : 0;
-        if (src < 0 || src >= a.M_src) src = 0;
-      }
-      er.sx = a.sx_per_token ? a.s_x[src] : a.s_x[0];
-      er.zp = (a.azp_mode == 1) ? a.zp[src] : 0;
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        epilogue_store(a, er, cols[j], n_begin + wn * TN + j * 16 + frag_row, acc[i][j][r]);
-    }
-  }
+  epilogue_tile<BM, BN, GROUPED>(a, t, sw, bias, smem, acc);
 }
 
 namespace {
-constexpr int kBM = 128, kBN = 128, kBK = 64;
+
+struct TileCfg {
+  int bm, bn;
+};
+
+// Tile menu: 256 x 256 (each LDS fragment feeds 4 MFMAs) when the problem has
+// enough tiles to fill the 256 compute units, 256 x 128 / 128 x 128 when the
+// big tile would leave much of the chip idle. Estimated cost = rounds of
+// workgroups over the CUs x tile area / measured relative throughput per
+// unit of tile area (1.0, 0.81, 0.72 for the three sizes on 8192 x 4096 x
+// 4096 with BK = 128).
+TileCfg pick_tile(int64_t M, int64_t N) {
+  const TileCfg menu[3] = {{256, 256}, {256, 128}, {128, 128}};
+  const double eff[3] = {1.0, 0.81, 0.72};
+  int best = 0;
+  double best_cost = 0;
+  for (int c = 0; c < 3; ++c) {
+    const int64_t tiles = ((M + menu[c].bm - 1) / menu[c].bm) * ((N + menu[c].bn - 1) / menu[c].bn);
+    const int64_t rounds = (tiles + 255) / 256;
+    const double cost = (double)rounds * menu[c].bm * menu[c].bn / eff[c];
+    if (c == 0 || cost < best_cost) {
+      best = c;
+      best_cost = cost;
+    }
+  }
+  return menu[best];
 }
 
-hipError_t launch_scaled_mm(const GemmArgs& a, hipStream_t stream) {
-  const int tiles_m = (int)((a.M + kBM - 1) / kBM), tiles_n = (int)((a.N + kBN - 1) / kBN);
-  hipLaunchKernelGGL((gemm_i8_kernel<kBM, kBN, kBK, false>), dim3(tiles_m * tiles_n), dim3(256), 0,
-                     stream, a, tiles_m, tiles_n);
+// K-step variant: 128-byte steps (full cache lines per row and load) when K
+// allows, 64-byte steps with a deeper ring otherwise, registers-staged with
+// zero fill for any other K. The 128-byte ring takes as many stages (up to
+// 4) as the 160 KiB of LDS hold.
+enum KVariant { kK128 = 0, kK64 = 1, kKAny = 2 };
+KVariant pick_k(int64_t K) { return K % 128 == 0 ? kK128 : (K % 64 == 0 ? kK64 : kKAny); }
+
+template <int BM, int BN>
+constexpr int stages128() {
+  constexpr int kLds = 160 * 1024;
+  return (BM + BN) * 128 * 4 <= kLds ? 4 : ((BM + BN) * 128 * 3 <= kLds ? 3 : 2);
+}
+static_assert(stages128<256, 256>() == 2 && stages128<256, 128>() == 3 &&
+                  stages128<128, 128>() == 4,
+              "stage counts the kernel names below state");
+
+template <int BM, int BN, bool GROUPED>
+hipError_t launch_tiles(const GemmArgs& a, int64_t extra_m_tiles, hipStream_t stream) {
+  const int64_t tiles_m = (a.M + BM - 1) / BM + extra_m_tiles;
+  const int tiles_n = (int)((a.N + BN - 1) / BN);
+  const dim3 grid((unsigned)(tiles_m * tiles_n)), block(256);
+  switch (pick_k(a.K)) {
+    case kK128:
+      hipLaunchKernelGGL((gemm_i8_dma_kernel<BM, BN, 128, stages128<BM, BN>(), GROUPED>), grid, block,
+                         0, stream, a, (int)tiles_m, tiles_n);
+      break;
+    case kK64:
+      hipLaunchKernelGGL((gemm_i8_dma_kernel<BM, BN, 64, 4, GROUPED>), grid, block, 0, stream, a,
+                         (int)tiles_m, tiles_n);
+      break;
+    default:
+      hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, GROUPED>), grid, block, 0, stream, a, (int)tiles_m,
+                         tiles_n);
+  }
   return hipGetLastError();
+}
+
+const char* kernel_name(int bm, int bn, bool grouped, int64_t K) {
+  static const char* names[3][2][3] = {
+      {{"gemm_i8_dma_kernel<256, 256, 128, 2, false>", "gemm_i8_dma_kernel<256, 128, 128, 3, false>",
+        "gemm_i8_dma_kernel<128, 128, 128, 4, false>"},
+       {"gemm_i8_dma_kernel<256, 256, 128, 2, true>", "gemm_i8_dma_kernel<256, 128, 128, 3, true>",
+        "gemm_i8_dma_kernel<128, 128, 128, 4, true>"}},
+      {{"gemm_i8_dma_kernel<256, 256, 64, 4, false>", "gemm_i8_dma_kernel<256, 128, 64, 4, false>",
+        "gemm_i8_dma_kernel<128, 128, 64, 4, false>"},
+       {"gemm_i8_dma_kernel<256, 256, 64, 4, true>", "gemm_i8_dma_kernel<256, 128, 64, 4, true>",
+        "gemm_i8_dma_kernel<128, 128, 64, 4, true>"}},
+      {{"gemm_i8_kernel<256, 256, false>", "gemm_i8_kernel<256, 128, false>",
+        "gemm_i8_kernel<128, 128, false>"},
+       {"gemm_i8_kernel<256, 256, true>", "gemm_i8_kernel<256, 128, true>",
+        "gemm_i8_kernel<128, 128, true>"}}};
+  const int c = (bm == 256 && bn == 256) ? 0 : (bm == 256 ? 1 : 2);
+  return names[pick_k(K)][grouped][c];
+}
+
+}  // namespace
+
+hipError_t launch_scaled_mm(const GemmArgs& a, hipStream_t stream) {
+  const TileCfg t = pick_tile(a.M, a.N);
+  if (t.bm == 256 && t.bn == 256) return launch_tiles<256, 256, false>(a, 0, stream);
+  if (t.bm == 256) return launch_tiles<256, 128, false>(a, 0, stream);
+  return launch_tiles<128, 128, false>(a, 0, stream);
 }
 
 const char* scaled_mm_kernel_name(int64_t M, int64_t N, int64_t K) {
-  (void)M, (void)N, (void)K;
-  return "gemm_i8_kernel<128, 128, 64, false>";
+  const TileCfg t = pick_tile(M, N);
+  return kernel_name(t.bm, t.bn, false, K);
 }
 
 hipError_t launch_grouped_mm(const GemmArgs& a, hipStream_t stream) {
-  const int64_t tiles_m = (a.M + kBM - 1) / kBM + a.E;  // bound on the sum over experts
-  const int tiles_n = (int)((a.N + kBN - 1) / kBN);
-  hipLaunchKernelGGL((gemm_i8_kernel<kBM, kBN, kBK, true>), dim3((unsigned)(tiles_m * tiles_n)),
-                     dim3(256), 0, stream, a, (int)tiles_m, tiles_n);
-  return hipGetLastError();
+  // one partial m-tile per expert on top of the full tiles
+  return launch_tiles<256, 256, true>(a, a.E, stream);
 }
+
+const char* grouped_mm_kernel_name(int64_t K) { return kernel_name(256, 256, true, K); }
 
 }  // namespace w8a8

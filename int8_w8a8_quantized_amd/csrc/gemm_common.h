@@ -18,6 +18,17 @@ __device__ __forceinline__ i32x4 mfma16x16x64(i32x4 a, i32x4 b, i32x4 c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
+// v_mfma_i32_32x32x32_i8: D[32x32] += A[32x32] * B[32x32], exact int32, at
+// twice the int8 rate of the 16x16x64 form on gfx950. Operand lane layout:
+// lane l supplies row (A) / column (B) l % 32 and 16 consecutive k values of
+// k-group l / 32 (the same pairing argument as above applies). Result
+// layout: lane l holds column l % 32; its register r holds row
+// 8 * (r / 4) + 4 * (l / 32) + r % 4.
+typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ i32x16 mfma32x32x32(i32x4 a, i32x4 b, i32x16 c) {
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ i32x4 as_i32x4(uint4 v) {
   i32x4 r;
   r.x = (int)v.x;

@@ -63,5 +63,6 @@ const char* decode_kernel_name(int64_t M);
 const char* scaled_mm_kernel_name(int64_t M, int64_t N, int64_t K);
 constexpr int64_t kDecodeMaxM = 64;
 hipError_t launch_grouped_mm(const GemmArgs& a, hipStream_t stream);
+const char* grouped_mm_kernel_name(int64_t K);
 
 }  // namespace w8a8

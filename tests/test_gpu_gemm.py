@@ -144,3 +144,27 @@ def test_decode_without_workspace():
                            out_dtype=W.OUT_I32, workspace=False)
     torch.cuda.synchronize()
     assert_equal(host(got), O.int_gemm(d["xq"], d["w"]).astype(np.int32), "unsplit int32")
+
+
+# Every (tile, K step) variant of the MFMA path, with ragged M, N and a K that
+# selects the 128-byte, the 64-byte or the zero-filled register-staged K loop.
+# The shapes are chosen so that the tile-size heuristic lands on each tile.
+PATH_CASES = [
+    (2300, 640, 4600, "gemm_i8_dma_kernel<256, 256, 128, 2, false>"),
+    (2300, 576, 4600, "gemm_i8_dma_kernel<256, 256, 64, 4, false>"),
+    (2300, 592, 4600, "gemm_i8_kernel<256, 256, false>"),
+    (2100, 384, 2100, "gemm_i8_dma_kernel<256, 128, 128, 3, false>"),
+    (2100, 320, 2100, "gemm_i8_dma_kernel<256, 128, 64, 4, false>"),
+    (2100, 336, 2100, "gemm_i8_kernel<256, 128, false>"),
+    (300, 1152, 520, "gemm_i8_dma_kernel<128, 128, 128, 4, false>"),
+    (130, 192, 260, "gemm_i8_dma_kernel<128, 128, 64, 4, false>"),
+    (130, 208, 260, "gemm_i8_kernel<128, 128, false>"),
+]
+
+
+@pytest.mark.parametrize("M,K,N,kernel", PATH_CASES)
+def test_every_tile_path(M, K, N, kernel):
+    assert W.scaled_mm_kernel_name(M, N, K) == kernel
+    d = _inputs(M, K, N, seed=7)
+    _run(d, W.AZP_PER_TOKEN, out_dtype=W.OUT_I32)
+    _run(d, W.AZP_NONE, bias=True)

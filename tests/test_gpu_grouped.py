@@ -57,6 +57,8 @@ def _run(d, bias, out_dtype):
     ([300], 1040, 130, 41),
     ([128, 128, 127, 129], 512, 256, None),
     ([1] * 40, 96, 64, 7),
+    ([300, 513, 7, 0, 260], 640, 300, 1000),
+    ([257, 0, 511], 192, 520, None),
 ])
 def test_grouped(counts, K, N, M_src):
     d = _case(counts, K, N, M_src)
