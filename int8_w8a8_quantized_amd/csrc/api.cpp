@@ -228,9 +228,8 @@ w8a8_status w8a8_prepare_fp8_block_to_int8(const uint8_t* W8, const float* S, in
 }
 
 size_t w8a8_scaled_mm_workspace_size(int64_t M, int64_t N, int64_t K) {
-  (void)K;
-  if (M <= 0 || N <= 0 || M > w8a8::kDecodeMaxM || N >= kMaxDim) return 0;
-  return w8a8::decode_workspace_bytes(M, N);
+  if (M <= 0 || N <= 0 || M > w8a8::kDecodeMaxM || N >= kMaxDim || K <= 0 || K > W8A8_MAX_K) return 0;
+  return w8a8::decode_workspace_bytes(M, N, K);
 }
 
 static w8a8_status check_gemm_common(const int8_t* xq, int64_t ldx, const int8_t* Wq, int64_t K,
@@ -335,7 +334,7 @@ w8a8_status w8a8_grouped_scaled_mm_int8(const int8_t* xq, int64_t ldx, int64_t M
 
 const char* w8a8_scaled_mm_kernel_name(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K <= 0) return "";
-  return (M <= w8a8::kDecodeMaxM) ? w8a8::decode_kernel_name(M) : w8a8::scaled_mm_kernel_name(M, N, K);
+  return (M <= w8a8::kDecodeMaxM) ? w8a8::decode_kernel_name(M, N, K) : w8a8::scaled_mm_kernel_name(M, N, K);
 }
 
 const char* w8a8_status_string(w8a8_status s) {

@@ -98,10 +98,14 @@ def test_gemm_rejects_before_device_work(L):
     assert mm(sw=None) == W.ERR_INVALID_ARG
     assert mm(M=1 << 26) == W.ERR_INVALID_ARG
     assert mm(M=0) == W.OK and mm(N=0) == W.OK
-    # decode (M <= 64): int32 sums [M, N] + one counter per 64 weight rows, 256-byte rounded
-    assert W.scaled_mm_workspace_size(64, 4096, 4096) == (64 * 4096 + 64) * 4
-    assert W.scaled_mm_workspace_size(1, 100, 4096) == 512
-    assert W.scaled_mm_workspace_size(65, 4096, 4096) == 0
+    # decode (M <= 64) split over K: 4096 arrival counters, then int32 partial
+    # sums [splits, M, N] (splits from the decode launch table)
+    assert W.scaled_mm_workspace_size(64, 4096, 4096) == 0                    # one K range
+    assert W.scaled_mm_workspace_size(1, 100, 4096) == 4096 * 4 + 2 * 1 * 100 * 4
+    assert W.scaled_mm_workspace_size(1, 28672, 4096) == 4096 * 4 + 2 * 28672 * 4
+    assert W.scaled_mm_workspace_size(8, 4096, 14336) == 4096 * 4 + 4 * 8 * 4096 * 4
+    assert W.scaled_mm_workspace_size(8, 4096, 272) == 0      # K % 128 != 0: no split
+    assert W.scaled_mm_workspace_size(65, 4096, 4096) == 0    # not the decode path
 
 
 def test_grouped_rejects_before_device_work(L):

@@ -122,20 +122,41 @@ def test_empty():
     assert out.shape == (0, 8)
 
 
-def test_decode_split_workspace_is_left_zero():
-    """The split-K decode path adds partial sums into a caller workspace and
-    must leave it all-zero after every call, whatever the shape sequence."""
-    ws = torch.zeros(W.scaled_mm_workspace_size(64, 4096, 14336) // 4, dtype=torch.int32,
-                     device="cuda:0")
-    for i, (M, K, N) in enumerate([(1, 14336, 4096), (64, 4096, 200), (17, 14336, 96),
-                                   (64, 14336, 4096), (3, 272, 64), (48, 8192, 1000)]):
-        d = _inputs(M, K, N, seed=10 + i)
-        note(f"split workspace M={M} K={K} N={N}")
-        got = W.scaled_mm_int8(to_dev(d["xq"]), to_dev(d["w"]), to_dev(d["sx"]), to_dev(d["sw"]),
-                               out_dtype=W.OUT_I32, workspace=ws)
-        torch.cuda.synchronize()
-        assert_equal(host(got), O.int_gemm(d["xq"], d["w"]).astype(np.int32), "split-K int32")
-        assert int(torch.count_nonzero(ws)) == 0
+DECODE_SEQ = [(1, 14336, 4096), (64, 4096, 200), (17, 14336, 96), (64, 14336, 4096), (3, 272, 64),
+              (48, 8192, 1000), (32, 4096, 300), (20, 256, 16400), (5, 512, 16390), (1, 256, 100)]
+
+
+def test_decode_shape_sequence_shared_workspace():
+    """The decode paths over a sequence of shapes that share one workspace
+    (K split or not, ragged N, M not a multiple of 16, K not a multiple of
+    128): int32 exact every time, twice over, and the arrival counters at the
+    head of the workspace are back to zero after every call."""
+    need = max(W.scaled_mm_workspace_size(M, N, K) for (M, K, N) in DECODE_SEQ)
+    assert need > 0
+    ws = torch.zeros(need // 4, dtype=torch.int32, device="cuda:0")
+    for rep in range(2):
+        for i, (M, K, N) in enumerate(DECODE_SEQ):
+            d = _inputs(M, K, N, seed=10 + i)
+            note(f"decode sequence rep={rep} M={M} K={K} N={N} kernel={W.scaled_mm_kernel_name(M, N, K)}")
+            got = W.scaled_mm_int8(to_dev(d["xq"]), to_dev(d["w"]), to_dev(d["sx"]), to_dev(d["sw"]),
+                                   out_dtype=W.OUT_I32, workspace=ws)
+            torch.cuda.synchronize()
+            assert_equal(host(got), O.int_gemm(d["xq"], d["w"]).astype(np.int32), "decode int32")
+            assert int(torch.count_nonzero(ws[:4096])) == 0
+
+
+def test_decode_workspace_too_small_is_unused():
+    """A workspace smaller than the size query asks for is not touched (the
+    call keeps the whole K in one workgroup)."""
+    M, K, N = 1, 14336, 4096
+    assert W.scaled_mm_workspace_size(M, N, K) > 4096
+    ws = torch.full((1024,), 7, dtype=torch.int32, device="cuda:0")
+    d = _inputs(M, K, N, seed=30)
+    got = W.scaled_mm_int8(to_dev(d["xq"]), to_dev(d["w"]), to_dev(d["sx"]), to_dev(d["sw"]),
+                           out_dtype=W.OUT_I32, workspace=ws)
+    torch.cuda.synchronize()
+    assert_equal(host(got), O.int_gemm(d["xq"], d["w"]).astype(np.int32), "decode int32")
+    assert bool((ws == 7).all())
 
 
 def test_decode_without_workspace():
