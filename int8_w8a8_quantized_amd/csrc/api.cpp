@@ -37,11 +37,9 @@ w8a8_status hip_status(hipError_t e, const char* what) {
   return fail(W8A8_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// Per-device arch check: 0 = not yet checked, 1 = gfx950, 2 = other; and the
-// device's compute-unit count (used to size split-K launches).
+// Per-device arch check: 0 = not yet checked, 1 = gfx950, 2 = other.
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_arch[kMaxDevices];
-std::atomic<int> g_cus[kMaxDevices];
 
 w8a8_status check_device(int dev) {
   if (dev < 0 || dev >= kMaxDevices) return fail(W8A8_ERR_UNSUPPORTED_DEVICE, "device %d out of range", dev);
@@ -51,8 +49,6 @@ w8a8_status check_device(int dev) {
     hipError_t e = hipGetDeviceProperties(&prop, dev);
     if (e != hipSuccess) return hip_status(e, "hipGetDeviceProperties");
     st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
-    g_cus[dev].store(prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256,
-                     std::memory_order_relaxed);
     g_arch[dev].store(st, std::memory_order_release);
     if (st == 2)
       return fail(W8A8_ERR_UNSUPPORTED_DEVICE, "device %d is %s; this library is built for gfx950 (MI355X)",
@@ -62,13 +58,11 @@ w8a8_status check_device(int dev) {
   return W8A8_OK;
 }
 
-w8a8_status check_current_device(int* cus = nullptr) {
+w8a8_status check_current_device() {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_status(e, "hipGetDevice");
-  w8a8_status st = check_device(dev);
-  if (st == W8A8_OK && cus) *cus = g_cus[dev].load(std::memory_order_relaxed);
-  return st;
+  return check_device(dev);
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -227,11 +221,6 @@ w8a8_status w8a8_prepare_fp8_block_to_int8(const uint8_t* W8, const float* S, in
                     "fp8_block_to_int8 launch");
 }
 
-size_t w8a8_scaled_mm_workspace_size(int64_t M, int64_t N, int64_t K) {
-  if (M <= 0 || N <= 0 || M > w8a8::kDecodeMaxM || N >= kMaxDim || K <= 0 || K > W8A8_MAX_K) return 0;
-  return w8a8::decode_workspace_bytes(M, N, K);
-}
-
 static w8a8_status check_gemm_common(const int8_t* xq, int64_t ldx, const int8_t* Wq, int64_t K,
                                      const void* out, int32_t out_dtype, int64_t ldo, int64_t N) {
   W8A8_REQUIRE(xq && Wq && out, "xq, Wq and out must not be NULL");
@@ -246,8 +235,7 @@ w8a8_status w8a8_scaled_mm_int8(const int8_t* xq, int64_t M, int64_t K, int64_t 
                                 int64_t N, int64_t ldw, const float* s_x, int32_t s_x_per_token,
                                 const float* s_w, int32_t s_w_per_channel, const int32_t* zp,
                                 const int32_t* colsum, int32_t azp_mode, const uint16_t* bias, void* out,
-                                int32_t out_dtype, int64_t ldo, void* workspace, size_t workspace_bytes,
-                                void* stream) {
+                                int32_t out_dtype, int64_t ldo, void* stream) {
   w8a8_status st;
   if ((st = check_dim(M, "M")) != W8A8_OK) return st;
   if ((st = check_dim(N, "N")) != W8A8_OK) return st;
@@ -260,9 +248,7 @@ w8a8_status w8a8_scaled_mm_int8(const int8_t* xq, int64_t M, int64_t K, int64_t 
   if (azp_mode == W8A8_AZP_PER_TOKEN) W8A8_REQUIRE(zp && colsum, "AZP_PER_TOKEN needs zp and colsum");
   if (azp_mode == W8A8_AZP_STATIC) W8A8_REQUIRE(colsum, "AZP_STATIC needs azp_adj (passed as colsum)");
   if ((st = check_tiles(M, 0, N)) != W8A8_OK) return st;
-  W8A8_REQUIRE(workspace == nullptr || aligned16(workspace), "workspace must be 16-byte aligned");
-  int cus = 256;
-  if ((st = check_current_device(&cus)) != W8A8_OK) return st;
+  if ((st = check_current_device()) != W8A8_OK) return st;
   w8a8::GemmArgs a{};
   a.A = xq;
   a.lda = ldx;
@@ -284,7 +270,7 @@ w8a8_status w8a8_scaled_mm_int8(const int8_t* xq, int64_t M, int64_t K, int64_t 
   a.ldo = ldo;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = (M <= w8a8::kDecodeMaxM)
-                           ? w8a8::launch_decode_mm(a, workspace, workspace_bytes, cus, s)
+                           ? w8a8::launch_decode_mm(a, s)
                            : w8a8::launch_scaled_mm(a, s);
   return hip_status(e, "scaled_mm launch");
 }

@@ -2,26 +2,33 @@
 //
 // Same product and fused epilogue as the prefill GEMM ("[SGLang] W4A8, W8A8,
 // W4A4: 혼합 정밀도 양자화 스킴", 핵심 코드 분석 §3-§4), but with a handful of
-// token rows the time is reading the N x K int8 weight from HBM once, so the
-// kernels are built around the HBM access pattern and the bytes in flight.
+// token rows the time is reading the N x K int8 weight from HBM once. Two
+// facts measured on MI355X shape the kernels:
+//  - HBM streams at full rate when each wave instruction reads whole 128-byte
+//    lines (8 rows x 128 bytes); the MFMA operand order (16 rows x 64 bytes)
+//    reaches only about 60-70% of it;
+//  - the loaded latency is several microseconds, so a CU needs on the order
+//    of 100+ KiB of weight loads in flight. LDS (160 KiB, shared with the
+//    activation stages) cannot hold that much; the register file can.
 //
-// Main kernel (K a multiple of 128), gemv_dma_kernel: a workgroup of 4
-// waves owns 64 weight rows and a contiguous range of K (one of `splits`
-// ranges). Weights and the (M padded to 16-row MFMA blocks) activations
-// travel HBM/L2 -> LDS with the direct-to-LDS load, one wave instruction
-// moving 8 rows x 128 bytes -- whole cache lines per row, the pattern that
-// streams HBM at full rate (MFMA operand order, 16 rows x 64 bytes per
-// instruction, reaches only about 60-70% of it) -- into a ring of NS stages
-// of 128 bytes of K, so NS - 1 stages are in flight per workgroup. Chunks are
-// XOR-swizzled within a row as in the prefill GEMM, so each wave's fragment
-// reads (16 rows x one 16-byte chunk) hit distinct banks. Wave w multiplies
-// weight rows 16w..16w+15 with all activation blocks with
-// v_mfma_i32_16x16x64_i8. With one range the workgroup applies the epilogue
-// from registers; with several, each workgroup stores its int32 partial tile
-// to a caller workspace and the last one to arrive for the row block (an
-// arrival counter) adds the partials, applies the epilogue and resets the
-// counter (partials and counter through agent-scope
-// atomics, no cache-wide fences). Integer sums are exact in any order.
+// Main kernel, gemv_reg_kernel (K a multiple of 128): a workgroup of W waves
+// owns 16 * RG weight rows; the waves split K into interleaved 128-byte steps.
+// Each wave keeps a ring of U steps of loads in flight in registers: the
+// weight rows as whole lines (2 * RG instructions per step), and the
+// activation fragments already in MFMA operand order (rows past M repeat row
+// M - 1, so they cost cache hits, not HBM). A step's weight lines go through a
+// 2 KiB-per-row-group LDS buffer of the wave to reach operand order (one
+// 16-byte write and one 16-byte read per lane per 8 rows; XOR-swizzled chunks
+// keep both conflict-free), then v_mfma_i32_16x16x64_i8 accumulates. At the
+// end the waves' partial tiles are added in LDS and the epilogue, whose
+// per-row / per-column operands were loaded before the K loop, writes out.
+//
+// Direct-to-LDS kernel, gemv_dma_kernel (K a multiple of 128; used for M > 16
+// with many weight rows, where one workgroup's activation stage serves 64
+// weight rows): a workgroup of 4 waves owns 64 weight rows; weights and
+// activations travel HBM/L2 -> LDS with the direct-to-LDS load (8 rows x 128
+// bytes per instruction) into a ring of NS stages; wave w multiplies weight
+// rows 16w..16w+15 with all activation blocks.
 //
 // General kernel (any K that is a multiple of 16), gemv_i8_kernel: operands
 // go straight from memory into MFMA registers, as described above it.
@@ -41,16 +48,152 @@ __device__ __forceinline__ void gemv_wait_vmcnt() {
   __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 __device__ __forceinline__ void gemv_barrier() { __asm__ volatile("s_barrier" ::: "memory"); }
+__device__ __forceinline__ int64_t gemv_min(int64_t a, int64_t b) { return a < b ? a : b; }
 
 // Chunk position of logical 16-byte chunk c of an 8-chunk (128-byte) row r:
 // distinct banks for 16-byte reads of 8 (32-bank view) or 16 (64-bank view)
 // consecutive rows at one chunk.
 __device__ __forceinline__ int gemv_swz(int r) { return (r ^ ((r >> 3) & 3)) & 7; }
 
+// Epilogue operands of the tile elements a thread stores, loaded before the K
+// loop. Element e of a wave's accumulator tile (RG row groups x MF token
+// blocks of 16 x 16): gf = e / 256 -> row group gf / MF, token block gf % MF;
+// register r = (e / 64) % 4; lane l = e % 64 -> weight row 16 * (gf / MF) +
+// l % 16, token 16 * (gf % MF) + 4 * (l / 16) + r (the MFMA result layout).
+template <int MF, int EP>
+struct GemvEpi {
+  EpiRow er[EP];
+  EpiCol ec[EP];
+  int64_t n[EP];
+  __device__ __forceinline__ void load(const GemmArgs& a, int64_t n0, int first, int stride, int per) {
+#pragma unroll
+    for (int j = 0; j < EP; ++j) {
+      const int e = first + stride * j;
+      const int gf = e >> 8, r = (e >> 6) & 3, l = e & 63;
+      const int64_t nn = n0 + 16 * (gf / MF) + (l & 15);
+      const int64_t m = 16 * (gf % MF) + 4 * (l >> 4) + r;
+      er[j].ok = e < per && m < a.M;
+      const int64_t mm = er[j].ok ? m : 0;
+      er[j].out_row = mm;
+      er[j].sx = a.sx_per_token ? a.s_x[mm] : a.s_x[0];
+      er[j].zp = (a.azp_mode == 1) ? a.zp[mm] : 0;
+      ec[j] = load_col(a, nn, a.s_w, a.bias);  // a row past N is marked not ok
+      n[j] = nn;
+    }
+  }
+};
+
+// ---------------------------------------------------------------- main kernel
+template <int MF, int RG, int W, int U>
+__global__ __launch_bounds__(W * 64) void gemv_reg_kernel(GemmArgs a) {
+  constexpr int BN = 16 * RG, BK = 128;
+  constexpr int PER = RG * MF * 256;  // accumulator ints of one wave
+  constexpr int TB = BN * BK;         // the wave's transpose buffer
+  constexpr int SM = (W * TB > W * PER * 4) ? W * TB : W * PER * 4;
+  constexpr int EP = (PER + W * 64 - 1) / (W * 64);
+  __shared__ __attribute__((aligned(1024))) int8_t smem[SM];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t n0 = (int64_t)blockIdx.x * BN;
+  const int nsteps = (int)(a.K / BK);
+  const int nkw = nsteps > wave ? (nsteps - wave + W - 1) / W : 0;  // this wave's steps
+  int8_t* tb = smem + wave * TB;
+
+  // weight lines: instruction h reads rows 8h .. 8h+7 (lane l: row 8h + l/8,
+  // bytes 16 (l%8) .. +15 of the step); rows past N repeat row N-1
+  const int8_t* wsrc[2 * RG];
+#pragma unroll
+  for (int h = 0; h < 2 * RG; ++h)
+    wsrc[h] = a.B + gemv_min(n0 + 8 * h + (lane >> 3), a.N - 1) * a.ldb + (lane & 7) * 16;
+  // activation fragments of token block f: lane l reads token 16f + l%16
+  // (rows past M repeat row M-1), k-group l/16 of each 64-byte half step
+  const int8_t* asrc[MF];
+#pragma unroll
+  for (int f = 0; f < MF; ++f)
+    asrc[f] = a.A + gemv_min(16 * f + (lane & 15), a.M - 1) * a.lda + 16 * (lane >> 4);
+
+  GemvEpi<MF, EP> epi;
+  epi.load(a, n0, tid, W * 64, PER);
+
+  u32x4 wr[U][2 * RG], ar[U][MF][2];
+  // Loads of the wave's step j into ring slot u; a step past the end reloads
+  // the last one (a cache hit), so every slot issues the same loads and the
+  // compiler's in-order wait counts stay exact.
+  auto issue = [&](int u, int j) __attribute__((always_inline)) {
+    const int64_t k0 = (int64_t)(wave + W * min(j, nkw - 1)) * BK;
+#pragma unroll
+    for (int h = 0; h < 2 * RG; ++h)
+      wr[u][h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wsrc[h] + k0));
+#pragma unroll
+    for (int f = 0; f < MF; ++f)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        ar[u][f][kb] = *reinterpret_cast<const u32x4*>(asrc[f] + k0 + 64 * kb);
+  };
+  i32x4 acc[MF][RG];
+#pragma unroll
+  for (int f = 0; f < MF; ++f)
+#pragma unroll
+    for (int g = 0; g < RG; ++g) acc[f][g] = i32x4{0, 0, 0, 0};
+
+  if (nkw > 0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) issue(u, u);
+  }
+  for (int i0 = 0; i0 < nkw; i0 += U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (i0 + u < nkw) {
+        // weight lines -> operand order through the wave's LDS buffer (the
+        // wave's LDS accesses execute in order, so no wait is needed between
+        // this step's writes and reads, nor against the previous step's reads)
+#pragma unroll
+        for (int h = 0; h < 2 * RG; ++h) {
+          const int row = 8 * h + (lane >> 3);
+          *reinterpret_cast<u32x4*>(tb + row * BK + (((lane & 7) ^ gemv_swz(row)) * 16)) = wr[u][h];
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int c = 4 * kb + (lane >> 4);
+#pragma unroll
+          for (int g = 0; g < RG; ++g) {
+            const int row = 16 * g + (lane & 15);
+            const i32x4 wf = *reinterpret_cast<const i32x4*>(tb + row * BK + ((c ^ gemv_swz(row)) * 16));
+#pragma unroll
+            for (int f = 0; f < MF; ++f)
+              acc[f][g] = mfma16x16x64(__builtin_bit_cast(i32x4, ar[u][f][kb]), wf, acc[f][g]);
+          }
+        }
+      }
+      issue(u, i0 + u + U);
+    }
+  }
+
+  // add the waves' partial tiles
+  __syncthreads();
+  int32_t* red = reinterpret_cast<int32_t*>(smem);
+#pragma unroll
+  for (int g = 0; g < RG; ++g)
+#pragma unroll
+    for (int f = 0; f < MF; ++f)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[wave * PER + (g * MF + f) * 256 + r * 64 + lane] = acc[f][g][r];
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < EP; ++j) {
+    const int e = tid + W * 64 * j;
+    if (e >= PER) continue;
+    int v = 0;
+#pragma unroll
+    for (int w = 0; w < W; ++w) v += red[w * PER + e];
+    epilogue_store(a, epi.er[j], epi.ec[j], epi.n[j], v);
+  }
+}
+
+// ------------------------------------------------------ direct-to-LDS kernel
 template <int MF, int NS>
-__global__ __launch_bounds__(256) void gemv_dma_kernel(GemmArgs a, int splits, int steps_per_split,
-                                                       int32_t* __restrict__ part,
-                                                       int32_t* __restrict__ counters) {
+__global__ __launch_bounds__(256) void gemv_dma_kernel(GemmArgs a) {
   constexpr int BN = 64, BK = 128;
   constexpr int XR = MF * 16;                    // activation rows held in LDS
   constexpr int STAGE = (BN + XR) * BK;
@@ -60,12 +203,8 @@ __global__ __launch_bounds__(256) void gemv_dma_kernel(GemmArgs a, int splits, i
   __shared__ __attribute__((aligned(1024))) int8_t smem[NS * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int rb = blockIdx.x / splits, sp = blockIdx.x % splits;
-  const int64_t n0 = (int64_t)rb * BN;
-  const int nsteps = (int)(a.K / BK);
-  const int s_begin = sp * steps_per_split;
-  const int s_end = min(nsteps, s_begin + steps_per_split);
-  const int nk = max(s_end - s_begin, 0);
+  const int64_t n0 = (int64_t)blockIdx.x * BN;
+  const int nk = (int)(a.K / BK);
 
   // ---- DMA sources: instruction j (this wave's q-th) fills tile rows
   // 8j..8j+7 (weights for j < BN/8, activations after); lane l writes row
@@ -78,25 +217,42 @@ __global__ __launch_bounds__(256) void gemv_dma_kernel(GemmArgs a, int splits, i
     const int trow = 8 * j + (lane >> 3);        // row within the stage
     const int lch = (lane & 7) ^ gemv_swz(trow);
     if (trow < BN) {
-      src[q] = a.B + min(n0 + trow, a.N - 1) * a.ldb + lch * 16;
+      src[q] = a.B + gemv_min(n0 + trow, a.N - 1) * a.ldb + lch * 16;
     } else {
-      const int64_t m = min<int64_t>(trow - BN, a.M - 1);  // rows past M repeat the last one
+      const int64_t m = gemv_min(trow - BN, a.M - 1);  // rows past M repeat the last one
       src[q] = a.A + m * a.lda + lch * 16;
     }
     dst[q] = j * 1024;
   }
   auto issue = [&](int kt_src, int kt_dst) __attribute__((always_inline)) {
     int8_t* st = smem + (kt_dst % NS) * STAGE;
-    const int64_t k0 = (int64_t)(s_begin + kt_src) * BK;
+    const int64_t k0 = (int64_t)kt_src * BK;
 #pragma unroll
     for (int q = 0; q < Q; ++q)
       __builtin_amdgcn_global_load_lds((global_void_ptr_g)(src[q] + k0), (lds_void_ptr_g)(st + dst[q]),
                                        16, 0, 0);
   };
 
+  // ---- epilogue operands (lane holds tokens 16f + 4*(lane/16) + r of
+  // weight row n0 + 16w + lane%16)
+  const int fr = lane & 15;
+  const int64_t n = n0 + 16 * wave + fr;
+  const EpiCol col = load_col(a, n, a.s_w, a.bias);
+  EpiRow er[MF][4];
+#pragma unroll
+  for (int f = 0; f < MF; ++f)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t m = 16 * f + 4 * (lane >> 4) + r;
+      er[f][r].ok = m < a.M;
+      const int64_t mm = er[f][r].ok ? m : 0;
+      er[f][r].out_row = mm;
+      er[f][r].sx = a.sx_per_token ? a.s_x[mm] : a.s_x[0];
+      er[f][r].zp = (a.azp_mode == 1) ? a.zp[mm] : 0;
+    }
+
   // ---- fragments: wave w reads weight rows 16w + lane%16, activation rows
   // 16f + lane%16, logical chunk 4*ks + lane/16
-  const int fr = lane & 15;
   const int w_off = (16 * wave + fr) * BK;
   const int w_sw = gemv_swz(16 * wave + fr);
   i32x4 acc[MF];
@@ -126,74 +282,10 @@ __global__ __launch_bounds__(256) void gemv_dma_kernel(GemmArgs a, int splits, i
   }
   gemv_wait_vmcnt<0>();  // the trailing reloads land before the workgroup ends
 
-  // ---- results: lane holds rows 16f + 4*(lane/16) + r of column n0 + 16w + lane%16
-  const int64_t n = n0 + 16 * wave + fr;
-  if (splits == 1) {
-    const EpiCol col = load_col(a, n, a.s_w, a.bias);
 #pragma unroll
-    for (int f = 0; f < MF; ++f)
+  for (int f = 0; f < MF; ++f)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t m = 16 * f + 4 * (lane >> 4) + r;
-        if (m >= a.M) continue;
-        EpiRow er;
-        er.ok = true;
-        er.out_row = m;
-        er.sx = a.sx_per_token ? a.s_x[m] : a.s_x[0];
-        er.zp = (a.azp_mode == 1) ? a.zp[m] : 0;
-        epilogue_store(a, er, col, n, acc[f][r]);
-      }
-    return;
-  }
-
-  // split K: partial tiles [splits][M][N], then the last arriver sums them.
-  // Partials are written and read with agent-scope atomic stores / loads,
-  // which go to and come from the device's point of coherence (past the
-  // per-XCD L2s), so neither side needs a cache-wide fence (on this part a
-  // release fence writes back the whole L2, which costs more than the
-  // kernel): each thread's stores have completed (vmcnt drained, then the
-  // barrier) before the workgroup takes its arrival number, and the last
-  // arriver's loads are issued after it has seen the count.
-  if (n < a.N) {
-#pragma unroll
-    for (int f = 0; f < MF; ++f)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t m = 16 * f + 4 * (lane >> 4) + r;
-        if (m < a.M)
-          __hip_atomic_store(part + ((int64_t)sp * a.M + m) * a.N + n, acc[f][r], __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-      }
-  }
-  gemv_wait_vmcnt<0>();
-  __syncthreads();
-  int& last = *reinterpret_cast<int*>(smem);  // the stage ring is idle by now
-  if (tid == 0) {
-    const int prev = __hip_atomic_fetch_add(counters + rb, 1, __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT);
-    last = prev == splits - 1;
-    // the last arriver leaves the counter at zero for the next call
-    if (last) __hip_atomic_store(counters + rb, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __syncthreads();
-  if (!last) return;
-  const int rows = (int)min<int64_t>(a.M, XR);
-  for (int e = tid; e < rows * BN; e += 256) {
-    const int m = e / BN;
-    const int64_t nn = n0 + e % BN;
-    if (nn >= a.N) continue;
-    int v = 0;
-    for (int s2 = 0; s2 < splits; ++s2)
-      v += __hip_atomic_load(part + ((int64_t)s2 * a.M + m) * a.N + nn, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-    EpiRow er;
-    er.ok = true;
-    er.out_row = m;
-    er.sx = a.sx_per_token ? a.s_x[m] : a.s_x[0];
-    er.zp = (a.azp_mode == 1) ? a.zp[m] : 0;
-    const EpiCol col = load_col(a, nn, a.s_w, a.bias);
-    epilogue_store(a, er, col, nn, v);
-  }
+    for (int r = 0; r < 4; ++r) epilogue_store(a, er[f][r], col, n, acc[f][r]);
 }
 
 // ------------------------------------------------------------- general kernel
@@ -312,47 +404,46 @@ __global__ __launch_bounds__(W * 64) void gemv_i8_kernel(GemmArgs a) {
 
 namespace {
 
-constexpr int kGemvRows = 64;  // weight rows per workgroup of the main kernel
-constexpr int kCounters = 4096;  // arrival counters at the head of the workspace
-
-// Launch shape of the main kernel: LDS stages and K ranges per row block,
-// from a sweep over the Llama-3-8B decode linears (M in {1, 8, 32, 64},
-// K x N in {4096 x 6144, 4096 x 4096, 4096 x 28672, 14336 x 4096}):
-//  - many row blocks (N >= 16384): enough workgroups already; M <= 16 still
-//    gains from two K ranges;
-//  - long K (>= 8192) with few row blocks: four K ranges;
-//  - otherwise one range (two for M <= 16).
-// Larger M pays for every extra range with M x N int32 of partial sums.
+// Launch shape of the decode kernels, from sweeps over the Llama-3-8B decode
+// linears (M in {1, 8, 32, 64}, K x N in {4096 x 6144, 4096 x 4096,
+// 4096 x 28672, 14336 x 4096}) timed as graph replays with the weights
+// rotated over 1 GiB:
+//  - M <= 16: the register kernel, 16 rows per workgroup; 4 waves split K,
+//    2 once there are 1024+ row groups (the waves then live long enough);
+//  - M > 16 with 16384+ weight rows: the direct-to-LDS kernel (one
+//    activation stage serves 64 weight rows);
+//  - otherwise the register kernel, with 32 rows per workgroup when 16-row
+//    groups would need between one and two workgroups per CU (a half-empty
+//    second round costs more than the larger tile).
+enum class GemvKind { kReg, kDma, kGeneral };
 struct GemvCfg {
-  int ns, splits;
+  GemvKind kind;
+  int mf, rg, w, u;  // u: ring steps (register kernel) or LDS stages (DMA kernel)
 };
 
 int gemv_mf(int64_t M) { return (int)std::min<int64_t>((M + 15) / 16, 4); }
 
 GemvCfg gemv_cfg(int64_t M, int64_t N, int64_t K) {
   const int mf = gemv_mf(M);
-  const int64_t blocks = (N + kGemvRows - 1) / kGemvRows;
-  const int64_t nsteps = K / 128;
-  GemvCfg c;
-  if (mf == 1) c = blocks >= 256 ? GemvCfg{4, 2} : (nsteps >= 64 ? GemvCfg{4, 4} : GemvCfg{8, 2});
-  else if (mf == 2) c = blocks >= 256 ? GemvCfg{6, 1} : (nsteps >= 64 ? GemvCfg{6, 4} : GemvCfg{4, 1});
-  else c = blocks >= 256 ? GemvCfg{5, 1} : (nsteps >= 64 ? GemvCfg{5, 4} : GemvCfg{5, 1});
-  if (K % 128 != 0 || blocks > kCounters) c.splits = 1;
-  c.splits = (int)std::max<int64_t>(1, std::min<int64_t>(c.splits, nsteps));
-  return c;
+  if (K % 128 != 0) return {GemvKind::kGeneral, mf, 2, 4, 8};
+  const int64_t groups = (N + 15) / 16;
+  if (mf == 1) return {GemvKind::kReg, 1, 1, groups >= 1024 ? 2 : 4, 4};
+  if (N >= 16384) return {GemvKind::kDma, mf, 4, 4, mf == 2 ? 6 : 5};
+  if (groups > 256 && groups <= 512) return {GemvKind::kReg, mf, 2, 4, mf == 2 ? 4 : 3};
+  return {GemvKind::kReg, mf, 1, 4, 4};
 }
 
-int gemv_splits(int64_t M, int64_t N, int64_t K) { return gemv_cfg(M, N, K).splits; }
+template <int MF, int RG, int W, int U>
+hipError_t launch_reg(const GemmArgs& a, hipStream_t stream) {
+  const int64_t blocks = (a.N + 16 * RG - 1) / (16 * RG);
+  hipLaunchKernelGGL((gemv_reg_kernel<MF, RG, W, U>), dim3((unsigned)blocks), dim3(W * 64), 0, stream, a);
+  return hipGetLastError();
+}
 
 template <int MF, int NS>
-hipError_t launch_dma(const GemmArgs& a, int splits, int32_t* part, int32_t* counters,
-                      hipStream_t stream) {
-  static_assert((kGemvRows + MF * 16) * 128 * NS <= 80 * 1024, "two workgroups per CU");
-  const int64_t nsteps = a.K / 128;
-  const int sps = (int)((nsteps + splits - 1) / splits);
-  const int64_t blocks = (a.N + kGemvRows - 1) / kGemvRows;
-  hipLaunchKernelGGL((gemv_dma_kernel<MF, NS>), dim3((unsigned)(blocks * splits)), dim3(256), 0,
-                     stream, a, splits, sps, part, counters);
+hipError_t launch_dma(const GemmArgs& a, hipStream_t stream) {
+  static_assert((64 + MF * 16) * 128 * NS <= 80 * 1024, "two workgroups per CU");
+  hipLaunchKernelGGL((gemv_dma_kernel<MF, NS>), dim3((unsigned)((a.N + 63) / 64)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -365,54 +456,51 @@ hipError_t launch_general(const GemmArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-// Workspace of the split path: a fixed block of kCounters arrival counters
-// (one per 64-row block; zero on entry, left zero by the last arriver), then
-// the int32 partial sums [splits][M][N]. The counters sit at the same place
-// for every shape, so one workspace serves any sequence of calls on a stream.
-size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  const int s = gemv_splits(M, N, K);
-  if (s == 1) return 0;
-  return (size_t)kCounters * sizeof(int32_t) + (size_t)(s * M * N) * sizeof(int32_t);
-}
-
 const char* decode_kernel_name(int64_t M, int64_t N, int64_t K) {
-  static const char* gen[4] = {"gemv_i8_kernel<1, 2, 4, 8>", "gemv_i8_kernel<2, 2, 4, 8>",
-                               "gemv_i8_kernel<3, 2, 4, 8>", "gemv_i8_kernel<4, 2, 4, 8>"};
-  const int mf = gemv_mf(M);
-  if (K % 128 != 0) return gen[mf - 1];
   const GemvCfg c = gemv_cfg(M, N, K);
-  if (mf == 1) return c.ns == 4 ? "gemv_dma_kernel<1, 4>" : "gemv_dma_kernel<1, 8>";
-  if (mf == 2) return c.ns == 4 ? "gemv_dma_kernel<2, 4>" : "gemv_dma_kernel<2, 6>";
-  return mf == 3 ? "gemv_dma_kernel<3, 5>" : "gemv_dma_kernel<4, 5>";
+  switch (c.kind) {
+    case GemvKind::kGeneral: {
+      static const char* gen[4] = {"gemv_i8_kernel<1, 2, 4, 8>", "gemv_i8_kernel<2, 2, 4, 8>",
+                                   "gemv_i8_kernel<3, 2, 4, 8>", "gemv_i8_kernel<4, 2, 4, 8>"};
+      return gen[c.mf - 1];
+    }
+    case GemvKind::kDma: {
+      static const char* dma[3] = {"gemv_dma_kernel<2, 6>", "gemv_dma_kernel<3, 5>", "gemv_dma_kernel<4, 5>"};
+      return dma[c.mf - 2];
+    }
+    default: break;
+  }
+  if (c.mf == 1) return c.w == 2 ? "gemv_reg_kernel<1, 1, 2, 4>" : "gemv_reg_kernel<1, 1, 4, 4>";
+  static const char* reg1[3] = {"gemv_reg_kernel<2, 1, 4, 4>", "gemv_reg_kernel<3, 1, 4, 4>",
+                                "gemv_reg_kernel<4, 1, 4, 4>"};
+  static const char* reg2[3] = {"gemv_reg_kernel<2, 2, 4, 4>", "gemv_reg_kernel<3, 2, 4, 3>",
+                                "gemv_reg_kernel<4, 2, 4, 3>"};
+  return c.rg == 2 ? reg2[c.mf - 2] : reg1[c.mf - 2];
 }
 
-hipError_t launch_decode_mm(const GemmArgs& a, void* workspace, size_t ws_bytes, int num_cus,
-                            hipStream_t stream) {
-  (void)num_cus;
-  const int mf = gemv_mf(a.M);
-  if (a.K % 128 != 0) {
-    switch (mf) {
-      case 1: return launch_general<1>(a, stream);
-      case 2: return launch_general<2>(a, stream);
-      case 3: return launch_general<3>(a, stream);
-      default: return launch_general<4>(a, stream);
-    }
-  }
+hipError_t launch_decode_mm(const GemmArgs& a, hipStream_t stream) {
   const GemvCfg c = gemv_cfg(a.M, a.N, a.K);
-  int splits = c.splits;
-  const size_t need = decode_workspace_bytes(a.M, a.N, a.K);
-  if (splits > 1 && (workspace == nullptr || ws_bytes < need)) splits = 1;
-  int32_t* counters = static_cast<int32_t*>(workspace);
-  int32_t* part = counters ? counters + kCounters : nullptr;
-  switch (mf) {
-    case 1:
-      return c.ns == 4 ? launch_dma<1, 4>(a, splits, part, counters, stream)
-                       : launch_dma<1, 8>(a, splits, part, counters, stream);
-    case 2:
-      return c.ns == 4 ? launch_dma<2, 4>(a, splits, part, counters, stream)
-                       : launch_dma<2, 6>(a, splits, part, counters, stream);
-    case 3: return launch_dma<3, 5>(a, splits, part, counters, stream);
-    default: return launch_dma<4, 5>(a, splits, part, counters, stream);
+  switch (c.kind) {
+    case GemvKind::kGeneral:
+      switch (c.mf) {
+        case 1: return launch_general<1>(a, stream);
+        case 2: return launch_general<2>(a, stream);
+        case 3: return launch_general<3>(a, stream);
+        default: return launch_general<4>(a, stream);
+      }
+    case GemvKind::kDma:
+      switch (c.mf) {
+        case 2: return launch_dma<2, 6>(a, stream);
+        case 3: return launch_dma<3, 5>(a, stream);
+        default: return launch_dma<4, 5>(a, stream);
+      }
+    default: break;
+  }
+  switch (c.mf) {
+    case 1: return c.w == 2 ? launch_reg<1, 1, 2, 4>(a, stream) : launch_reg<1, 1, 4, 4>(a, stream);
+    case 2: return c.rg == 2 ? launch_reg<2, 2, 4, 4>(a, stream) : launch_reg<2, 1, 4, 4>(a, stream);
+    case 3: return c.rg == 2 ? launch_reg<3, 2, 4, 3>(a, stream) : launch_reg<3, 1, 4, 4>(a, stream);
+    default: return c.rg == 2 ? launch_reg<4, 2, 4, 3>(a, stream) : launch_reg<4, 1, 4, 4>(a, stream);
   }
 }
 

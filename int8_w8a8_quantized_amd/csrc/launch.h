@@ -53,12 +53,8 @@ struct GemmArgs {
 };
 
 hipError_t launch_scaled_mm(const GemmArgs& a, hipStream_t stream);  // MFMA tiles, any M
-// M <= 64: weight streaming, split over K through the workspace when one of
-// decode_workspace_bytes(M, N, K) bytes is given (its counters zero on entry,
-// zero on exit); without it the whole K stays in one workgroup.
-hipError_t launch_decode_mm(const GemmArgs& a, void* workspace, size_t ws_bytes, int num_cus,
-                            hipStream_t stream);
-size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K);
+// M <= 64: weight streaming (no workspace).
+hipError_t launch_decode_mm(const GemmArgs& a, hipStream_t stream);
 // Name of the kernel instance launch_decode_mm / launch_scaled_mm runs for a shape.
 const char* decode_kernel_name(int64_t M, int64_t N, int64_t K);
 const char* scaled_mm_kernel_name(int64_t M, int64_t N, int64_t K);

@@ -49,9 +49,8 @@ _SIGS = {
     "w8a8_prepare_colsum": (_i32, [_p, _i64, _i64, _i64, _p, _p, _p]),
     "w8a8_prepare_requant_max": (_i32, [_p, _i64, _i64, _i64, _p, ctypes.POINTER(_i64), _i32, _p, _p, _p]),
     "w8a8_prepare_fp8_block_to_int8": (_i32, [_p, _p, _i64, _i64, _i64, _p, _p, _p, _p]),
-    "w8a8_scaled_mm_workspace_size": (ctypes.c_size_t, [_i64, _i64, _i64]),
     "w8a8_scaled_mm_int8": (_i32, [_p, _i64, _i64, _i64, _p, _i64, _i64, _p, _i32, _p, _i32,
-                                   _p, _p, _i32, _p, _p, _i32, _i64, _p, ctypes.c_size_t, _p]),
+                                   _p, _p, _i32, _p, _p, _i32, _i64, _p]),
     "w8a8_grouped_scaled_mm_int8": (_i32, [_p, _i64, _i64, _p, _p, _i64, _i64, _i64, _i64, _p,
                                            _p, _p, _p, _p, _i32, _i64, _p]),
     "w8a8_scaled_mm_kernel_name": (ctypes.c_char_p, [_i64, _i64, _i64]),
@@ -193,55 +192,27 @@ def prepare_fp8_block_to_int8(W8, S, Wq=None, s=None, err_flag=None):
     return Wq, s, err_flag
 
 
-def scaled_mm_workspace_size(M: int, N: int, K: int) -> int:
-    return int(load().w8a8_scaled_mm_workspace_size(M, N, K))
-
-
 def scaled_mm_kernel_name(M: int, N: int, K: int) -> str:
     """Name of the kernel instance scaled_mm_int8 launches for this shape."""
     return load().w8a8_scaled_mm_kernel_name(M, N, K).decode()
 
 
-_ws_cache = {}
-
-
-def _workspace(device, stream: int, nbytes: int):
-    """A zero-filled workspace kept per (device, stream). The library leaves a
-    workspace zero after each call, so one buffer serves every later call that
-    is ordered on the same stream."""
-    import torch
-    key = (device.index, stream)
-    ws = _ws_cache.get(key)
-    if ws is None or ws.numel() * 4 < nbytes:
-        ws = torch.zeros((nbytes + 3) // 4, dtype=torch.int32, device=device)
-        _ws_cache[key] = ws
-    return ws
-
-
 def scaled_mm_int8(xq, Wq, s_x, s_w, zp=None, colsum=None, azp_mode: int = AZP_NONE, bias=None,
-                   out_dtype: int = OUT_BF16, out=None, workspace=None):
+                   out_dtype: int = OUT_BF16, out=None):
     """xq int8 [M,K], Wq int8 [N,K], s_x float [M] or [1], s_w float [N] or [1],
     zp int32 [M] / colsum int32 [N] (AZP_PER_TOKEN) or azp_adj int32 [N] as
-    colsum (AZP_STATIC), bias bf16 [N]. Returns bf16 (or int32) [M,N].
-    workspace: None = a cached zero-filled buffer for this device and stream,
-    a tensor = that buffer (zero on first use), False = none (no split-K)."""
+    colsum (AZP_STATIC), bias bf16 [N]. Returns bf16 (or int32) [M,N]."""
     import torch
     M, K = xq.shape
     N = Wq.shape[0]
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16 if out_dtype == OUT_BF16 else torch.int32,
                           device=xq.device)
-    if workspace is None:
-        need = scaled_mm_workspace_size(M, N, K)
-        workspace = _workspace(xq.device, _stream(), need) if need else False
-    if workspace is False:
-        workspace = None
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = load().w8a8_scaled_mm_int8(_ptr(xq), M, K, xq.stride(0), _ptr(Wq), N, Wq.stride(0),
                                     _ptr(s_x), int(s_x.numel() != 1 or M == 1), _ptr(s_w),
                                     int(s_w.numel() != 1 or N == 1), _ptr(zp), _ptr(colsum), azp_mode,
                                     _ptr(bias), _ptr(out), out_dtype, out.stride(0) if M else N,
-                                    _ptr(workspace), ws_bytes, _stream())
+                                    _stream())
     _raise(st, "w8a8_scaled_mm_int8")
     return out
 

@@ -16,7 +16,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = W.header_functions()
-    assert len(names) == 12, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -85,7 +85,7 @@ def test_gemm_rejects_before_device_work(L):
     def mm(M=8, K=64, N=32, ldx=64, ldw=64, ldo=32, xq=FAKE, wq=FAKE, out=FAKE, sx=FAKE, sw=FAKE,
            zp=None, cs=None, azp=0, dt=0):
         return L.w8a8_scaled_mm_int8(xq, M, K, ldx, wq, N, ldw, sx, 1, sw, 1, zp, cs, azp, None, out,
-                                     dt, ldo, None, 0, None)
+                                     dt, ldo, None)
     assert mm(K=24) == W.ERR_INVALID_ARG
     assert mm(ldx=48) == W.ERR_INVALID_ARG
     assert mm(ldw=72) == W.ERR_INVALID_ARG
@@ -98,14 +98,6 @@ def test_gemm_rejects_before_device_work(L):
     assert mm(sw=None) == W.ERR_INVALID_ARG
     assert mm(M=1 << 26) == W.ERR_INVALID_ARG
     assert mm(M=0) == W.OK and mm(N=0) == W.OK
-    # decode (M <= 64) split over K: 4096 arrival counters, then int32 partial
-    # sums [splits, M, N] (splits from the decode launch table)
-    assert W.scaled_mm_workspace_size(64, 4096, 4096) == 0                    # one K range
-    assert W.scaled_mm_workspace_size(1, 100, 4096) == 4096 * 4 + 2 * 1 * 100 * 4
-    assert W.scaled_mm_workspace_size(1, 28672, 4096) == 4096 * 4 + 2 * 28672 * 4
-    assert W.scaled_mm_workspace_size(8, 4096, 14336) == 4096 * 4 + 4 * 8 * 4096 * 4
-    assert W.scaled_mm_workspace_size(8, 4096, 272) == 0      # K % 128 != 0: no split
-    assert W.scaled_mm_workspace_size(65, 4096, 4096) == 0    # not the decode path
 
 
 def test_grouped_rejects_before_device_work(L):

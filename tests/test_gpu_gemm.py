@@ -122,49 +122,52 @@ def test_empty():
     assert out.shape == (0, 8)
 
 
-DECODE_SEQ = [(1, 14336, 4096), (64, 4096, 200), (17, 14336, 96), (64, 14336, 4096), (3, 272, 64),
-              (48, 8192, 1000), (32, 4096, 300), (20, 256, 16400), (5, 512, 16390), (1, 256, 100)]
+# Every decode (M <= 64) kernel instance, with ragged M and N, K = 128 (one
+# step: three of four waves hold no K), and K not a multiple of 128.
+DECODE_CASES = [
+    (1, 4096, 4096, "gemv_reg_kernel<1, 1, 4, 4>"),
+    (7, 128, 300, "gemv_reg_kernel<1, 1, 4, 4>"),
+    (16, 4096, 16400, "gemv_reg_kernel<1, 1, 2, 4>"),
+    (32, 1024, 200, "gemv_reg_kernel<2, 1, 4, 4>"),
+    (17, 4096, 4100, "gemv_reg_kernel<2, 2, 4, 4>"),
+    (48, 8192, 1000, "gemv_reg_kernel<3, 1, 4, 4>"),
+    (33, 2048, 6000, "gemv_reg_kernel<3, 2, 4, 3>"),
+    (64, 14336, 4096, "gemv_reg_kernel<4, 1, 4, 4>"),
+    (60, 4096, 6144, "gemv_reg_kernel<4, 2, 4, 3>"),
+    (20, 256, 16400, "gemv_dma_kernel<2, 6>"),
+    (40, 512, 16390, "gemv_dma_kernel<3, 5>"),
+    (64, 384, 16384, "gemv_dma_kernel<4, 5>"),
+    (3, 272, 64, "gemv_i8_kernel<1, 2, 4, 8>"),
+    (64, 4112, 200, "gemv_i8_kernel<4, 2, 4, 8>"),
+]
 
 
-def test_decode_shape_sequence_shared_workspace():
-    """The decode paths over a sequence of shapes that share one workspace
-    (K split or not, ragged N, M not a multiple of 16, K not a multiple of
-    128): int32 exact every time, twice over, and the arrival counters at the
-    head of the workspace are back to zero after every call."""
-    need = max(W.scaled_mm_workspace_size(M, N, K) for (M, K, N) in DECODE_SEQ)
-    assert need > 0
-    ws = torch.zeros(need // 4, dtype=torch.int32, device="cuda:0")
-    for rep in range(2):
-        for i, (M, K, N) in enumerate(DECODE_SEQ):
-            d = _inputs(M, K, N, seed=10 + i)
-            note(f"decode sequence rep={rep} M={M} K={K} N={N} kernel={W.scaled_mm_kernel_name(M, N, K)}")
-            got = W.scaled_mm_int8(to_dev(d["xq"]), to_dev(d["w"]), to_dev(d["sx"]), to_dev(d["sw"]),
-                                   out_dtype=W.OUT_I32, workspace=ws)
-            torch.cuda.synchronize()
-            assert_equal(host(got), O.int_gemm(d["xq"], d["w"]).astype(np.int32), "decode int32")
-            assert int(torch.count_nonzero(ws[:4096])) == 0
-
-
-def test_decode_workspace_too_small_is_unused():
-    """A workspace smaller than the size query asks for is not touched (the
-    call keeps the whole K in one workgroup)."""
-    M, K, N = 1, 14336, 4096
-    assert W.scaled_mm_workspace_size(M, N, K) > 4096
-    ws = torch.full((1024,), 7, dtype=torch.int32, device="cuda:0")
-    d = _inputs(M, K, N, seed=30)
+@pytest.mark.parametrize("M,K,N,kernel", DECODE_CASES)
+def test_decode_paths(M, K, N, kernel):
+    """Each decode kernel instance: the launch table picks it, its int32
+    product is exact, and a bf16 call with per-token AZP and bias matches the
+    oracle's epilogue."""
+    assert W.scaled_mm_kernel_name(M, N, K) == kernel
+    d = _inputs(M, K, N, seed=M * 7 + N)
+    note(f"decode path M={M} K={K} N={N} kernel={kernel}")
     got = W.scaled_mm_int8(to_dev(d["xq"]), to_dev(d["w"]), to_dev(d["sx"]), to_dev(d["sw"]),
-                           out_dtype=W.OUT_I32, workspace=ws)
+                           out_dtype=W.OUT_I32)
     torch.cuda.synchronize()
     assert_equal(host(got), O.int_gemm(d["xq"], d["w"]).astype(np.int32), "decode int32")
-    assert bool((ws == 7).all())
+    _run(d, W.AZP_PER_TOKEN, bias=True)
 
 
-def test_decode_without_workspace():
-    d = _inputs(9, 8192, 256, seed=20)
-    got = W.scaled_mm_int8(to_dev(d["xq"]), to_dev(d["w"]), to_dev(d["sx"]), to_dev(d["sw"]),
-                           out_dtype=W.OUT_I32, workspace=False)
-    torch.cuda.synchronize()
-    assert_equal(host(got), O.int_gemm(d["xq"], d["w"]).astype(np.int32), "unsplit int32")
+def test_decode_shape_sequence():
+    """The decode shapes back to back, twice: exact every time (no state is
+    carried from one call to the next)."""
+    for rep in range(2):
+        for i, (M, K, N, _) in enumerate(DECODE_CASES):
+            d = _inputs(M, K, N, seed=10 + i)
+            note(f"decode sequence rep={rep} M={M} K={K} N={N}")
+            got = W.scaled_mm_int8(to_dev(d["xq"]), to_dev(d["w"]), to_dev(d["sx"]), to_dev(d["sw"]),
+                                   out_dtype=W.OUT_I32)
+            torch.cuda.synchronize()
+            assert_equal(host(got), O.int_gemm(d["xq"], d["w"]).astype(np.int32), "decode int32")
 
 
 # Every (tile, K step) variant of the MFMA path, with ragged M, N and a K that
