@@ -23,11 +23,14 @@
 // per-element division is replaced by t = fl(x * r) with r = fl(1 / s), which
 // is provably enough except near a rounding boundary: |t - fl(x/s)| <
 // |t| * 2^-22 whenever 1/s is a normal number (two roundings of relative
-// size 2^-24 in t, one in fl(x/s)), so if the distance from t to the nearest
-// half-integer exceeds |t| * 2^-22 both round to the same integer. Elements
-// that fail that test (about 1 in 16000), and rows whose scale is outside
-// (2^-100, 2^100), take the true division. Quotients of magnitude >= 1024
-// saturate every mode's clamp whichever way they round.
+// size 2^-24 in t, one in fl(x/s)). t is clamped to the mode's range L first
+// (127, or 512 before an asymmetric zero point; the bounds are integers, so
+// clamping and rounding commute, and a clamped t saturates either way), so
+// if t is farther than L * 2^-22 from every half-integer both round to the
+// same integer. t is rounded by adding 1.5 * 2^23, which leaves rint(t) in
+// the low mantissa bits (two's complement in the low byte). Chunks with an
+// element near a half-integer, and rows whose scale is outside
+// (2^-100, 2^100), take the true division.
 
 #include "device_common.h"
 #include "launch.h"
@@ -52,51 +55,61 @@ __device__ __forceinline__ RowParams finish_params(float s, int zp) {
   return p;
 }
 
-// rint(fl(x / s)) via the multiply when it provably agrees; flags the rest.
-__device__ __forceinline__ float quot_round(float x, const RowParams& p, bool& fix) {
-  const float t = x * p.r;
-  const float f = t - floorf(t);
-  const float at = fabsf(t);
-  const bool ok = p.fast && (fabsf(f - 0.5f) > at * 0x1p-22f || at >= 1024.0f);
-  fix = !ok;
-  return rne(t);
-}
+// Adding kMagic = 1.5 * 2^23 to a float of magnitude <= 2^22 rounds it to an
+// integer (ties to even) and leaves that integer + 0x400000 in the mantissa.
+constexpr float kMagic = 12582912.0f;
+constexpr uint32_t kMagicBits = 0x4B400000u;
 
-template <int MODE>
-__device__ __forceinline__ int finish_code(float rq, int zp) {
-  if (MODE == kDynSym || MODE == kStaticSym) return (int)fminf(fmaxf(rq, -127.0f), 127.0f);
-  return clampi((int)fminf(fmaxf(rq, -512.0f), 512.0f) + zp, -128, 127);
+// Low bytes of four words packed into one (v_perm_b32).
+__device__ __forceinline__ uint32_t low_bytes4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0c0c0400u);
+  const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x0c0c0400u);
+  return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
 }
 
 // Codes of one 16-byte chunk (8 bf16) as 8 bytes.
 template <int MODE>
 __device__ __forceinline__ uint2 codes8(uint4 v, const RowParams& p) {
+  constexpr bool kSym = MODE == kDynSym || MODE == kStaticSym;
+  constexpr float kLim = kSym ? 127.0f : 512.0f;  // range of rint(x/s) before the zero point
+  // |t| <= kLim after the clamp, so t and fl(x/s) differ by less than kLim * 2^-22
+  constexpr float kTie = 0.5f - kLim * 0x1p-22f;
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  float xs[8], rq[8];
-  uint32_t fix = 0;
+  float xs[8];
+  uint32_t m[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     xs[2 * i] = bf16_lo(w[i]);
     xs[2 * i + 1] = bf16_hi(w[i]);
   }
+  bool fix = !p.fast;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    bool f;
-    rq[e] = quot_round(xs[e], p, f);
-    fix |= (uint32_t)f << e;
+    const float t = fminf(fmaxf(xs[e] * p.r, -kLim), kLim);
+    const float r = t + kMagic;
+    fix |= fabsf(t - (r - kMagic)) >= kTie;
+    m[e] = __float_as_uint(r);
   }
-  if (__builtin_expect(fix != 0, 0)) {
+  if (__builtin_expect(fix, 0)) {
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      if ((fix >> e) & 1u) rq[e] = rne(xs[e] / p.s);
+      m[e] = __float_as_uint(fminf(fmaxf(rne(xs[e] / p.s), -kLim), kLim) + kMagic);
   }
-  int q[8];
+  if (!kSym) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) q[e] = finish_code<MODE>(rq[e], p.zp);
+    for (int e = 0; e < 8; ++e) m[e] = (uint32_t)clampi((int)(m[e] - kMagicBits) + p.zp, -128, 127);
+  }
   uint2 o;
-  o.x = pack4(q[0], q[1], q[2], q[3]);
-  o.y = pack4(q[4], q[5], q[6], q[7]);
+  o.x = low_bytes4(m[0], m[1], m[2], m[3]);
+  o.y = low_bytes4(m[4], m[5], m[6], m[7]);
   return o;
+}
+
+// Largest magnitude of one chunk folded into a.
+__device__ __forceinline__ void absmax8(uint4 v, float& a) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a = fmaxf(a, fmaxf(fabsf(bf16_lo(w[i])), fabsf(bf16_hi(w[i]))));
 }
 
 __device__ __forceinline__ void minmax8(uint4 v, float& lo, float& hi) {
@@ -151,10 +164,16 @@ __global__ __launch_bounds__(TPR < 256 ? 256 : TPR) void quant_kernel(
   RowParams p;
   if (MODE == kDynSym || MODE == kDynAsym) {
     float lo = 0.0f, hi = 0.0f;
+    if (MODE == kDynSym) {  // only the largest magnitude matters: hi = max |x|
 #pragma unroll
-    for (int c = 0; c < CH; ++c) minmax8(v[c], lo, hi);
-    lo = wave_min(lo);
-    hi = wave_max(hi);
+      for (int c = 0; c < CH; ++c) absmax8(v[c], hi);
+      hi = wave_max(hi);
+    } else {
+#pragma unroll
+      for (int c = 0; c < CH; ++c) minmax8(v[c], lo, hi);
+      lo = wave_min(lo);
+      hi = wave_max(hi);
+    }
     if (WPR > 1) {
       __shared__ float red_lo[WPR > 1 ? WPR : 1], red_hi[WPR > 1 ? WPR : 1];
       const int wv = sub >> 6;
