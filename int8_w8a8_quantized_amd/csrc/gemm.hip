@@ -151,7 +151,7 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const TileLoc& 
   for (int q = 0; q < 4; ++q) {
     const EpiCol c = load_col(a, col0 + q, sw, bias);
     csw[q] = c.sw;
-    cbias[q] = c.bias;
+    cbias[q] = c.bias();
     ccorr[q] = c.corr;
     cok[q] = c.ok;
   }

@@ -42,15 +42,16 @@ __device__ __forceinline__ i32x4 as_i32x4(uint4 v) {
 // bf16(float(c) * s_x * s_w + bias) or c itself.
 struct EpiRow {
   float sx;
-  int zp;   // per-token zero point (0 unless AZP_PER_TOKEN)
+  int zp;   // per-token zero point (used only with AZP_PER_TOKEN)
   bool ok;  // row inside the output
   int64_t out_row;
 };
 struct EpiCol {
   float sw;
-  int corr;   // colsum[n] (per-token AZP) or azp_adj[n] (static AZP), else 0
-  float bias;
+  int corr;            // colsum[n] (per-token AZP) or azp_adj[n] (static AZP); unused otherwise
+  uint32_t bias_bits;  // bf16 bits of bias[n] (meaningless without bias), widened when used
   bool ok;
+  __device__ __forceinline__ float bias() const { return __uint_as_float(bias_bits << 16); }
 };
 
 __device__ __forceinline__ void epilogue_store(const GemmArgs& a, const EpiRow& r, const EpiCol& c,
@@ -63,7 +64,7 @@ __device__ __forceinline__ void epilogue_store(const GemmArgs& a, const EpiRow& 
     reinterpret_cast<int32_t*>(a.out)[r.out_row * a.ldo + col] = v;
   } else {
     float y = (float)v * r.sx * c.sw;
-    if (a.bias) y += c.bias;
+    if (a.bias) y += c.bias();
     reinterpret_cast<uint16_t*>(a.out)[r.out_row * a.ldo + col] = f32_to_bf16_rne(y);
   }
 }
@@ -73,9 +74,12 @@ __device__ __forceinline__ EpiCol load_col(const GemmArgs& a, int64_t n, const f
   EpiCol c;
   c.ok = n < a.N;
   const int64_t nn = c.ok ? n : 0;
-  c.sw = a.sw_per_channel ? sw[nn] : sw[0];
-  c.corr = (a.azp_mode != 0) ? a.colsum[nn] : 0;
-  c.bias = bias ? bf16_to_f32(bias[nn]) : 0.0f;
+  // Addresses are selected instead of values (a missing operand reads the
+  // scale, which always exists, and is never used), so no instruction next
+  // to the loads consumes them and the wait for them lands at the epilogue.
+  c.sw = sw[a.sw_per_channel ? nn : 0];
+  c.corr = *(a.azp_mode != 0 ? a.colsum + nn : reinterpret_cast<const int32_t*>(sw));
+  c.bias_bits = *(bias ? bias + nn : reinterpret_cast<const uint16_t*>(sw));
   return c;
 }
 

@@ -75,8 +75,8 @@ struct GemvEpi {
       er[j].ok = e < per && m < a.M;
       const int64_t mm = er[j].ok ? m : 0;
       er[j].out_row = mm;
-      er[j].sx = a.sx_per_token ? a.s_x[mm] : a.s_x[0];
-      er[j].zp = (a.azp_mode == 1) ? a.zp[mm] : 0;
+      er[j].sx = a.s_x[a.sx_per_token ? mm : 0];
+      er[j].zp = *(a.azp_mode == 1 ? a.zp + mm : reinterpret_cast<const int32_t*>(a.s_x));
       ec[j] = load_col(a, nn, a.s_w, a.bias);  // a row past N is marked not ok
       n[j] = nn;
     }
@@ -247,8 +247,8 @@ __global__ __launch_bounds__(256) void gemv_dma_kernel(GemmArgs a) {
       er[f][r].ok = m < a.M;
       const int64_t mm = er[f][r].ok ? m : 0;
       er[f][r].out_row = mm;
-      er[f][r].sx = a.sx_per_token ? a.s_x[mm] : a.s_x[0];
-      er[f][r].zp = (a.azp_mode == 1) ? a.zp[mm] : 0;
+      er[f][r].sx = a.s_x[a.sx_per_token ? mm : 0];
+      er[f][r].zp = *(a.azp_mode == 1 ? a.zp + mm : reinterpret_cast<const int32_t*>(a.s_x));
     }
 
   // ---- fragments: wave w reads weight rows 16w + lane%16, activation rows
