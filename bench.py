@@ -188,13 +188,15 @@ def main():
                                s_x=torch.empty(M, dtype=torch.float32, device=dev),
                                out=torch.empty((M, N), dtype=torch.bfloat16, device=dev))
     step_bytes = sum(gemm_bytes(M, K, N, bias=True) + quant_bytes(M, K) for (M, K, N) in shapes)
+    ws_bytes = max(W.scaled_mm_workspace_size(M, N, K) for (M, K, N) in shapes)
+    workspace = torch.empty(max(16, ws_bytes), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     def gemm(shape, copy):
         M, K, N = shape
         a, p = acts[shape], pools[(K, N)]
         W.scaled_mm_int8(a["xq"], p["w"][copy % len(p["w"])], a["s_x"], p["s_w"], bias=p["bias"],
-                         out=a["out"])
+                         out=a["out"], workspace=workspace)
 
     def quant(shape):
         a = acts[shape]

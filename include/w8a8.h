@@ -181,6 +181,14 @@ w8a8_status w8a8_prepare_fp8_block_to_int8(const uint8_t* W8, const float* S, in
                                            int64_t N, int64_t K, int8_t* Wq, float* s,
                                            int32_t* err_flag, void* stream);
 
+/* Bytes of workspace w8a8_scaled_mm_int8 can use for this shape (0 when it
+ * uses none). With at least this many bytes, decode shapes (M <= 64) with a
+ * long K split K over workgroups and add the ranges in a second kernel; with
+ * fewer (or NULL) the call runs unsplit, with the same result. No state is
+ * kept in it between calls, so any buffer serves; calls that may run at the
+ * same time (other streams) need buffers of their own. */
+size_t w8a8_scaled_mm_workspace_size(int64_t M, int64_t N, int64_t K);
+
 /* The scaled int8 GEMM with its fused epilogue ([SGLang] 핵심 코드 분석 §3-§4):
  *   acc[t,n] = sum_k xq[t,k] * Wq[n,k]        (exact int32)
  *   c = acc - zp[t]*colsum[n]   (azp_mode W8A8_AZP_PER_TOKEN)
@@ -193,6 +201,7 @@ w8a8_status w8a8_prepare_fp8_block_to_int8(const uint8_t* W8, const float* S, in
  * s_w float [N] if s_w_per_channel else [1]; zp int32 [M] and colsum int32 [N]
  * (PER_TOKEN), or azp_adj int32 [N] (STATIC) -- pass it as `colsum`;
  * bias bf16 [N] or NULL; out bf16 or int32 [M,N] (ldo).
+ * workspace: device memory, 16-byte aligned, see w8a8_scaled_mm_workspace_size.
  * Requires K % 16 == 0, 1 <= K <= W8A8_MAX_K, xq/Wq/out 16-byte aligned,
  * ldx % 16 == 0, ldw % 16 == 0, ld* >= the row length. */
 w8a8_status w8a8_scaled_mm_int8(const int8_t* xq, int64_t M, int64_t K, int64_t ldx,
@@ -201,7 +210,8 @@ w8a8_status w8a8_scaled_mm_int8(const int8_t* xq, int64_t M, int64_t K, int64_t 
                                 const float* s_w, int32_t s_w_per_channel,
                                 const int32_t* zp, const int32_t* colsum, int32_t azp_mode,
                                 const uint16_t* bias, void* out, int32_t out_dtype,
-                                int64_t ldo, void* stream);
+                                int64_t ldo, void* workspace, size_t workspace_bytes,
+                                void* stream);
 
 /* Grouped (MoE) scaled GEMM: the rows of the expert-sorted activation are
  * split by expert_offsets (device int32 [E+1], non-decreasing, [0] == 0,

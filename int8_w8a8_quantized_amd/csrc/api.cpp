@@ -221,6 +221,11 @@ w8a8_status w8a8_prepare_fp8_block_to_int8(const uint8_t* W8, const float* S, in
                     "fp8_block_to_int8 launch");
 }
 
+size_t w8a8_scaled_mm_workspace_size(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || M > w8a8::kDecodeMaxM || N >= kMaxDim || K <= 0 || K > W8A8_MAX_K) return 0;
+  return w8a8::decode_workspace_bytes(M, N, K);
+}
+
 static w8a8_status check_gemm_common(const int8_t* xq, int64_t ldx, const int8_t* Wq, int64_t K,
                                      const void* out, int32_t out_dtype, int64_t ldo, int64_t N) {
   W8A8_REQUIRE(xq && Wq && out, "xq, Wq and out must not be NULL");
@@ -235,7 +240,8 @@ w8a8_status w8a8_scaled_mm_int8(const int8_t* xq, int64_t M, int64_t K, int64_t 
                                 int64_t N, int64_t ldw, const float* s_x, int32_t s_x_per_token,
                                 const float* s_w, int32_t s_w_per_channel, const int32_t* zp,
                                 const int32_t* colsum, int32_t azp_mode, const uint16_t* bias, void* out,
-                                int32_t out_dtype, int64_t ldo, void* stream) {
+                                int32_t out_dtype, int64_t ldo, void* workspace, size_t workspace_bytes,
+                                void* stream) {
   w8a8_status st;
   if ((st = check_dim(M, "M")) != W8A8_OK) return st;
   if ((st = check_dim(N, "N")) != W8A8_OK) return st;
@@ -248,6 +254,7 @@ w8a8_status w8a8_scaled_mm_int8(const int8_t* xq, int64_t M, int64_t K, int64_t 
   if (azp_mode == W8A8_AZP_PER_TOKEN) W8A8_REQUIRE(zp && colsum, "AZP_PER_TOKEN needs zp and colsum");
   if (azp_mode == W8A8_AZP_STATIC) W8A8_REQUIRE(colsum, "AZP_STATIC needs azp_adj (passed as colsum)");
   if ((st = check_tiles(M, 0, N)) != W8A8_OK) return st;
+  W8A8_REQUIRE(workspace == nullptr || aligned16(workspace), "workspace must be 16-byte aligned");
   if ((st = check_current_device()) != W8A8_OK) return st;
   w8a8::GemmArgs a{};
   a.A = xq;
@@ -270,7 +277,7 @@ w8a8_status w8a8_scaled_mm_int8(const int8_t* xq, int64_t M, int64_t K, int64_t 
   a.ldo = ldo;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = (M <= w8a8::kDecodeMaxM)
-                           ? w8a8::launch_decode_mm(a, s)
+                           ? w8a8::launch_decode_mm(a, workspace, workspace_bytes, s)
                            : w8a8::launch_scaled_mm(a, s);
   return hip_status(e, "scaled_mm launch");
 }
@@ -320,7 +327,7 @@ w8a8_status w8a8_grouped_scaled_mm_int8(const int8_t* xq, int64_t ldx, int64_t M
 
 const char* w8a8_scaled_mm_kernel_name(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K <= 0) return "";
-  return (M <= w8a8::kDecodeMaxM) ? w8a8::decode_kernel_name(M, N, K) : w8a8::scaled_mm_kernel_name(M, N, K);
+  return (M <= w8a8::kDecodeMaxM) ? w8a8::decode_kernel_name(M, N, K, w8a8::decode_workspace_bytes(M, N, K)) : w8a8::scaled_mm_kernel_name(M, N, K);
 }
 
 const char* w8a8_status_string(w8a8_status s) {

@@ -288,6 +288,139 @@ __global__ __launch_bounds__(256) void gemv_dma_kernel(GemmArgs a) {
     for (int r = 0; r < 4; ++r) epilogue_store(a, er[f][r], col, n, acc[f][r]);
 }
 
+// ---------------------------------------------- shared-activation split kernel
+// For M > 16 with a long K and few weight rows. The L1 fill of a CU (HBM and
+// L2 traffic together) is the limit there: the register kernel's 16-row
+// workgroups each read the whole activation, four times the weight bytes at
+// M = 64. Here the 4 waves of a workgroup own 16 weight rows each and walk
+// the same K steps, so one activation stage (16 * MF rows x 128 bytes, whole
+// lines, loaded cooperatively into registers with the weights) serves 64
+// weight rows: it is written to a double-buffered LDS stage and, after a
+// barrier, every wave reads its fragments there. Weight lines ride each
+// wave's register ring and LDS transpose as in the register kernel. K is cut
+// into `splits` ranges, one per workgroup; each workgroup stores its int32
+// tile in accumulator order (256 contiguous bytes per wave instruction) to
+// the caller's workspace, and gemv_reduce_kernel adds the ranges and applies
+// the epilogue. The stage buffer written at step i was last read at step
+// i - 2, before every wave passed the barrier of step i - 1.
+constexpr int kSharedWaves = 4;
+
+template <int MF, int U>
+__global__ __launch_bounds__(kSharedWaves * 64) void gemv_shared_kernel(GemmArgs a, int splits,
+                                                                        int steps_per_split,
+                                                                        int32_t* __restrict__ part) {
+  constexpr int W = kSharedWaves, BK = 128, XR = 16 * MF;
+  constexpr int AI = XR / 8;            // activation line instructions per step
+  constexpr int AQ = (AI + W - 1) / W;  // per wave (the last may repeat)
+  constexpr int PER = MF * 256;         // accumulator ints of one wave
+  __shared__ __attribute__((aligned(1024))) int8_t abuf[2][XR * BK];
+  __shared__ __attribute__((aligned(1024))) int8_t tbuf[W][16 * BK];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rb = blockIdx.x / splits, sp = blockIdx.x % splits;
+  const int64_t n0 = (int64_t)rb * 16 * W + 16 * wave;  // this wave's first weight row
+  const int nsteps = (int)(a.K / BK);
+  const int s_begin = sp * steps_per_split;
+  const int nk = max(min(nsteps, s_begin + steps_per_split) - s_begin, 0);
+  int8_t* tb = tbuf[wave];
+
+  const int8_t* wsrc[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    wsrc[h] = a.B + gemv_min(n0 + 8 * h + (lane >> 3), a.N - 1) * a.ldb + (lane & 7) * 16;
+  // activation line instruction j: stage rows 8j .. 8j+7 (rows past M repeat row M-1)
+  const int8_t* asrc[AQ];
+  int adst[AQ];
+#pragma unroll
+  for (int q = 0; q < AQ; ++q) {
+    const int j = min(wave * AQ + q, AI - 1);
+    const int row = 8 * j + (lane >> 3);
+    asrc[q] = a.A + gemv_min(row, a.M - 1) * a.lda + (lane & 7) * 16;
+    adst[q] = row * BK + (((lane & 7) ^ gemv_swz(row)) * 16);
+  }
+  u32x4 wr[U][2], xr[U][AQ];
+  // step j of this range into ring slot u; past the end: a reload of the last step
+  auto issue = [&](int u, int j) __attribute__((always_inline)) {
+    const int64_t k0 = (int64_t)(s_begin + min(j, nk - 1)) * BK;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      wr[u][h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wsrc[h] + k0));
+#pragma unroll
+    for (int q = 0; q < AQ; ++q) xr[u][q] = *reinterpret_cast<const u32x4*>(asrc[q] + k0);
+  };
+  i32x4 acc[MF];
+#pragma unroll
+  for (int f = 0; f < MF; ++f) acc[f] = i32x4{0, 0, 0, 0};
+  if (nk > 0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) issue(u, u);
+  }
+  for (int i0 = 0; i0 < nk; i0 += U) {  // nk is the same for every wave of the workgroup
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u;
+      if (i < nk) {
+        int8_t* ab = abuf[i & 1];
+#pragma unroll
+        for (int q = 0; q < AQ; ++q) *reinterpret_cast<u32x4*>(ab + adst[q]) = xr[u][q];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int row = 8 * h + (lane >> 3);
+          *reinterpret_cast<u32x4*>(tb + row * BK + (((lane & 7) ^ gemv_swz(row)) * 16)) = wr[u][h];
+        }
+        // the stage is complete once every wave's writes have landed (no vmcnt
+        // wait here: the ring's later loads stay in flight)
+        __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int c = 4 * kb + (lane >> 4);
+          const int wrow = lane & 15;
+          const i32x4 wf = *reinterpret_cast<const i32x4*>(tb + wrow * BK + ((c ^ gemv_swz(wrow)) * 16));
+#pragma unroll
+          for (int f = 0; f < MF; ++f) {
+            const int xrow = 16 * f + (lane & 15);
+            const i32x4 xf = *reinterpret_cast<const i32x4*>(ab + xrow * BK + ((c ^ gemv_swz(xrow)) * 16));
+            acc[f] = mfma16x16x64(xf, wf, acc[f]);
+          }
+        }
+      }
+      issue(u, i + U);
+    }
+  }
+  // lane holds tokens 16f + 4*(lane/16) + r of weight row n0 + lane%16
+  int32_t* dst = part + (((int64_t)rb * splits + sp) * W + wave) * PER + lane;
+#pragma unroll
+  for (int f = 0; f < MF; ++f)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dst[(f * 4 + r) * 64] = acc[f][r];
+}
+
+// Sum of the K ranges' tiles and the epilogue; one thread per accumulator
+// element, in the order gemv_shared_kernel stored them.
+template <int MF>
+__global__ __launch_bounds__(256) void gemv_reduce_kernel(GemmArgs a, int splits,
+                                                          const int32_t* __restrict__ part) {
+  constexpr int W = kSharedWaves, PER = MF * 256;
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over row blocks x waves x PER
+  const int64_t rbw = e / PER;                                 // row block * W + wave
+  const int pe = (int)(e % PER);
+  const int64_t rb = rbw / W;
+  const int wave = (int)(rbw % W);
+  const int f = pe / 256, r = (pe / 64) % 4, lane = pe % 64;
+  const int64_t n = rb * 16 * W + 16 * wave + (lane & 15);
+  const int64_t m = 16 * f + 4 * (lane >> 4) + r;
+  if (n >= a.N || m >= a.M) return;
+  const int32_t* src = part + (rb * splits * W + wave) * PER + pe;
+  int v = 0;
+  for (int s = 0; s < splits; ++s) v += src[(int64_t)s * W * PER];
+  EpiRow er;
+  er.ok = true;
+  er.out_row = m;
+  er.sx = a.s_x[a.sx_per_token ? m : 0];
+  er.zp = (a.azp_mode == 1) ? a.zp[m] : 0;
+  epilogue_store(a, er, load_col(a, n, a.s_w, a.bias), n, v);
+}
+
 // ------------------------------------------------------------- general kernel
 // A workgroup of W waves owns 16 * NB weight rows over the whole K (no
 // cross-workgroup reduction). K is cut into 64-byte steps (one
@@ -412,25 +545,46 @@ namespace {
 //    2 once there are 1024+ row groups (the waves then live long enough);
 //  - M > 16 with 16384+ weight rows: the direct-to-LDS kernel (one
 //    activation stage serves 64 weight rows);
+//  - M > 16, 64 steps of K or more and a workspace: the shared-activation
+//    kernel over about 256 workgroups (K ranges of at least 16 steps), then
+//    the reduction;
 //  - otherwise the register kernel, with 32 rows per workgroup when 16-row
 //    groups would need between one and two workgroups per CU (a half-empty
 //    second round costs more than the larger tile).
-enum class GemvKind { kReg, kDma, kGeneral };
+enum class GemvKind { kReg, kDma, kShared, kGeneral };
 struct GemvCfg {
   GemvKind kind;
-  int mf, rg, w, u;  // u: ring steps (register kernel) or LDS stages (DMA kernel)
+  int mf, rg, w, u;  // u: ring steps (register / shared kernels) or LDS stages (DMA kernel)
+  int splits;        // K ranges of the shared kernel
 };
 
 int gemv_mf(int64_t M) { return (int)std::min<int64_t>((M + 15) / 16, 4); }
 
-GemvCfg gemv_cfg(int64_t M, int64_t N, int64_t K) {
+// The shared kernel's K ranges for this shape (0: not used).
+int shared_splits(int64_t M, int64_t N, int64_t K) {
+  if (gemv_mf(M) == 1 || K % 128 != 0 || N >= 16384) return 0;
+  const int64_t nsteps = K / 128, rbs = (N + 63) / 64;
+  if (nsteps < 64) return 0;
+  const int64_t s = std::min<int64_t>(std::max<int64_t>(256 / rbs, 1), std::min<int64_t>(8, nsteps / 16));
+  return s >= 2 ? (int)s : 0;
+}
+
+size_t shared_workspace_bytes(int64_t M, int64_t N, int splits) {
+  const int64_t rbs = (N + 63) / 64;
+  return (size_t)splits * rbs * kSharedWaves * gemv_mf(M) * 256 * sizeof(int32_t);
+}
+
+GemvCfg gemv_cfg(int64_t M, int64_t N, int64_t K, size_t ws_bytes) {
   const int mf = gemv_mf(M);
-  if (K % 128 != 0) return {GemvKind::kGeneral, mf, 2, 4, 8};
+  if (K % 128 != 0) return {GemvKind::kGeneral, mf, 2, 4, 8, 1};
   const int64_t groups = (N + 15) / 16;
-  if (mf == 1) return {GemvKind::kReg, 1, 1, groups >= 1024 ? 2 : 4, 4};
-  if (N >= 16384) return {GemvKind::kDma, mf, 4, 4, mf == 2 ? 6 : 5};
-  if (groups > 256 && groups <= 512) return {GemvKind::kReg, mf, 2, 4, mf == 2 ? 4 : 3};
-  return {GemvKind::kReg, mf, 1, 4, 4};
+  if (mf == 1) return {GemvKind::kReg, 1, 1, groups >= 1024 ? 2 : 4, 4, 1};
+  if (N >= 16384) return {GemvKind::kDma, mf, 4, 4, mf == 2 ? 6 : 5, 1};
+  const int s = shared_splits(M, N, K);
+  if (s > 0 && ws_bytes >= shared_workspace_bytes(M, N, s))
+    return {GemvKind::kShared, mf, 1, kSharedWaves, mf == 2 ? 8 : 6, s};
+  if (groups > 256 && groups <= 512) return {GemvKind::kReg, mf, 2, 4, mf == 2 ? 4 : 3, 1};
+  return {GemvKind::kReg, mf, 1, 4, 4, 1};
 }
 
 template <int MF, int RG, int W, int U>
@@ -447,6 +601,21 @@ hipError_t launch_dma(const GemmArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int MF, int U>
+hipError_t launch_shared(const GemmArgs& a, int splits, int32_t* part, hipStream_t stream) {
+  const int64_t rbs = (a.N + 63) / 64;
+  const int64_t nsteps = a.K / 128;
+  const int sps = (int)((nsteps + splits - 1) / splits);
+  hipLaunchKernelGGL((gemv_shared_kernel<MF, U>), dim3((unsigned)(rbs * splits)), dim3(kSharedWaves * 64), 0,
+                     stream, a, splits, sps, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t elems = rbs * kSharedWaves * MF * 256;
+  hipLaunchKernelGGL((gemv_reduce_kernel<MF>), dim3((unsigned)((elems + 255) / 256)), dim3(256), 0, stream,
+                     a, splits, part);
+  return hipGetLastError();
+}
+
 template <int MF>
 hipError_t launch_general(const GemmArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((gemv_i8_kernel<MF, 2, 4, 8>), dim3((unsigned)((a.N + 31) / 32)), dim3(256), 0,
@@ -456,8 +625,13 @@ hipError_t launch_general(const GemmArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-const char* decode_kernel_name(int64_t M, int64_t N, int64_t K) {
-  const GemvCfg c = gemv_cfg(M, N, K);
+size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  const int s = shared_splits(M, N, K);
+  return s > 0 ? shared_workspace_bytes(M, N, s) : 0;
+}
+
+const char* decode_kernel_name(int64_t M, int64_t N, int64_t K, size_t ws_bytes) {
+  const GemvCfg c = gemv_cfg(M, N, K, ws_bytes);
   switch (c.kind) {
     case GemvKind::kGeneral: {
       static const char* gen[4] = {"gemv_i8_kernel<1, 2, 4, 8>", "gemv_i8_kernel<2, 2, 4, 8>",
@@ -467,6 +641,11 @@ const char* decode_kernel_name(int64_t M, int64_t N, int64_t K) {
     case GemvKind::kDma: {
       static const char* dma[3] = {"gemv_dma_kernel<2, 6>", "gemv_dma_kernel<3, 5>", "gemv_dma_kernel<4, 5>"};
       return dma[c.mf - 2];
+    }
+    case GemvKind::kShared: {
+      static const char* shr[3] = {"gemv_shared_kernel<2, 8>", "gemv_shared_kernel<3, 6>",
+                                   "gemv_shared_kernel<4, 6>"};
+      return shr[c.mf - 2];
     }
     default: break;
   }
@@ -478,8 +657,9 @@ const char* decode_kernel_name(int64_t M, int64_t N, int64_t K) {
   return c.rg == 2 ? reg2[c.mf - 2] : reg1[c.mf - 2];
 }
 
-hipError_t launch_decode_mm(const GemmArgs& a, hipStream_t stream) {
-  const GemvCfg c = gemv_cfg(a.M, a.N, a.K);
+hipError_t launch_decode_mm(const GemmArgs& a, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  const GemvCfg c = gemv_cfg(a.M, a.N, a.K, workspace ? ws_bytes : 0);
+  int32_t* part = static_cast<int32_t*>(workspace);
   switch (c.kind) {
     case GemvKind::kGeneral:
       switch (c.mf) {
@@ -493,6 +673,12 @@ hipError_t launch_decode_mm(const GemmArgs& a, hipStream_t stream) {
         case 2: return launch_dma<2, 6>(a, stream);
         case 3: return launch_dma<3, 5>(a, stream);
         default: return launch_dma<4, 5>(a, stream);
+      }
+    case GemvKind::kShared:
+      switch (c.mf) {
+        case 2: return launch_shared<2, 8>(a, c.splits, part, stream);
+        case 3: return launch_shared<3, 6>(a, c.splits, part, stream);
+        default: return launch_shared<4, 6>(a, c.splits, part, stream);
       }
     default: break;
   }

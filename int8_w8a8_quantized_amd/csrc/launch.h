@@ -53,10 +53,13 @@ struct GemmArgs {
 };
 
 hipError_t launch_scaled_mm(const GemmArgs& a, hipStream_t stream);  // MFMA tiles, any M
-// M <= 64: weight streaming (no workspace).
-hipError_t launch_decode_mm(const GemmArgs& a, hipStream_t stream);
+// M <= 64: weight streaming. Some shapes split K over workgroups when a
+// workspace of decode_workspace_bytes(M, N, K) bytes is given (no state is
+// kept in it between calls); without it they run unsplit.
+hipError_t launch_decode_mm(const GemmArgs& a, void* workspace, size_t ws_bytes, hipStream_t stream);
+size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K);
 // Name of the kernel instance launch_decode_mm / launch_scaled_mm runs for a shape.
-const char* decode_kernel_name(int64_t M, int64_t N, int64_t K);
+const char* decode_kernel_name(int64_t M, int64_t N, int64_t K, size_t ws_bytes);
 const char* scaled_mm_kernel_name(int64_t M, int64_t N, int64_t K);
 constexpr int64_t kDecodeMaxM = 64;
 hipError_t launch_grouped_mm(const GemmArgs& a, hipStream_t stream);

@@ -49,8 +49,9 @@ _SIGS = {
     "w8a8_prepare_colsum": (_i32, [_p, _i64, _i64, _i64, _p, _p, _p]),
     "w8a8_prepare_requant_max": (_i32, [_p, _i64, _i64, _i64, _p, ctypes.POINTER(_i64), _i32, _p, _p, _p]),
     "w8a8_prepare_fp8_block_to_int8": (_i32, [_p, _p, _i64, _i64, _i64, _p, _p, _p, _p]),
+    "w8a8_scaled_mm_workspace_size": (ctypes.c_size_t, [_i64, _i64, _i64]),
     "w8a8_scaled_mm_int8": (_i32, [_p, _i64, _i64, _i64, _p, _i64, _i64, _p, _i32, _p, _i32,
-                                   _p, _p, _i32, _p, _p, _i32, _i64, _p]),
+                                   _p, _p, _i32, _p, _p, _i32, _i64, _p, ctypes.c_size_t, _p]),
     "w8a8_grouped_scaled_mm_int8": (_i32, [_p, _i64, _i64, _p, _p, _i64, _i64, _i64, _i64, _p,
                                            _p, _p, _p, _p, _i32, _i64, _p]),
     "w8a8_scaled_mm_kernel_name": (ctypes.c_char_p, [_i64, _i64, _i64]),
@@ -192,27 +193,55 @@ def prepare_fp8_block_to_int8(W8, S, Wq=None, s=None, err_flag=None):
     return Wq, s, err_flag
 
 
+def scaled_mm_workspace_size(M: int, N: int, K: int) -> int:
+    """Bytes of workspace scaled_mm_int8 can use for this shape (0: none)."""
+    return int(load().w8a8_scaled_mm_workspace_size(M, N, K))
+
+
+_ws_cache = {}
+
+
+def _workspace(device, stream: int, nbytes: int):
+    """A workspace of at least nbytes kept per (device, stream); the library
+    keeps no state in it, so calls ordered on one stream can share it."""
+    import torch
+    key = (device.index, stream)
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    return ws
+
+
 def scaled_mm_kernel_name(M: int, N: int, K: int) -> str:
     """Name of the kernel instance scaled_mm_int8 launches for this shape."""
     return load().w8a8_scaled_mm_kernel_name(M, N, K).decode()
 
 
 def scaled_mm_int8(xq, Wq, s_x, s_w, zp=None, colsum=None, azp_mode: int = AZP_NONE, bias=None,
-                   out_dtype: int = OUT_BF16, out=None):
+                   out_dtype: int = OUT_BF16, out=None, workspace=None):
     """xq int8 [M,K], Wq int8 [N,K], s_x float [M] or [1], s_w float [N] or [1],
     zp int32 [M] / colsum int32 [N] (AZP_PER_TOKEN) or azp_adj int32 [N] as
-    colsum (AZP_STATIC), bias bf16 [N]. Returns bf16 (or int32) [M,N]."""
+    colsum (AZP_STATIC), bias bf16 [N]. Returns bf16 (or int32) [M,N].
+    workspace: None = a buffer cached per device and stream, sized by
+    scaled_mm_workspace_size; a tensor = that buffer; False = none (unsplit)."""
     import torch
     M, K = xq.shape
     N = Wq.shape[0]
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16 if out_dtype == OUT_BF16 else torch.int32,
                           device=xq.device)
+    if workspace is None:
+        need = scaled_mm_workspace_size(M, N, K)
+        workspace = _workspace(xq.device, _stream(), need) if need else False
+    if workspace is False:
+        workspace = None
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = load().w8a8_scaled_mm_int8(_ptr(xq), M, K, xq.stride(0), _ptr(Wq), N, Wq.stride(0),
                                     _ptr(s_x), int(s_x.numel() != 1 or M == 1), _ptr(s_w),
                                     int(s_w.numel() != 1 or N == 1), _ptr(zp), _ptr(colsum), azp_mode,
                                     _ptr(bias), _ptr(out), out_dtype, out.stride(0) if M else N,
-                                    _stream())
+                                    _ptr(workspace), ws_bytes, _stream())
     _raise(st, "w8a8_scaled_mm_int8")
     return out
 

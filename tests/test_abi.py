@@ -16,7 +16,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = W.header_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -85,7 +85,7 @@ def test_gemm_rejects_before_device_work(L):
     def mm(M=8, K=64, N=32, ldx=64, ldw=64, ldo=32, xq=FAKE, wq=FAKE, out=FAKE, sx=FAKE, sw=FAKE,
            zp=None, cs=None, azp=0, dt=0):
         return L.w8a8_scaled_mm_int8(xq, M, K, ldx, wq, N, ldw, sx, 1, sw, 1, zp, cs, azp, None, out,
-                                     dt, ldo, None)
+                                     dt, ldo, None, 0, None)
     assert mm(K=24) == W.ERR_INVALID_ARG
     assert mm(ldx=48) == W.ERR_INVALID_ARG
     assert mm(ldw=72) == W.ERR_INVALID_ARG
@@ -98,6 +98,19 @@ def test_gemm_rejects_before_device_work(L):
     assert mm(sw=None) == W.ERR_INVALID_ARG
     assert mm(M=1 << 26) == W.ERR_INVALID_ARG
     assert mm(M=0) == W.OK and mm(N=0) == W.OK
+
+    # decode (M <= 64) shapes with 64+ steps of K and fewer than 16384 weight
+    # rows split K over workgroups: int32 tiles [splits][row blocks of 64][4
+    # waves][16*MF x 16], splits = min(256 / row blocks, 8, steps / 16)
+    assert W.scaled_mm_workspace_size(64, 4096, 14336) == 4 * 64 * 4 * 4 * 256 * 4
+    assert W.scaled_mm_workspace_size(32, 4096, 14336) == 4 * 64 * 4 * 2 * 256 * 4
+    assert W.scaled_mm_workspace_size(48, 1000, 8192) == 4 * 16 * 4 * 3 * 256 * 4
+    assert W.scaled_mm_workspace_size(17, 100, 8192) == 4 * 2 * 4 * 2 * 256 * 4
+    assert W.scaled_mm_workspace_size(8, 4096, 14336) == 0      # M <= 16: register kernel
+    assert W.scaled_mm_workspace_size(64, 4096, 4096) == 0      # fewer than 64 steps
+    assert W.scaled_mm_workspace_size(64, 28672, 14336) == 0    # 16384+ weight rows
+    assert W.scaled_mm_workspace_size(40, 4096, 8200) == 0      # K % 128 != 0
+    assert W.scaled_mm_workspace_size(65, 4096, 14336) == 0     # not the decode path
 
 
 def test_grouped_rejects_before_device_work(L):

@@ -130,13 +130,17 @@ DECODE_CASES = [
     (16, 4096, 16400, "gemv_reg_kernel<1, 1, 2, 4>"),
     (32, 1024, 200, "gemv_reg_kernel<2, 1, 4, 4>"),
     (17, 4096, 4100, "gemv_reg_kernel<2, 2, 4, 4>"),
-    (48, 8192, 1000, "gemv_reg_kernel<3, 1, 4, 4>"),
+    (48, 4096, 1000, "gemv_reg_kernel<3, 1, 4, 4>"),
     (33, 2048, 6000, "gemv_reg_kernel<3, 2, 4, 3>"),
-    (64, 14336, 4096, "gemv_reg_kernel<4, 1, 4, 4>"),
+    (64, 4096, 4096, "gemv_reg_kernel<4, 1, 4, 4>"),
     (60, 4096, 6144, "gemv_reg_kernel<4, 2, 4, 3>"),
     (20, 256, 16400, "gemv_dma_kernel<2, 6>"),
     (40, 512, 16390, "gemv_dma_kernel<3, 5>"),
     (64, 384, 16384, "gemv_dma_kernel<4, 5>"),
+    (64, 14336, 4096, "gemv_shared_kernel<4, 6>"),
+    (48, 8192, 1000, "gemv_shared_kernel<3, 6>"),
+    (17, 8192, 100, "gemv_shared_kernel<2, 8>"),
+    (30, 8320, 300, "gemv_shared_kernel<2, 8>"),
     (3, 272, 64, "gemv_i8_kernel<1, 2, 4, 8>"),
     (64, 4112, 200, "gemv_i8_kernel<4, 2, 4, 8>"),
 ]
@@ -157,15 +161,31 @@ def test_decode_paths(M, K, N, kernel):
     _run(d, W.AZP_PER_TOKEN, bias=True)
 
 
+@pytest.mark.parametrize("M,K,N", [(64, 14336, 4096), (48, 8192, 1000)])
+def test_decode_split_without_workspace(M, K, N):
+    """Without a workspace (or with one too small) a split shape runs unsplit,
+    with the same exact result."""
+    d = _inputs(M, K, N, seed=40)
+    xq, w, sx, sw = to_dev(d["xq"]), to_dev(d["w"]), to_dev(d["sx"]), to_dev(d["sw"])
+    ref = O.int_gemm(d["xq"], d["w"]).astype(np.int32)
+    small = torch.empty(W.scaled_mm_workspace_size(M, N, K) - 16, dtype=torch.uint8, device="cuda:0")
+    for ws in (False, small):
+        got = W.scaled_mm_int8(xq, w, sx, sw, out_dtype=W.OUT_I32, workspace=ws)
+        torch.cuda.synchronize()
+        assert_equal(host(got), ref, "unsplit int32")
+
+
 def test_decode_shape_sequence():
-    """The decode shapes back to back, twice: exact every time (no state is
-    carried from one call to the next)."""
+    """The decode shapes back to back, twice, the split ones sharing one
+    workspace: exact every time (no state is carried between calls)."""
+    ws = torch.empty(max(W.scaled_mm_workspace_size(M, N, K) for (M, K, N, _) in DECODE_CASES),
+                     dtype=torch.uint8, device="cuda:0")
     for rep in range(2):
         for i, (M, K, N, _) in enumerate(DECODE_CASES):
             d = _inputs(M, K, N, seed=10 + i)
             note(f"decode sequence rep={rep} M={M} K={K} N={N}")
             got = W.scaled_mm_int8(to_dev(d["xq"]), to_dev(d["w"]), to_dev(d["sx"]), to_dev(d["sw"]),
-                                   out_dtype=W.OUT_I32)
+                                   out_dtype=W.OUT_I32, workspace=ws)
             torch.cuda.synchronize()
             assert_equal(host(got), O.int_gemm(d["xq"], d["w"]).astype(np.int32), "decode int32")
 
