@@ -14,6 +14,7 @@
 
 #include "device_common.h"
 #include "launch.h"
+#include "rounding.h"
 
 namespace w8a8 {
 
@@ -117,29 +118,29 @@ __device__ __forceinline__ bool legal_block_scale(float s) {
   return s >= 0.0f && s <= 3.402823466e38f;  // NaN, +-Inf and negatives fail; -0 passes
 }
 
-// One chunk = 16 codes of one row. Decodes and scales them into w32[16].
+// One chunk = 16 codes of one row, decoded by gfx950's v_cvt_pk_f32_fp8 (OCP
+// E4M3FN; equal to e4m3_decode on all 254 non-NaN codes, NaN for the two NaN
+// codes, whose rows are flagged) and multiplied by the block scale.
+typedef float f32x2_fp8 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void decode16(uint4 v, float scale, float* w32) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) w32[i * 4 + b] = e4m3_decode((w[i] >> (8 * b)) & 0xFFu) * scale;
+  for (int i = 0; i < 4; ++i) {
+    const f32x2_fp8 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);  // bytes 0, 1
+    const f32x2_fp8 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);   // bytes 2, 3
+    w32[4 * i] = lo.x * scale;
+    w32[4 * i + 1] = lo.y * scale;
+    w32[4 * i + 2] = hi.x * scale;
+    w32[4 * i + 3] = hi.y * scale;
+  }
 }
 
-__device__ __forceinline__ uint4 encode16(const float* w32, float s) {
-  uint32_t o[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int q[4];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      float r = rne(w32[i * 4 + b] / s);
-      r = fminf(fmaxf(r, -127.0f), 127.0f);  // NaN (flagged rows only) -> -127
-      q[b] = (int)r;
-    }
-    o[i] = pack4(q[0], q[1], q[2], q[3]);
-  }
-  return make_uint4(o[0], o[1], o[2], o[3]);
+// Codes clamp(rint(fl(w32 / s)), -127, 127) of one chunk (rounding.h).
+__device__ __forceinline__ uint4 encode16(const float* w32, const RowParams& p) {
+  uint32_t m[16];
+  round_quotients<16, 127>(w32, p, m);
+  return make_uint4(low_bytes4(m[0], m[1], m[2], m[3]), low_bytes4(m[4], m[5], m[6], m[7]),
+                    low_bytes4(m[8], m[9], m[10], m[11]), low_bytes4(m[12], m[13], m[14], m[15]));
 }
 
 // Flags of one row, computed after its absmax: a NaN code, an illegal scale
@@ -151,9 +152,9 @@ struct RowCtx {
   int64_t K;
 };
 
-__device__ int row_flags_slow(RowCtx r, int lane) {
+__device__ int row_flags_slow(RowCtx r, int lane, int stride) {
   int f = 0;
-  for (int64_t j = lane; j < (r.K >> 4); j += 64) {
+  for (int64_t j = lane; j < (r.K >> 4); j += stride) {
     const uint4 v = ld16(r.codes + j * 16);
     const float sc = r.srow[(j * 16) >> 7];
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -168,16 +169,31 @@ __device__ int row_flags_slow(RowCtx r, int lane) {
   return f;
 }
 
-// CH = 16-code chunks per lane kept in registers; rows with K <= CH*1024.
-template <int CH>
+// Reductions over the LPR lanes of one row (a whole wave, or half of one).
+template <int LPR>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+  for (int o = LPR / 2; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+template <int LPR>
+__device__ __forceinline__ int group_or(int v) {
+#pragma unroll
+  for (int o = LPR / 2; o >= 1; o >>= 1) v |= __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// LPR lanes own one row (64, or 32 when that packs the row's chunks tighter);
+// CH = 16-code chunks per lane kept in registers; rows with K <= CH*LPR*16.
+template <int CH, int LPR>
 __global__ __launch_bounds__(256) void fp8_rows_kernel(const uint8_t* __restrict__ W8,
                                                        const float* __restrict__ S, int64_t E,
                                                        int64_t N, int64_t K, int8_t* __restrict__ Wq,
                                                        float* __restrict__ s_out,
                                                        int32_t* __restrict__ err_flag) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // over E*N rows
-  if (row >= E * N) return;
+  const int lane = threadIdx.x % LPR;
+  const int64_t row = (int64_t)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;  // over E*N rows
+  if (row >= E * N) return;  // a whole row group leaves: the reductions stay inside groups
   const int64_t e = row / N, i = row - e * N;
   const int64_t nb = (N + 127) >> 7, kb = (K + 127) >> 7;
   const float* srow = S + (e * nb + (i >> 7)) * kb;
@@ -188,7 +204,7 @@ __global__ __launch_bounds__(256) void fp8_rows_kernel(const uint8_t* __restrict
   float amax = 0.0f;
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
-    const int64_t j = (int64_t)c * 64 + lane;
+    const int64_t j = (int64_t)c * LPR + lane;
     if (j < nchunk) {
       const uint4 v = ld16(codes + j * 16);
       const float sc = srow[(j * 16) >> 7];
@@ -202,16 +218,17 @@ __global__ __launch_bounds__(256) void fp8_rows_kernel(const uint8_t* __restrict
       for (int b = 0; b < 16; ++b) w32[c][b] = 0.0f;
     }
   }
-  amax = wave_max(amax);
-  const int any_nan = wave_or((int)nan_code), any_bad = wave_or((int)bad_scale);
+  amax = group_max<LPR>(amax);
+  const int any_nan = group_or<LPR>((int)nan_code), any_bad = group_or<LPR>((int)bad_scale);
   int flags = (any_nan ? 1 : 0) | (any_bad ? 2 : 0);
-  if (!(amax <= 3.402823466e38f)) flags |= wave_or(row_flags_slow(RowCtx{codes, srow, K}, lane));
+  if (!(amax <= 3.402823466e38f)) flags |= group_or<LPR>(row_flags_slow(RowCtx{codes, srow, K}, lane, LPR));
   const float s = (amax == 0.0f) ? 1.0f : amax / 127.0f;
+  const RowParams rp = finish_params(s, 0);
   int8_t* orow = Wq + row * K;
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
-    const int64_t j = (int64_t)c * 64 + lane;
-    if (j < nchunk) st16(orow + j * 16, encode16(w32[c], s));
+    const int64_t j = (int64_t)c * LPR + lane;
+    if (j < nchunk) st16(orow + j * 16, encode16(w32[c], rp));
   }
   if (lane == 0) {
     s_out[row] = s;
@@ -248,12 +265,13 @@ __global__ __launch_bounds__(256) void fp8_rows_loop_kernel(const uint8_t* __res
   amax = wave_max(amax);
   const int any_nan = wave_or((int)nan_code), any_bad = wave_or((int)bad_scale);
   int flags = (any_nan ? 1 : 0) | (any_bad ? 2 : 0);
-  if (!(amax <= 3.402823466e38f)) flags |= wave_or(row_flags_slow(RowCtx{codes, srow, K}, lane));
+  if (!(amax <= 3.402823466e38f)) flags |= wave_or(row_flags_slow(RowCtx{codes, srow, K}, lane, 64));
   const float s = (amax == 0.0f) ? 1.0f : amax / 127.0f;
+  const RowParams rp = finish_params(s, 0);
   int8_t* orow = Wq + row * K;
   for (int64_t j = lane; j < nchunk; j += 64) {
     decode16(ld16(codes + j * 16), srow[(j * 16) >> 7], w32);
-    st16(orow + j * 16, encode16(w32, s));
+    st16(orow + j * 16, encode16(w32, rp));
   }
   if (lane == 0) {
     s_out[row] = s;
@@ -265,19 +283,34 @@ hipError_t launch_fp8_block_to_int8(const uint8_t* W8, const float* S, int64_t E
                                     int64_t K, int8_t* Wq, float* s, int32_t* err_flag,
                                     hipStream_t stream) {
   const int64_t rows = E * N;
-  const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
-  const int64_t per_lane = ((K >> 4) + 63) / 64;
-  if (per_lane <= 1)
-    hipLaunchKernelGGL(fp8_rows_kernel<1>, grid, block, 0, stream, W8, S, E, N, K, Wq, s, err_flag);
-  else if (per_lane <= 2)
-    hipLaunchKernelGGL(fp8_rows_kernel<2>, grid, block, 0, stream, W8, S, E, N, K, Wq, s, err_flag);
-  else if (per_lane <= 3)
-    hipLaunchKernelGGL(fp8_rows_kernel<3>, grid, block, 0, stream, W8, S, E, N, K, Wq, s, err_flag);
-  else if (per_lane <= 4)
-    hipLaunchKernelGGL(fp8_rows_kernel<4>, grid, block, 0, stream, W8, S, E, N, K, Wq, s, err_flag);
-  else
-    hipLaunchKernelGGL(fp8_rows_loop_kernel, grid, block, 0, stream, W8, S, E, N, K, Wq, s,
-                       err_flag);
+  const int64_t nchunk = K >> 4;
+  const int64_t ch64 = (nchunk + 63) / 64, ch32 = (nchunk + 31) / 32;
+  // 32 lanes per row when that wastes fewer chunk slots (e.g. K = 1536: 96
+  // chunks fill 3 x 32 exactly, but only 96 of 2 x 64)
+  const bool half = ch32 <= 4 && 32 * ch32 < 64 * ch64;
+  const dim3 block(256);
+#define W8A8_FP8(CHV, LPRV)                                                                         \
+  hipLaunchKernelGGL((fp8_rows_kernel<CHV, LPRV>), dim3((unsigned)((rows + 256 / LPRV - 1) / (256 / LPRV))), \
+                     block, 0, stream, W8, S, E, N, K, Wq, s, err_flag)
+  if (half) {
+    switch (ch32) {
+      case 1: W8A8_FP8(1, 32); break;
+      case 2: W8A8_FP8(2, 32); break;
+      case 3: W8A8_FP8(3, 32); break;
+      default: W8A8_FP8(4, 32); break;
+    }
+  } else if (ch64 <= 4) {
+    switch (ch64) {
+      case 1: W8A8_FP8(1, 64); break;
+      case 2: W8A8_FP8(2, 64); break;
+      case 3: W8A8_FP8(3, 64); break;
+      default: W8A8_FP8(4, 64); break;
+    }
+  } else {
+    hipLaunchKernelGGL(fp8_rows_loop_kernel, dim3((unsigned)((rows + 3) / 4)), block, 0, stream, W8, S, E, N,
+                       K, Wq, s, err_flag);
+  }
+#undef W8A8_FP8
   return hipGetLastError();
 }
 

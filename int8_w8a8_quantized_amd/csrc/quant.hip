@@ -19,61 +19,22 @@
 // per thread) to cut latency; large batches use narrow rows and many waves.
 //
 // Exactness: the absmax / min / max are exact, the scale is one IEEE binary32
-// division, and each code is rint(fl(x / s)) with round-half-to-even. The
-// per-element division is replaced by t = fl(x * r) with r = fl(1 / s), which
-// is provably enough except near a rounding boundary: |t - fl(x/s)| <
-// |t| * 2^-22 whenever 1/s is a normal number (two roundings of relative
-// size 2^-24 in t, one in fl(x/s)). t is clamped to the mode's range L first
-// (127, or 512 before an asymmetric zero point; the bounds are integers, so
-// clamping and rounding commute, and a clamped t saturates either way), so
-// if t is farther than L * 2^-22 from every half-integer both round to the
-// same integer. t is rounded by adding 1.5 * 2^23, which leaves rint(t) in
-// the low mantissa bits (two's complement in the low byte). Chunks with an
-// element near a half-integer, and rows whose scale is outside
-// (2^-100, 2^100), take the true division.
+// division, and each code is rint(fl(x / s)) with round-half-to-even, computed
+// by the exact multiplication of rounding.h (about 8 VALU operations per
+// element; the true division only near a half-integer).
 
 #include "device_common.h"
 #include "launch.h"
+#include "rounding.h"
 
 namespace w8a8 {
 
 enum { kDynSym = 0, kDynAsym = 1, kStaticSym = 2, kStaticAsym = 3 };
 
-struct RowParams {
-  float s;     // scale
-  float r;     // fl(1/s)
-  int zp;      // zero point (0 for symmetric modes)
-  bool fast;   // 1/s is comfortably normal: the multiply-and-check path applies
-};
-
-__device__ __forceinline__ RowParams finish_params(float s, int zp) {
-  RowParams p;
-  p.s = s;
-  p.zp = zp;
-  p.fast = s > 0x1p-100f && s < 0x1p100f;
-  p.r = 1.0f / s;
-  return p;
-}
-
-// Adding kMagic = 1.5 * 2^23 to a float of magnitude <= 2^22 rounds it to an
-// integer (ties to even) and leaves that integer + 0x400000 in the mantissa.
-constexpr float kMagic = 12582912.0f;
-constexpr uint32_t kMagicBits = 0x4B400000u;
-
-// Low bytes of four words packed into one (v_perm_b32).
-__device__ __forceinline__ uint32_t low_bytes4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-  const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0c0c0400u);
-  const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x0c0c0400u);
-  return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
-}
-
 // Codes of one 16-byte chunk (8 bf16) as 8 bytes.
 template <int MODE>
 __device__ __forceinline__ uint2 codes8(uint4 v, const RowParams& p) {
   constexpr bool kSym = MODE == kDynSym || MODE == kStaticSym;
-  constexpr float kLim = kSym ? 127.0f : 512.0f;  // range of rint(x/s) before the zero point
-  // |t| <= kLim after the clamp, so t and fl(x/s) differ by less than kLim * 2^-22
-  constexpr float kTie = 0.5f - kLim * 0x1p-22f;
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
   float xs[8];
   uint32_t m[8];
@@ -82,19 +43,8 @@ __device__ __forceinline__ uint2 codes8(uint4 v, const RowParams& p) {
     xs[2 * i] = bf16_lo(w[i]);
     xs[2 * i + 1] = bf16_hi(w[i]);
   }
-  bool fix = !p.fast;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float t = fminf(fmaxf(xs[e] * p.r, -kLim), kLim);
-    const float r = t + kMagic;
-    fix |= fabsf(t - (r - kMagic)) >= kTie;
-    m[e] = __float_as_uint(r);
-  }
-  if (__builtin_expect(fix, 0)) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      m[e] = __float_as_uint(fminf(fmaxf(rne(xs[e] / p.s), -kLim), kLim) + kMagic);
-  }
+  // range of rint(x/s): the int8 codes, or +-512 before an asymmetric zero point
+  round_quotients<8, kSym ? 127 : 512>(xs, p, m);
   if (!kSym) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) m[e] = (uint32_t)clampi((int)(m[e] - kMagicBits) + p.zp, -128, 127);
