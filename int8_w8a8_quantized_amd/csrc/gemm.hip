@@ -36,8 +36,8 @@
 // id is first remapped to give each XCD a contiguous range of tiles, which
 // are then walked in groups of 8 tile-rows so that the workgroups running
 // together on one XCD share A and B tiles in its L2. The grouped variant maps
-// each workgroup to (expert, m-tile of that expert's row range, n-tile) by
-// scanning expert_offsets; rows may be gathered through row_ids.
+// each workgroup to (expert, n-tile, m-tile of that expert's row range), m
+// fastest, by scanning expert_offsets; rows may be gathered through row_ids.
 
 #include <type_traits>
 
@@ -68,25 +68,54 @@ __device__ __forceinline__ TileLoc locate_tile(const GemmArgs& a, int tiles_m, i
   TileLoc t;
   const int pid = xcd_remap(blockIdx.x, gridDim.x);
   if (GROUPED) {
-    const int mt = pid / tiles_n;
-    t.n_begin = (int64_t)(pid % tiles_n) * BN;
+    // expert by expert; within an expert, n-tile by n-tile with its m-tiles
+    // consecutive, so the workgroups that share a weight tile run together on
+    // one XCD and read it from its L2 (an expert's whole weight exceeds it).
+    // Every wave scans the experts 64 at a time, one per lane: the clamped
+    // segment starts are a running max of the offsets (capped at T), each
+    // expert's tile count a running sum, and the expert holding tile `pid` is
+    // the lowest lane whose running range contains it.
+    t.n_begin = 0;
     t.expert = -1;
     t.row_begin = t.row_end = 0;
     const int64_t T = a.M;
-    int64_t cum = 0, prev = 0;
-    for (int64_t e = 0; e < a.E; ++e) {
-      int64_t s0 = a.expert_offsets[e], s1 = a.expert_offsets[e + 1];
-      s0 = min(max(s0, prev), T);
-      s1 = min(max(s1, s0), T);
-      prev = s0;
-      const int64_t t_e = (s1 - s0 + BM - 1) / BM;
-      if (mt < cum + t_e) {
-        t.expert = e;
-        t.row_begin = s0 + (int64_t)(mt - cum) * BM;
-        t.row_end = s1;
+    const int lane = threadIdx.x & 63;
+    int64_t carry_s0 = 0, carry_cum = 0;
+    for (int64_t base = 0; base < a.E; base += 64) {
+      const int64_t e = base + lane;
+      const bool live = e < a.E;
+      int64_t s0 = live ? (int64_t)a.expert_offsets[e] : T;
+      const int64_t raw1 = live ? (int64_t)a.expert_offsets[e + 1] : T;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int64_t v = __shfl_up(s0, o, 64);
+        if (lane >= o) s0 = max(s0, v);
+      }
+      s0 = min(max(s0, carry_s0), T);
+      const int64_t s1 = min(max(raw1, s0), T);
+      const int64_t span = live ? ((s1 - s0 + BM - 1) / BM) * tiles_n : 0;
+      int64_t cum = span;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int64_t v = __shfl_up(cum, o, 64);
+        if (lane >= o) cum += v;
+      }
+      cum += carry_cum;
+      const uint64_t hit = __ballot(live && pid >= cum - span && pid < cum);
+      if (hit) {
+        const int src = __builtin_ctzll(hit);
+        const int64_t e_s0 = __shfl(s0, src, 64), e_s1 = __shfl(s1, src, 64);
+        const int64_t e_first = __shfl(cum - span, src, 64);
+        const int64_t t_e = (e_s1 - e_s0 + BM - 1) / BM;
+        const int64_t local = pid - e_first;
+        t.expert = base + src;
+        t.row_begin = e_s0 + (local % t_e) * BM;
+        t.row_end = e_s1;
+        t.n_begin = (local / t_e) * BN;
         break;
       }
-      cum += t_e;
+      carry_s0 = __shfl(s0, 63, 64);
+      carry_cum = __shfl(cum, 63, 64);
     }
   } else {
     constexpr int GM = 8;
@@ -170,7 +199,12 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const TileLoc& 
     row_sx[r] = a.sx_per_token ? a.s_x[s0] : a.s_x[0];
     row_zp[r] = (a.azp_mode == 1) ? a.zp[s0] : 0;
   }
+  // the row parameters are visible to every wave; no wait for global stores
+  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
+  // Each wave owns its slab and a wave's LDS accesses execute in order, so the
+  // slab's writes, its row-contiguous reads and the next slab's writes need no
+  // barrier, and the output stores of one slab overlap the next.
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -178,7 +212,6 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const TileLoc& 
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         slab[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * CSTRIDE + j * 32 + frag_row] = acc[i][j][r];
-    __syncthreads();
 #pragma unroll 4
     for (int p = 0; p < 32 / ROWS_PER_PASS; ++p) {
       const int lr = p * ROWS_PER_PASS + lrow;
@@ -226,7 +259,6 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const TileLoc& 
         }
       }
     }
-    __syncthreads();
   }
 }
 
