@@ -67,13 +67,18 @@ def fp8_convert_bytes(E, N, K):
     return 2 * E * N * K + 4 * E * (-(-N // 128)) * (-(-K // 128)) + 4 * E * N
 
 
+# Sources the decode kernels are compiled from (the kernels whose HBM traffic
+# profiles/traffic.json records).
+DECODE_SOURCES = ("gemv.hip", "gemm_common.h", "device_common.h", "launch.h")
+
+
 def kernel_source_hash():
-    """sha256 over the HIP library sources, to tell whether recorded counters
-    were taken on the kernels being run."""
+    """sha256 over the decode kernels' sources, to tell whether recorded
+    counters were taken on the kernels being run."""
     import hashlib
     csrc = os.path.join(ROOT, "int8_w8a8_quantized_amd", "csrc")
     h = hashlib.sha256()
-    for name in sorted(os.listdir(csrc)):
+    for name in DECODE_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
@@ -141,8 +146,8 @@ def capture(torch, fn):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
-              "(the layer would shard by output columns across GPUs; see DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(across GPUs the layer would shard by output columns)", file=sys.stderr)
         return 2
 
     import numpy as np

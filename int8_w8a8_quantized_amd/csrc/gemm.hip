@@ -166,6 +166,7 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const TileLoc& 
   constexpr int CSTRIDE = TN + 8;  // int32 words; rows 4 apart land 32 banks apart
   constexpr int LANES_PER_ROW = TN / 4;
   constexpr int ROWS_PER_PASS = 64 / LANES_PER_ROW;
+  static_assert(32 % ROWS_PER_PASS == 0, "passes cover the slab");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int frag_row = lane & 31;
@@ -214,6 +215,7 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const TileLoc& 
         slab[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * CSTRIDE + j * 32 + frag_row] = acc[i][j][r];
 #pragma unroll 4
     for (int p = 0; p < 32 / ROWS_PER_PASS; ++p) {
+      if (lrow >= ROWS_PER_PASS) continue;  // lanes past whole rows (TN = 96) sit out
       const int lr = p * ROWS_PER_PASS + lrow;
       const int4 v = *reinterpret_cast<const int4*>(slab + lr * CSTRIDE + c4);
       const int tr = wm * TM + i * 32 + lr;  // row within the tile
@@ -551,17 +553,18 @@ struct TileCfg {
 };
 
 // Tile menu: 256 x 256 (each LDS fragment feeds 4 MFMAs) when the problem has
-// enough tiles to fill the 256 compute units, 256 x 128 / 128 x 128 when the
-// big tile would leave much of the chip idle. Estimated cost = rounds of
-// workgroups over the CUs x tile area / measured relative throughput per
-// unit of tile area (1.0, 0.81, 0.72 for the three sizes on 8192 x 4096 x
-// 4096 with BK = 128).
+// enough tiles to fill the 256 compute units, 256 x 192 / 256 x 128 /
+// 128 x 128 when the big tile would leave much of the chip idle (2048 x 6144
+// makes 192 tiles of 256 x 256 but exactly 256 of 256 x 192). Estimated cost
+// = rounds of workgroups over the CUs x tile area / measured relative
+// throughput per unit of tile area (1.0, 0.82, 0.81, 0.72 for the four sizes
+// on 8192 x 4096 x 4096 with BK = 128).
 TileCfg pick_tile(int64_t M, int64_t N) {
-  const TileCfg menu[3] = {{256, 256}, {256, 128}, {128, 128}};
-  const double eff[3] = {1.0, 0.81, 0.72};
+  const TileCfg menu[4] = {{256, 256}, {256, 192}, {256, 128}, {128, 128}};
+  const double eff[4] = {1.0, 0.82, 0.81, 0.72};
   int best = 0;
   double best_cost = 0;
-  for (int c = 0; c < 3; ++c) {
+  for (int c = 0; c < 4; ++c) {
     const int64_t tiles = ((M + menu[c].bm - 1) / menu[c].bm) * ((N + menu[c].bn - 1) / menu[c].bn);
     const int64_t rounds = (tiles + 255) / 256;
     const double cost = (double)rounds * menu[c].bm * menu[c].bn / eff[c];
@@ -585,7 +588,7 @@ constexpr int stages128() {
   constexpr int kLds = 160 * 1024;
   return (BM + BN) * 128 * 4 <= kLds ? 4 : ((BM + BN) * 128 * 3 <= kLds ? 3 : 2);
 }
-static_assert(stages128<256, 256>() == 2 && stages128<256, 128>() == 3 &&
+static_assert(stages128<256, 256>() == 2 && stages128<256, 192>() == 2 && stages128<256, 128>() == 3 &&
                   stages128<128, 128>() == 4,
               "stage counts the kernel names below state");
 
@@ -611,20 +614,20 @@ hipError_t launch_tiles(const GemmArgs& a, int64_t extra_m_tiles, hipStream_t st
 }
 
 const char* kernel_name(int bm, int bn, bool grouped, int64_t K) {
-  static const char* names[3][2][3] = {
-      {{"gemm_i8_dma_kernel<256, 256, 128, 2, false>", "gemm_i8_dma_kernel<256, 128, 128, 3, false>",
-        "gemm_i8_dma_kernel<128, 128, 128, 4, false>"},
-       {"gemm_i8_dma_kernel<256, 256, 128, 2, true>", "gemm_i8_dma_kernel<256, 128, 128, 3, true>",
-        "gemm_i8_dma_kernel<128, 128, 128, 4, true>"}},
-      {{"gemm_i8_dma_kernel<256, 256, 64, 4, false>", "gemm_i8_dma_kernel<256, 128, 64, 4, false>",
-        "gemm_i8_dma_kernel<128, 128, 64, 4, false>"},
-       {"gemm_i8_dma_kernel<256, 256, 64, 4, true>", "gemm_i8_dma_kernel<256, 128, 64, 4, true>",
-        "gemm_i8_dma_kernel<128, 128, 64, 4, true>"}},
-      {{"gemm_i8_kernel<256, 256, false>", "gemm_i8_kernel<256, 128, false>",
+  static const char* names[3][2][4] = {
+      {{"gemm_i8_dma_kernel<256, 256, 128, 2, false>", "gemm_i8_dma_kernel<256, 192, 128, 2, false>",
+        "gemm_i8_dma_kernel<256, 128, 128, 3, false>", "gemm_i8_dma_kernel<128, 128, 128, 4, false>"},
+       {"gemm_i8_dma_kernel<256, 256, 128, 2, true>", "gemm_i8_dma_kernel<256, 192, 128, 2, true>",
+        "gemm_i8_dma_kernel<256, 128, 128, 3, true>", "gemm_i8_dma_kernel<128, 128, 128, 4, true>"}},
+      {{"gemm_i8_dma_kernel<256, 256, 64, 4, false>", "gemm_i8_dma_kernel<256, 192, 64, 4, false>",
+        "gemm_i8_dma_kernel<256, 128, 64, 4, false>", "gemm_i8_dma_kernel<128, 128, 64, 4, false>"},
+       {"gemm_i8_dma_kernel<256, 256, 64, 4, true>", "gemm_i8_dma_kernel<256, 192, 64, 4, true>",
+        "gemm_i8_dma_kernel<256, 128, 64, 4, true>", "gemm_i8_dma_kernel<128, 128, 64, 4, true>"}},
+      {{"gemm_i8_kernel<256, 256, false>", "gemm_i8_kernel<256, 192, false>", "gemm_i8_kernel<256, 128, false>",
         "gemm_i8_kernel<128, 128, false>"},
-       {"gemm_i8_kernel<256, 256, true>", "gemm_i8_kernel<256, 128, true>",
+       {"gemm_i8_kernel<256, 256, true>", "gemm_i8_kernel<256, 192, true>", "gemm_i8_kernel<256, 128, true>",
         "gemm_i8_kernel<128, 128, true>"}}};
-  const int c = (bm == 256 && bn == 256) ? 0 : (bm == 256 ? 1 : 2);
+  const int c = bm == 128 ? 3 : (bn == 256 ? 0 : (bn == 192 ? 1 : 2));
   return names[pick_k(K)][grouped][c];
 }
 
@@ -633,6 +636,7 @@ const char* kernel_name(int bm, int bn, bool grouped, int64_t K) {
 hipError_t launch_scaled_mm(const GemmArgs& a, hipStream_t stream) {
   const TileCfg t = pick_tile(a.M, a.N);
   if (t.bm == 256 && t.bn == 256) return launch_tiles<256, 256, false>(a, 0, stream);
+  if (t.bm == 256 && t.bn == 192) return launch_tiles<256, 192, false>(a, 0, stream);
   if (t.bm == 256) return launch_tiles<256, 128, false>(a, 0, stream);
   return launch_tiles<128, 128, false>(a, 0, stream);
 }

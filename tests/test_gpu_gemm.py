@@ -194,9 +194,12 @@ def test_decode_shape_sequence():
 # selects the 128-byte, the 64-byte or the zero-filled register-staged K loop.
 # The shapes are chosen so that the tile-size heuristic lands on each tile.
 PATH_CASES = [
-    (2300, 640, 4600, "gemm_i8_dma_kernel<256, 256, 128, 2, false>"),
-    (2300, 576, 4600, "gemm_i8_dma_kernel<256, 256, 64, 4, false>"),
-    (2300, 592, 4600, "gemm_i8_kernel<256, 256, false>"),
+    (2300, 640, 6100, "gemm_i8_dma_kernel<256, 256, 128, 2, false>"),
+    (2300, 576, 6100, "gemm_i8_dma_kernel<256, 256, 64, 4, false>"),
+    (2300, 592, 6100, "gemm_i8_kernel<256, 256, false>"),
+    (1800, 256, 5900, "gemm_i8_dma_kernel<256, 192, 128, 2, false>"),
+    (1800, 320, 5900, "gemm_i8_dma_kernel<256, 192, 64, 4, false>"),
+    (1800, 272, 5900, "gemm_i8_kernel<256, 192, false>"),
     (2100, 384, 2100, "gemm_i8_dma_kernel<256, 128, 128, 3, false>"),
     (2100, 320, 2100, "gemm_i8_dma_kernel<256, 128, 64, 4, false>"),
     (2100, 336, 2100, "gemm_i8_kernel<256, 128, false>"),
