@@ -18,7 +18,7 @@ partial sum stays below 2**53). The one floating-point *output*, the
 dequantised bf16 result, is computed in float64 from the exact integer
 accumulator and then rounded once to bf16 (round-to-nearest-even).
 
-Readings of points the pages leave open (each is also listed in the design doc):
+Readings of points the pages leave open:
 
 * ``round`` is round-half-to-even (numpy ``rint``); the division by a scale is a
   true IEEE division, never a multiply by a reciprocal.
