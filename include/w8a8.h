@@ -201,6 +201,9 @@ size_t w8a8_scaled_mm_workspace_size(int64_t M, int64_t N, int64_t K);
  * s_w float [N] if s_w_per_channel else [1]; zp int32 [M] and colsum int32 [N]
  * (PER_TOKEN), or azp_adj int32 [N] (STATIC) -- pass it as `colsum`;
  * bias bf16 [N] or NULL; out bf16 or int32 [M,N] (ldo).
+ * PER_TOKEN expects int8 zero points (zp in [-128, 127], as w8a8_quantize_act
+ * writes them) and column sums of the int8 weight (|colsum| <= 2^23, which
+ * every K <= W8A8_MAX_K gives); the result is unspecified outside that range.
  * workspace: device memory, 16-byte aligned, see w8a8_scaled_mm_workspace_size.
  * Requires K % 16 == 0, 1 <= K <= W8A8_MAX_K, xq/Wq/out 16-byte aligned,
  * ldx % 16 == 0, ldw % 16 == 0, ld* >= the row length. */

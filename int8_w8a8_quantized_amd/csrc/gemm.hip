@@ -144,64 +144,111 @@ __device__ __forceinline__ int64_t source_row(const GemmArgs& a, int64_t gr) {
   return gr;
 }
 
-// The fused epilogue, one 32-row slab of the wave's sub-tile at a time: the
-// slab's accumulators go to LDS in MFMA layout (lane = column), come back
-// row-contiguous (4 consecutive columns per lane), get the zero-point
-// correction, scales and bias, and leave as 8-byte bf16 (or 16-byte int32)
-// stores that cover whole row segments. The tile's per-row parameters
-// (source row, token scale, zero point) are fetched once into LDS first, so
-// the row passes wait on no global load. `smem` must hold
-// epilogue_lds_bytes<BM, BN>() bytes and be free: the caller has passed a
-// barrier after its last read.
+// The fused epilogue. Its operands are fetched when the workgroup starts
+// (epilogue_fetch: thread r takes tile row r and tile column r into
+// registers, so the loads' latency hides under the main loop) and published
+// to two LDS tables once the main loop is done: per row {all-zero mask,
+// token scale, minus the zero point}, per column {weight scale, column sum,
+// static correction, bias}. Each wave then turns its sub-tile around one
+// 32-row slab at a time: the accumulators go to LDS in MFMA layout (lane =
+// column) and come back row-contiguous, each lane taking 8 columns of a row
+// (two groups of 4, half the sub-tile apart, so 16 consecutive lanes read
+// one contiguous row segment and store whole 128-byte lines).
+//
+// With one wave per SIMD every VALU instruction costs the wave its full
+// issue time, so the per-element work is kept to full-rate instructions:
+// the zero-point product uses the 24-bit multiply-add, exact here because a
+// zero point fits in 9 bits and a column sum of int8 rows with K <= 65536
+// in 24 (|colsum| <= 128 K <= 2^23); row addresses are one per-lane base
+// plus a wave-uniform offset. `smem` must hold epilogue_lds_bytes<BM, BN>()
+// bytes and be free: the caller has passed a barrier after its last read and
+// its last LDS load.
 template <int BM, int BN>
 constexpr int epilogue_lds_bytes() {
-  return 4 * 32 * (BN / 2 + 8) * 4 + BM * 12;
+  return 4 * 32 * (BN / 2 + 8) * 4 + BM * 16 + BN * 16;
 }
 
+struct EpiFetch {
+  int row_mask;    // -1, or 0 for a row that reads as all zeros
+  float row_sx;
+  int row_zp;
+  float col_sw;
+  int col_corr;
+  uint32_t col_bias;  // bf16 bits
+};
+
 template <int BM, int BN, bool GROUPED>
-__device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const TileLoc& t, const float* sw,
-                                              const uint16_t* bias, int8_t* smem,
-                                              i32x16 (&acc)[BM / 64][BN / 64]) {
+__device__ __forceinline__ EpiFetch epilogue_fetch(const GemmArgs& a, const TileLoc& t,
+                                                   const float* sw, const uint16_t* bias) {
+  static_assert(BM <= 256 && BN <= 256, "one row and one column per thread");
+  EpiFetch f;
+  const int r = threadIdx.x;
+  const int64_t gr = t.row_begin + (r < BM ? r : 0);
+  const int64_t src = gr < t.row_end ? source_row<GROUPED>(a, gr) : -1;
+  const int64_t s0 = src > 0 ? src : 0;
+  f.row_mask = src >= 0 ? -1 : 0;
+  f.row_sx = a.s_x[a.sx_per_token ? s0 : 0];
+  // Addresses are selected instead of values (a missing operand reads the
+  // scale, which always exists), so the loads carry no use until the epilogue.
+  f.row_zp = *(a.azp_mode == 1 ? a.zp + s0 : reinterpret_cast<const int32_t*>(a.s_x));
+  const int64_t n = t.n_begin + (r < BN ? r : 0);
+  const int64_t nn = n < a.N ? n : 0;
+  f.col_sw = sw[a.sw_per_channel ? nn : 0];
+  f.col_corr = *(a.azp_mode != 0 ? a.colsum + nn : reinterpret_cast<const int32_t*>(sw));
+  f.col_bias = *(bias ? bias + nn : reinterpret_cast<const uint16_t*>(sw));
+  return f;
+}
+
+// MASKED: rows may read as all zeros (gathered rows). OUT_I32: int32
+// output, else bf16. AZP: 0 none, 1 per-token, 2 static,
+// 3 either (read from the tables). FULL: every row of the tile and every
+// column of the wave's sub-tile is inside the output and ldo allows 8- /
+// 16-byte stores; the passes then carry no predicate, so the compiler is
+// free to run the LDS reads of later passes ahead of earlier stores.
+template <int BM, int BN, bool MASKED, bool OUT_I32, int AZP, bool FULL>
+__device__ __forceinline__ void epilogue_store_tile(const GemmArgs& a, const TileLoc& t, int8_t* smem,
+                                                    i32x16 (&acc)[BM / 64][BN / 64]) {
   constexpr int TM = BM / 2, TN = BN / 2, FM = TM / 32, FN = TN / 32;
   constexpr int CSTRIDE = TN + 8;  // int32 words; rows 4 apart land 32 banks apart
-  constexpr int LANES_PER_ROW = TN / 4;
-  constexpr int ROWS_PER_PASS = 64 / LANES_PER_ROW;
-  static_assert(32 % ROWS_PER_PASS == 0, "passes cover the slab");
+  constexpr int LPR = TN / 8;      // lanes per row
+  constexpr int RPP = 64 / LPR >= 8 ? 8 : 4;  // rows per pass
+  static_assert(LPR * RPP <= 64 && 32 % RPP == 0, "passes cover the slab");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int frag_row = lane & 31;
   int32_t* slab = reinterpret_cast<int32_t*>(smem) + wave * 32 * CSTRIDE;
-  const int c4 = (lane * 4) % TN;  // first of this lane's 4 columns
-  const int lrow = (lane * 4) / TN;  // row of this lane within a pass
-  const int64_t col0 = t.n_begin + wn * TN + c4;
-  float csw[4], cbias[4];
-  int ccorr[4];
-  bool cok[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const EpiCol c = load_col(a, col0 + q, sw, bias);
-    csw[q] = c.sw;
-    cbias[q] = c.bias();
-    ccorr[q] = c.corr;
-    cok[q] = c.ok;
-  }
-  const bool vec_store = cok[3] && (a.ldo % 4 == 0);
+  const int4* row_tab = reinterpret_cast<const int4*>(smem + 4 * 32 * CSTRIDE * 4);
+  const float* col_sw = reinterpret_cast<const float*>(row_tab + BM);
+  const int* col_sum = reinterpret_cast<const int*>(col_sw + BN);
+  const int* col_adj = col_sum + BN;
+  const float* col_bias = reinterpret_cast<const float*>(col_adj + BN);
 
-  // per-row parameters of the tile: source row (-1: all-zero row, or past the
-  // end), token scale, zero point
-  int* row_src = reinterpret_cast<int*>(smem + 4 * 32 * CSTRIDE * 4);
-  float* row_sx = reinterpret_cast<float*>(row_src + BM);
-  int* row_zp = row_src + 2 * BM;
-  for (int r = threadIdx.x; r < BM; r += 256) {
-    const int64_t gr = t.row_begin + r;
-    const int64_t src = gr < t.row_end ? source_row<GROUPED>(a, gr) : -1;
-    const int64_t s0 = src > 0 ? src : 0;
-    row_src[r] = (int)src;
-    row_sx[r] = a.sx_per_token ? a.s_x[s0] : a.s_x[0];
-    row_zp[r] = (a.azp_mode == 1) ? a.zp[s0] : 0;
+  // lanes past whole rows (TN = 96) repeat the first lanes' stores
+  const int lw = lane % (LPR * RPP);
+  const int q = lw % LPR, lrow = lw / LPR;
+  const int cA = 4 * q, cB = TN / 2 + 4 * q;  // the lane's two column groups in the sub-tile
+  float sw8[8], bias8[8];
+  int sum8[8], adj8[8];
+  {
+    const int c0 = wn * TN;
+    auto get4f = [&](const float* p, float* d) __attribute__((always_inline)) {
+      const float4 u = *reinterpret_cast<const float4*>(p + c0 + cA);
+      const float4 v = *reinterpret_cast<const float4*>(p + c0 + cB);
+      d[0] = u.x; d[1] = u.y; d[2] = u.z; d[3] = u.w; d[4] = v.x; d[5] = v.y; d[6] = v.z; d[7] = v.w;
+    };
+    auto get4i = [&](const int* p, int* d) __attribute__((always_inline)) {
+      const int4 u = *reinterpret_cast<const int4*>(p + c0 + cA);
+      const int4 v = *reinterpret_cast<const int4*>(p + c0 + cB);
+      d[0] = u.x; d[1] = u.y; d[2] = u.z; d[3] = u.w; d[4] = v.x; d[5] = v.y; d[6] = v.z; d[7] = v.w;
+    };
+    if (!OUT_I32) get4f(col_sw, sw8), get4f(col_bias, bias8);
+    if (AZP == 1 || AZP == 3) get4i(col_sum, sum8);
+    if (AZP == 2 || AZP == 3) get4i(col_adj, adj8);
   }
-  // the row parameters are visible to every wave; no wait for global stores
-  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  const int64_t col_a = t.n_begin + wn * TN + cA, col_b = col_a + TN / 2;
+  const int lrow0 = wm * TM + lrow;  // the lane's row within the tile, first pass
+  using OutT = typename std::conditional<OUT_I32, int32_t, uint16_t>::type;
+  OutT* const o_lane = reinterpret_cast<OutT*>(a.out) + (t.row_begin + lrow0) * a.ldo + col_a;
 
   // Each wave owns its slab and a wave's LDS accesses execute in order, so the
   // slab's writes, its row-contiguous reads and the next slab's writes need no
@@ -213,54 +260,89 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const TileLoc& 
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         slab[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * CSTRIDE + j * 32 + frag_row] = acc[i][j][r];
-#pragma unroll 4
-    for (int p = 0; p < 32 / ROWS_PER_PASS; ++p) {
-      if (lrow >= ROWS_PER_PASS) continue;  // lanes past whole rows (TN = 96) sit out
-      const int lr = p * ROWS_PER_PASS + lrow;
-      const int4 v = *reinterpret_cast<const int4*>(slab + lr * CSTRIDE + c4);
-      const int tr = wm * TM + i * 32 + lr;  // row within the tile
-      const int64_t gr = t.row_begin + tr;
-      if (gr >= t.row_end) continue;
-      int c[4] = {v.x, v.y, v.z, v.w};
-      if (row_src[tr] < 0) c[0] = c[1] = c[2] = c[3] = 0;
-      if (a.azp_mode == 1) {
-        const int zp = row_zp[tr];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) c[q] -= zp * ccorr[q];
-      } else if (a.azp_mode == 2) {
+    for (int p = 0; p < 32 / RPP; ++p) {
+      const int lr = p * RPP + lrow;
+      const int dr = i * 32 + p * RPP;  // wave-uniform row step from the first pass
+      const int4 vA = *reinterpret_cast<const int4*>(slab + lr * CSTRIDE + cA);
+      const int4 vB = *reinterpret_cast<const int4*>(slab + lr * CSTRIDE + cB);
+      const int4 rp = row_tab[lrow0 + dr];  // {mask, sx, -zp, 0}
+      const int v[8] = {vA.x, vA.y, vA.z, vA.w, vB.x, vB.y, vB.z, vB.w};
+      int c[8];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) c[q] -= ccorr[q];
+      for (int k = 0; k < 8; ++k) {
+        c[k] = MASKED ? v[k] & rp.x : v[k];
+        if (AZP == 1 || AZP == 3) c[k] = __mul24(rp.z, sum8[k]) + c[k];
+        if (AZP == 2 || AZP == 3) c[k] -= adj8[k];
       }
-      if (a.out_i32) {
-        int32_t* o = reinterpret_cast<int32_t*>(a.out) + gr * a.ldo + col0;
-        if (vec_store) {
+      OutT* o = o_lane + (int64_t)dr * a.ldo;
+      const bool row_ok = FULL || t.row_begin + lrow0 + dr < t.row_end;
+      if (OUT_I32) {
+        if (FULL) {
           *reinterpret_cast<int4*>(o) = make_int4(c[0], c[1], c[2], c[3]);
-        } else {
+          *reinterpret_cast<int4*>(o + TN / 2) = make_int4(c[4], c[5], c[6], c[7]);
+        } else if (row_ok) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (cok[q]) o[q] = c[q];
+          for (int k = 0; k < 8; ++k)
+            if ((k < 4 ? col_a : col_b) + (k & 3) < a.N) o[(k < 4 ? 0 : TN / 2) + (k & 3)] = c[k];
         }
       } else {
-        const float sx = row_sx[tr];
-        float y[4];
+        const float sx = __int_as_float(rp.y);
+        uint32_t h[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          y[q] = (float)c[q] * sx * csw[q];
-          if (a.bias) y[q] += cbias[q];
+        for (int k = 0; k < 8; k += 2) {
+          const float y0 = __builtin_fmaf((float)c[k] * sx, sw8[k], bias8[k]);
+          const float y1 = __builtin_fmaf((float)c[k + 1] * sx, sw8[k + 1], bias8[k + 1]);
+          h[k / 2] = pack_bf16x2(y0, y1);
         }
-        const uint32_t h01 = pack_bf16x2(y[0], y[1]), h23 = pack_bf16x2(y[2], y[3]);
-        uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + gr * a.ldo + col0;
-        if (vec_store) {
-          *reinterpret_cast<uint2*>(o) = make_uint2(h01, h23);
-        } else {
-          const uint16_t h[4] = {(uint16_t)h01, (uint16_t)(h01 >> 16), (uint16_t)h23,
-                                 (uint16_t)(h23 >> 16)};
+        if (FULL) {
+          *reinterpret_cast<uint2*>(o) = make_uint2(h[0], h[1]);
+          *reinterpret_cast<uint2*>(o + TN / 2) = make_uint2(h[2], h[3]);
+        } else if (row_ok) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (cok[q]) o[q] = h[q];
+          for (int k = 0; k < 8; ++k)
+            if ((k < 4 ? col_a : col_b) + (k & 3) < a.N)
+              o[(k < 4 ? 0 : TN / 2) + (k & 3)] = (uint16_t)(h[k / 2] >> (16 * (k & 1)));
         }
       }
     }
+  }
+}
+
+template <int BM, int BN, bool GROUPED>
+__device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const TileLoc& t, const EpiFetch& f,
+                                              int8_t* smem, i32x16 (&acc)[BM / 64][BN / 64]) {
+  constexpr int TN = BN / 2;
+  constexpr int CSTRIDE = TN + 8;
+  int4* row_tab = reinterpret_cast<int4*>(smem + 4 * 32 * CSTRIDE * 4);
+  float* col_sw = reinterpret_cast<float*>(row_tab + BM);
+  int* col_sum = reinterpret_cast<int*>(col_sw + BN);
+  int* col_adj = col_sum + BN;
+  float* col_bias = reinterpret_cast<float*>(col_adj + BN);
+  const int r = threadIdx.x;
+  if (r < BM) row_tab[r] = make_int4(f.row_mask, __float_as_int(f.row_sx), a.azp_mode == 1 ? -f.row_zp : 0, 0);
+  if (r < BN) {
+    col_sw[r] = f.col_sw;
+    col_sum[r] = a.azp_mode == 1 ? f.col_corr : 0;
+    col_adj[r] = a.azp_mode == 2 ? f.col_corr : 0;
+    col_bias[r] = a.bias ? __uint_as_float(f.col_bias << 16) : 0.0f;
+  }
+  // the tables are visible to every wave; no wait for global stores
+  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  const int wn = (threadIdx.x >> 6) & 1;
+  // groups of 4 columns leave as 16-byte (int32) or 8-byte (bf16) stores
+  const bool full = t.n_begin + (wn + 1) * TN <= a.N && a.ldo % 4 == 0 && t.row_begin + BM <= t.row_end;
+  if (!full) {
+    if (a.out_i32) epilogue_store_tile<BM, BN, GROUPED, true, 3, false>(a, t, smem, acc);
+    else epilogue_store_tile<BM, BN, GROUPED, false, 3, false>(a, t, smem, acc);
+  } else if (a.out_i32) {
+    if (a.azp_mode == 1) epilogue_store_tile<BM, BN, GROUPED, true, 1, true>(a, t, smem, acc);
+    else if (a.azp_mode == 2) epilogue_store_tile<BM, BN, GROUPED, true, 2, true>(a, t, smem, acc);
+    else epilogue_store_tile<BM, BN, GROUPED, true, 0, true>(a, t, smem, acc);
+  } else {
+    if (a.azp_mode == 1) epilogue_store_tile<BM, BN, GROUPED, false, 1, true>(a, t, smem, acc);
+    else if (a.azp_mode == 2) epilogue_store_tile<BM, BN, GROUPED, false, 2, true>(a, t, smem, acc);
+    else epilogue_store_tile<BM, BN, GROUPED, false, 0, true>(a, t, smem, acc);
   }
 }
 
@@ -298,7 +380,7 @@ __global__ __launch_bounds__(256) void gemm_i8_dma_kernel(GemmArgs a, int tiles_
   constexpr int KS = BK / 32;                 // MFMA k slices per stage
   static_assert(CH == 4 || CH == 8, "BK is 64 or 128");
   static_assert(BM % (4 * RPI) == 0 && BN % (4 * RPI) == 0, "tile / load mismatch");
-  static_assert(NS >= 2 && (NS - 2) * PER_STAGE <= 63, "stages / vmcnt range");
+  static_assert(NS >= 2 && (NS - 1) * PER_STAGE <= 63, "stages / vmcnt range");
   static_assert(epilogue_lds_bytes<BM, BN>() <= NS * STAGE, "epilogue does not fit the LDS");
 
   __shared__ __attribute__((aligned(1024))) int8_t smem[NS * STAGE];
@@ -311,6 +393,8 @@ __global__ __launch_bounds__(256) void gemm_i8_dma_kernel(GemmArgs a, int tiles_
   const int8_t* B = a.B + t.expert * a.N * a.ldb;
   const float* sw = a.s_w + (GROUPED ? t.expert * a.N : 0);
   const uint16_t* bias = (GROUPED && a.bias) ? a.bias + t.expert * a.N : a.bias;
+  // issued before the ring's loads, so the ring's vmcnt waits retire them too
+  const EpiFetch ef = epilogue_fetch<BM, BN, GROUPED>(a, t, sw, bias);
 
   // ---- per-lane DMA sources: instruction q of this wave fills tile rows
   // (wave*AI + q)*RPI .. +RPI-1; lane l writes row +l/CH, physical chunk
@@ -370,63 +454,79 @@ __global__ __launch_bounds__(256) void gemm_i8_dma_kernel(GemmArgs a, int tiles_
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
+  auto mfmas = [&](int slot) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x32(fa[slot][i], fb[slot][j], acc[i][j]);
+  };
+  static_assert(KS % 2 == 0, "the next stage's first slice reuses fragment slot 0");
+  constexpr int NR = FM + FN, NM = FM * FN;
+  static_assert(NM >= NR, "more fragment reads than MFMAs in a slice");
+
+  // The ring's NS stages are all requested up front; the step that finishes
+  // with stage kt requests stage kt + NS into its buffer. Past the last stage
+  // the requests reload it into a retired buffer (same addresses, never
+  // read), which keeps every step one straight-line block.
   const int nk = (int)(a.K / BK);
 #pragma unroll
-  for (int s = 0; s < NS - 1; ++s) issue(min(s, nk - 1), s);
+  for (int s = 0; s < NS; ++s) issue(min(s, nk - 1), s);
+  wait_vmcnt<(NS - 1) * PER_STAGE>();
+  barrier_no_fence();  // every wave's part of stage 0 has landed
+  read_frags(smem, 0, 0);
 
   for (int kt = 0; kt < nk; ++kt) {
-    // This wave's loads of stage kt are done once at most the NS - 2 stages
-    // issued after it remain outstanding (every step issues exactly one
-    // stage, so the count is the same each time).
-    wait_vmcnt<(NS - 2) * PER_STAGE>();
-    barrier_no_fence();  // every wave's part of stage kt has landed; stage kt-1 is retired
     const int8_t* st = smem + (kt % NS) * STAGE;
-    read_frags(st, 0, 0);
+    // All slices but the last: each slice's MFMAs with the next slice's
+    // fragment reads slotted in after the first of them.
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      if (s + 1 < KS) read_frags(st, s + 1, (s + 1) & 1);
-      // The next stage's loads go out among the first slice's MFMAs, after
-      // its fragment reads (the compiler keeps LDS reads and these LDS-writing
-      // loads in program order). Past the last stage they reload it into a
-      // retired buffer (same addresses, never read), which keeps the step
-      // one straight-line block.
-      if (s == 0) issue(min(kt + NS - 1, nk - 1), kt + NS - 1);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x32(fa[s & 1][i], fb[s & 1][j], acc[i][j]);
+    for (int s = 0; s + 1 < KS; ++s) {
+      read_frags(st, s + 1, (s + 1) & 1);
+      mfmas(s & 1);
     }
-    // Instruction order for the step (left to the compiler, the fragment
-    // reads sink next to their MFMAs and every read's latency is exposed):
-    // the first slice's reads, then for each slice its MFMAs with one of the
-    // next slice's reads after each of the first MFMAs; in the first slice
-    // the next stage's global loads follow, spread over its last MFMAs.
-    constexpr int NR = FM + FN, NM = FM * FN;
-    static_assert(NM >= NR, "more fragment reads than MFMAs in a slice");
-    constexpr int FREE = NM - NR;  // MFMA slots of the first slice without a read
-    constexpr int VPS = FREE > 0 ? (PER_STAGE + FREE - 1) / FREE : 0;  // loads per slot
-    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const int nr = (s + 1 < KS) ? NR : 0;
+    for (int s = 0; s + 1 < KS; ++s) {
 #pragma unroll
       for (int q = 0; q < NM; ++q) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (q < nr) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        if (s == 0 && q >= NR) {
-#pragma unroll
-          for (int v = 0; v < VPS; ++v)
-            if ((q - NR) * VPS + v < PER_STAGE) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
-        }
+        if (q < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
-      if (s == 0 && FREE == 0) {
+    }
+    // Before the last slice (its fragments are already in registers): this
+    // wave's part of stage kt+1 has landed once the NS - 2 stages requested
+    // after it are all that is outstanding, and its reads of stage kt are
+    // done. After the barrier every wave's part of stage kt+1 is visible and
+    // no wave reads stage kt again, so its buffer takes stage kt + NS and
+    // the first fragments of stage kt+1 are read under the last slice's
+    // MFMAs: no step starts by waiting for LDS.
+    __builtin_amdgcn_sched_barrier(0);  // MFMAs do not cross the wait either
+    wait_vmcnt<(NS - 2) * PER_STAGE>();
+    __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(smem + ((kt + 1) % NS) * STAGE, 0, 0);
+    issue(min(kt + NS, nk - 1), kt + NS);
+    mfmas((KS - 1) & 1);
+    // The last slice's MFMAs with the fragment reads two to a slot first (the
+    // compiler keeps them ahead of the loads, which also write LDS), then the
+    // next stage's loads spread over the remaining MFMAs.
+    constexpr int RS = (NR + 1) / 2;  // slots that carry reads
+    constexpr int GS = NM - RS;       // slots that carry loads
+    static_assert(GS > 0, "no MFMA slot left for the loads");
 #pragma unroll
-        for (int v = 0; v < PER_STAGE; ++v) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+    for (int q = 0; q < NM; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (q < RS) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (2 * q + 1 < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      } else {
+        const int g = ((q - RS + 1) * PER_STAGE) / GS - ((q - RS) * PER_STAGE) / GS;
+#pragma unroll
+        for (int v = 0; v < g; ++v) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
       }
     }
   }
-  __syncthreads();
-  epilogue_tile<BM, BN, GROUPED>(a, t, sw, bias, smem, acc);
+  __syncthreads();  // waits for every load, including the reloads past the last stage
+  epilogue_tile<BM, BN, GROUPED>(a, t, ef, smem, acc);
 }
 
 // ------------------------------------------------------------- general kernel
@@ -452,6 +552,7 @@ __global__ __launch_bounds__(256) void gemm_i8_kernel(GemmArgs a, int tiles_m, i
   const int8_t* B = a.B + t.expert * a.N * a.ldb;
   const float* sw = a.s_w + (GROUPED ? t.expert * a.N : 0);
   const uint16_t* bias = (GROUPED && a.bias) ? a.bias + t.expert * a.N : a.bias;
+  const EpiFetch ef = epilogue_fetch<BM, BN, GROUPED>(a, t, sw, bias);
 
   // ---- per-thread global source pointers (fixed over K)
   const int8_t* a_src[A_PER_T];
@@ -543,7 +644,7 @@ __global__ __launch_bounds__(256) void gemm_i8_kernel(GemmArgs a, int tiles_m, i
     if (more) store_tile((kt + 1) & 1);
     __syncthreads();
   }
-  epilogue_tile<BM, BN, GROUPED>(a, t, sw, bias, smem, acc);
+  epilogue_tile<BM, BN, GROUPED>(a, t, ef, smem, acc);
 }
 
 namespace {
