@@ -369,21 +369,24 @@ __device__ __forceinline__ int swz(int r) {
   return CH == 4 ? (((r >> 1) ^ (r >> 3)) & 3) : ((r ^ ((r >> 3) & 3)) & 7);
 }
 
-template <int BM, int BN, int BK, int NS, bool GROUPED>
+template <int BM, int BN, int BK, int NH, bool GROUPED>
 __global__ __launch_bounds__(256) void gemm_i8_dma_kernel(GemmArgs a, int tiles_m, int tiles_n) {
-  constexpr int STAGE = (BM + BN) * BK;
   constexpr int TM = BM / 2, TN = BN / 2, FM = TM / 32, FN = TN / 32;
+  // The ring is made of NH half-stages: half-stage 2s + p holds K step s of
+  // the A rows [p*TM, p*TM + TM) and the B rows [p*TN, p*TN + TN) -- the
+  // operands of the waves in tile row p and tile column p.
+  constexpr int HSTAGE = (TM + TN) * BK;
   constexpr int CH = BK / 16;                 // 16-byte chunks per tile row
   constexpr int RPI = 64 / CH;                // tile rows per 1-KiB load instruction
-  constexpr int AI = BM / RPI / 4, BI = BN / RPI / 4;  // load instructions per wave per stage
-  constexpr int PER_STAGE = AI + BI;
-  constexpr int KS = BK / 32;                 // MFMA k slices per stage
+  constexpr int AI = TM / RPI / 4, BI = TN / RPI / 4;  // load instructions per wave per half-stage
+  constexpr int PER_HALF = AI + BI;
+  constexpr int KS = BK / 32;                 // MFMA k slices per K step
   static_assert(CH == 4 || CH == 8, "BK is 64 or 128");
-  static_assert(BM % (4 * RPI) == 0 && BN % (4 * RPI) == 0, "tile / load mismatch");
-  static_assert(NS >= 2 && (NS - 1) * PER_STAGE <= 63, "stages / vmcnt range");
-  static_assert(epilogue_lds_bytes<BM, BN>() <= NS * STAGE, "epilogue does not fit the LDS");
+  static_assert(TM % (4 * RPI) == 0 && TN % (4 * RPI) == 0, "tile / load mismatch");
+  static_assert(NH >= 5 && (NH - 3) * PER_HALF <= 63, "ring / vmcnt range");
+  static_assert(epilogue_lds_bytes<BM, BN>() <= NH * HSTAGE, "epilogue does not fit the LDS");
 
-  __shared__ __attribute__((aligned(1024))) int8_t smem[NS * STAGE];
+  __shared__ __attribute__((aligned(1024))) int8_t smem[NH * HSTAGE];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -396,54 +399,66 @@ __global__ __launch_bounds__(256) void gemm_i8_dma_kernel(GemmArgs a, int tiles_
   // issued before the ring's loads, so the ring's vmcnt waits retire them too
   const EpiFetch ef = epilogue_fetch<BM, BN, GROUPED>(a, t, sw, bias);
 
-  // ---- per-lane DMA sources: instruction q of this wave fills tile rows
-  // (wave*AI + q)*RPI .. +RPI-1; lane l writes row +l/CH, physical chunk
-  // l%CH, which holds logical chunk (l%CH) ^ swz(row).
+  // ---- per-lane DMA sources: in half-stage part p, instruction q of this
+  // wave fills tile rows p*TM + (wave*AI + q)*RPI .. +RPI-1 of A (likewise
+  // for B); lane l writes row +l/CH, physical chunk l%CH, which holds logical
+  // chunk (l%CH) ^ swz(row).
   const int lrow = lane / CH, pch = lane % CH;
-  const int8_t* a_src[AI];
+  const int8_t* a_src[2][AI];
+  const int8_t* b_src[2][BI];
 #pragma unroll
-  for (int q = 0; q < AI; ++q) {
-    const int r = (wave * AI + q) * RPI + lrow;
-    const int64_t gr = min(t.row_begin + r, t.row_end - 1);
-    const int64_t src = source_row<GROUPED>(a, gr);
-    a_src[q] = a.A + (src > 0 ? src : 0) * a.lda + (pch ^ swz<CH>(r)) * 16;
+  for (int p = 0; p < 2; ++p) {
+#pragma unroll
+    for (int q = 0; q < AI; ++q) {
+      const int r = p * TM + (wave * AI + q) * RPI + lrow;
+      const int64_t gr = min(t.row_begin + r, t.row_end - 1);
+      const int64_t src = source_row<GROUPED>(a, gr);
+      a_src[p][q] = a.A + (src > 0 ? src : 0) * a.lda + (pch ^ swz<CH>(r)) * 16;
+    }
+#pragma unroll
+    for (int q = 0; q < BI; ++q) {
+      const int r = p * TN + (wave * BI + q) * RPI + lrow;
+      const int64_t n = min(t.n_begin + r, a.N - 1);
+      b_src[p][q] = B + n * a.ldb + (pch ^ swz<CH>(r)) * 16;
+    }
   }
-  const int8_t* b_src[BI];
-#pragma unroll
-  for (int q = 0; q < BI; ++q) {
-    const int r = (wave * BI + q) * RPI + lrow;
-    const int64_t n = min(t.n_begin + r, a.N - 1);
-    b_src[q] = B + n * a.ldb + (pch ^ swz<CH>(r)) * 16;
-  }
-  // Loads K step kt_src into LDS stage kt_dst % NS.
-  auto issue = [&](int kt_src, int kt_dst) __attribute__((always_inline)) {
-    int8_t* st = smem + (kt_dst % NS) * STAGE;
-    const int64_t k0 = (int64_t)kt_src * BK;
-#pragma unroll
-    for (int q = 0; q < AI; ++q)
-      __builtin_amdgcn_global_load_lds((global_void_ptr)(a_src[q] + k0),
-                                       (lds_void_ptr)(st + (wave * AI + q) * 1024), 16, 0, 0);
-#pragma unroll
-    for (int q = 0; q < BI; ++q)
-      __builtin_amdgcn_global_load_lds((global_void_ptr)(b_src[q] + k0),
-                                       (lds_void_ptr)(st + BM * BK + (wave * BI + q) * 1024), 16, 0,
-                                       0);
+  const int nk = (int)(a.K / BK);
+  // Load instruction q (of PER_HALF) of half-stage h: K step h / 2 (past the
+  // last K step it reloads the last one), part P = h % 2, into ring slot
+  // h % NH. P is known where it is called, so the source pointers are picked
+  // at compile time.
+  auto issue_one = [&](int h, auto part, int q) __attribute__((always_inline)) {
+    constexpr int P = decltype(part)::value;
+    int8_t* dst = smem + (h % NH) * HSTAGE;
+    const int64_t k0 = (int64_t)min(h >> 1, nk - 1) * BK;
+    if (q < AI)
+      __builtin_amdgcn_global_load_lds((global_void_ptr)(a_src[P][q] + k0),
+                                       (lds_void_ptr)(dst + (wave * AI + q) * 1024), 16, 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds((global_void_ptr)(b_src[P][q - AI] + k0),
+                                       (lds_void_ptr)(dst + TM * BK + (wave * BI + q - AI) * 1024), 16,
+                                       0, 0);
   };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  using PA = std::integral_constant<int, (NH - 1) & 1>;  // part of the half-stage issued in region A
+  using PB = std::integral_constant<int, NH & 1>;        // part of the half-stage issued in region B
 
-  // ---- fragment reads: lane reads tile row (.. + lane%32), logical chunk
-  // 2*ks + lane/32 of the BK-byte row; rows 32 apart share swz().
+  // ---- fragment reads of K step s: lane reads tile row (.. + lane%32),
+  // logical chunk 2*ks + lane/32 of the BK-byte row, from the half-stage of
+  // this wave's tile row (A) and tile column (B); rows 32 apart share swz().
   const int fr = lane & 31;
   const int fsw = swz<CH>(fr);
-  const int a_base = wm * TM * BK + fr * BK, b_base = BM * BK + wn * TN * BK + fr * BK;
   i32x4 fa[2][FM], fb[2][FN];
-  auto read_frags = [&](const int8_t* st, int ks, int slot) __attribute__((always_inline)) {
+  auto read_one = [&](int s, int ks, int slot, int f) __attribute__((always_inline)) {
     const int off = ((2 * ks + (lane >> 5)) ^ fsw) * 16;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-      fa[slot][i] = *reinterpret_cast<const i32x4*>(st + a_base + i * 32 * BK + off);
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-      fb[slot][j] = *reinterpret_cast<const i32x4*>(st + b_base + j * 32 * BK + off);
+    if (f < FM) {
+      const int8_t* sa = smem + ((2 * s + wm) % NH) * HSTAGE + fr * BK;
+      fa[slot][f] = *reinterpret_cast<const i32x4*>(sa + f * 32 * BK + off);
+    } else {
+      const int8_t* sb = smem + ((2 * s + wn) % NH) * HSTAGE + TM * BK + fr * BK;
+      fb[slot][f - FM] = *reinterpret_cast<const i32x4*>(sb + (f - FM) * 32 * BK + off);
+    }
   };
 
   i32x16 acc[FM][FN];
@@ -460,28 +475,49 @@ __global__ __launch_bounds__(256) void gemm_i8_dma_kernel(GemmArgs a, int tiles_
 #pragma unroll
       for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x32(fa[slot][i], fb[slot][j], acc[i][j]);
   };
-  static_assert(KS % 2 == 0, "the next stage's first slice reuses fragment slot 0");
+  static_assert(KS % 2 == 0, "the next step's first slice reuses fragment slot 0");
   constexpr int NR = FM + FN, NM = FM * FN;
   static_assert(NM >= NR, "more fragment reads than MFMAs in a slice");
+  // Region A's loads go out one after every RA-th fragment read.
+  constexpr int READS_A = (KS - 1) * NR;
+  constexpr int RA = READS_A / PER_HALF;
+  static_assert(RA >= 1, "region A has fewer fragment reads than loads");
 
-  // The ring's NS stages are all requested up front; the step that finishes
-  // with stage kt requests stage kt + NS into its buffer. Past the last stage
-  // the requests reload it into a retired buffer (same addresses, never
+  // Half-stages 0 .. NH-2 are requested up front. Step kt then requests two
+  // more, each into the slot of a retired half-stage: half-stage 2kt + NH - 1
+  // (the second half of step kt-1's slots, retired at the previous barrier)
+  // spread over the step's first slices, and half-stage 2kt + NH (the first
+  // of step kt's own slots) right after the barrier. The loads in flight
+  // reach one and a half K steps ahead, each barrier waits only for the
+  // half-stage requested in the step before, and no slice issues more than
+  // a few loads: a load instruction that has to wait for the memory pipeline
+  // holds up the MFMAs queued behind it in the same wave. Past the last K
+  // step the requests reload it into retired slots (same addresses, never
   // read), which keeps every step one straight-line block.
-  const int nk = (int)(a.K / BK);
 #pragma unroll
-  for (int s = 0; s < NS; ++s) issue(min(s, nk - 1), s);
-  wait_vmcnt<(NS - 1) * PER_STAGE>();
-  barrier_no_fence();  // every wave's part of stage 0 has landed
-  read_frags(smem, 0, 0);
+  for (int h = 0; h < NH - 1; ++h)
+#pragma unroll
+    for (int q = 0; q < PER_HALF; ++q) {
+      if (h % 2 == 0) issue_one(h, P0{}, q);
+      else issue_one(h, P1{}, q);
+    }
+  wait_vmcnt<(NH - 3) * PER_HALF>();
+  barrier_no_fence();  // every wave's part of K step 0 has landed
+#pragma unroll
+  for (int f = 0; f < NR; ++f) read_one(0, 0, 0, f);
 
   for (int kt = 0; kt < nk; ++kt) {
-    const int8_t* st = smem + (kt % NS) * STAGE;
-    // All slices but the last: each slice's MFMAs with the next slice's
-    // fragment reads slotted in after the first of them.
+    // Region A, all slices but the last: each slice's MFMAs with the next
+    // slice's fragment reads slotted in after the first of them, and one
+    // load of half-stage 2kt + NH - 1 after every RA-th read.
 #pragma unroll
     for (int s = 0; s + 1 < KS; ++s) {
-      read_frags(st, s + 1, (s + 1) & 1);
+#pragma unroll
+      for (int f = 0; f < NR; ++f) {
+        read_one(kt, s + 1, (s + 1) & 1, f);
+        const int r = s * NR + f;
+        if (r % RA == RA - 1 && r / RA < PER_HALF) issue_one(2 * kt + NH - 1, PA{}, r / RA);
+      }
       mfmas(s & 1);
     }
 #pragma unroll
@@ -489,43 +525,46 @@ __global__ __launch_bounds__(256) void gemm_i8_dma_kernel(GemmArgs a, int tiles_
 #pragma unroll
       for (int q = 0; q < NM; ++q) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (q < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (q < NR) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          const int r = s * NR + q;
+          if (r % RA == RA - 1 && r / RA < PER_HALF) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+        }
       }
     }
     // Before the last slice (its fragments are already in registers): this
-    // wave's part of stage kt+1 has landed once the NS - 2 stages requested
-    // after it are all that is outstanding, and its reads of stage kt are
-    // done. After the barrier every wave's part of stage kt+1 is visible and
-    // no wave reads stage kt again, so its buffer takes stage kt + NS and
-    // the first fragments of stage kt+1 are read under the last slice's
-    // MFMAs: no step starts by waiting for LDS.
+    // wave's parts of K step kt+1 have landed once the NH - 4 half-stages
+    // requested after them are all that is outstanding, and its reads of K
+    // step kt are done. After the barrier every wave's parts of step kt+1 are
+    // visible and no wave reads step kt again, so its slots take the next
+    // requests and the first fragments of step kt+1 are read under the last
+    // slice's MFMAs: no step starts by waiting for LDS.
     __builtin_amdgcn_sched_barrier(0);  // MFMAs do not cross the wait either
-    wait_vmcnt<(NS - 2) * PER_STAGE>();
+    wait_vmcnt<(NH - 4) * PER_HALF>();
     __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-    read_frags(smem + ((kt + 1) % NS) * STAGE, 0, 0);
-    issue(min(kt + NS, nk - 1), kt + NS);
+    // Region B, the last slice: the next step's first fragment reads, each
+    // followed by one load of half-stage 2kt + NH.
+#pragma unroll
+    for (int f = 0; f < NR; ++f) {
+      read_one(kt + 1, 0, 0, f);
+      if (f < PER_HALF) issue_one(2 * kt + NH, PB{}, f);
+    }
+#pragma unroll
+    for (int q = NR; q < PER_HALF; ++q) issue_one(2 * kt + NH, PB{}, q);
     mfmas((KS - 1) & 1);
-    // The last slice's MFMAs with the fragment reads two to a slot first (the
-    // compiler keeps them ahead of the loads, which also write LDS), then the
-    // next stage's loads spread over the remaining MFMAs.
-    constexpr int RS = (NR + 1) / 2;  // slots that carry reads
-    constexpr int GS = NM - RS;       // slots that carry loads
-    static_assert(GS > 0, "no MFMA slot left for the loads");
 #pragma unroll
     for (int q = 0; q < NM; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (q < RS) {
+      if (q < NR) {
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        if (2 * q + 1 < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      } else {
-        const int g = ((q - RS + 1) * PER_STAGE) / GS - ((q - RS) * PER_STAGE) / GS;
-#pragma unroll
-        for (int v = 0; v < g; ++v) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+        if (q < PER_HALF) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+      } else if (q < PER_HALF) {
+        __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
       }
     }
   }
-  __syncthreads();  // waits for every load, including the reloads past the last stage
+  __syncthreads();  // waits for every load, including the reloads past the last step
   epilogue_tile<BM, BN, GROUPED>(a, t, ef, smem, acc);
 }
 
@@ -660,12 +699,19 @@ struct TileCfg {
 // = rounds of workgroups over the CUs x tile area / measured relative
 // throughput per unit of tile area (1.0, 0.82, 0.81, 0.72 for the four sizes
 // on 8192 x 4096 x 4096 with BK = 128).
-TileCfg pick_tile(int64_t M, int64_t N) {
+// K-step variant: 128-byte steps (full cache lines per row and load) when K
+// allows, 64-byte steps otherwise, registers-staged with zero fill for any
+// other K.
+enum KVariant { kK128 = 0, kK64 = 1, kKAny = 2 };
+KVariant pick_k(int64_t K) { return K % 128 == 0 ? kK128 : (K % 64 == 0 ? kK64 : kKAny); }
+
+TileCfg pick_tile(int64_t M, int64_t N, int64_t K) {
   const TileCfg menu[4] = {{256, 256}, {256, 192}, {256, 128}, {128, 128}};
   const double eff[4] = {1.0, 0.82, 0.81, 0.72};
   int best = 0;
   double best_cost = 0;
   for (int c = 0; c < 4; ++c) {
+    if (menu[c].bn == 192 && pick_k(K) == kK64) continue;  // 96-column halves need 128-byte steps
     const int64_t tiles = ((M + menu[c].bm - 1) / menu[c].bm) * ((N + menu[c].bn - 1) / menu[c].bn);
     const int64_t rounds = (tiles + 255) / 256;
     const double cost = (double)rounds * menu[c].bm * menu[c].bn / eff[c];
@@ -677,35 +723,36 @@ TileCfg pick_tile(int64_t M, int64_t N) {
   return menu[best];
 }
 
-// K-step variant: 128-byte steps (full cache lines per row and load) when K
-// allows, 64-byte steps with a deeper ring otherwise, registers-staged with
-// zero fill for any other K. The 128-byte ring takes as many stages (up to
-// 4) as the 160 KiB of LDS hold.
-enum KVariant { kK128 = 0, kK64 = 1, kKAny = 2 };
-KVariant pick_k(int64_t K) { return K % 128 == 0 ? kK128 : (K % 64 == 0 ? kK64 : kKAny); }
+// The ring takes as many half-stages (up to 10) as the 160 KiB of LDS hold.
 
-template <int BM, int BN>
-constexpr int stages128() {
+template <int BM, int BN, int BK>
+constexpr int ring_halves() {
   constexpr int kLds = 160 * 1024;
-  return (BM + BN) * 128 * 4 <= kLds ? 4 : ((BM + BN) * 128 * 3 <= kLds ? 3 : 2);
+  constexpr int n = kLds / ((BM + BN) / 2 * BK);
+  return n < 10 ? n : 10;
 }
-static_assert(stages128<256, 256>() == 2 && stages128<256, 192>() == 2 && stages128<256, 128>() == 3 &&
-                  stages128<128, 128>() == 4,
-              "stage counts the kernel names below state");
+static_assert(ring_halves<256, 256, 128>() == 5 && ring_halves<256, 192, 128>() == 5 &&
+                  ring_halves<256, 128, 128>() == 6 && ring_halves<128, 128, 128>() == 10 &&
+                  ring_halves<256, 256, 64>() == 10 && ring_halves<256, 128, 64>() == 10 &&
+                  ring_halves<128, 128, 64>() == 10,
+              "ring sizes the kernel names below state");
 
 template <int BM, int BN, bool GROUPED>
 hipError_t launch_tiles(const GemmArgs& a, int64_t extra_m_tiles, hipStream_t stream) {
   const int64_t tiles_m = (a.M + BM - 1) / BM + extra_m_tiles;
   const int tiles_n = (int)((a.N + BN - 1) / BN);
   const dim3 grid((unsigned)(tiles_m * tiles_n)), block(256);
-  switch (pick_k(a.K)) {
+  KVariant kv = pick_k(a.K);
+  if (kv == kK64 && BN == 192) kv = kKAny;  // not picked (pick_tile); kept launchable
+  switch (kv) {
     case kK128:
-      hipLaunchKernelGGL((gemm_i8_dma_kernel<BM, BN, 128, stages128<BM, BN>(), GROUPED>), grid, block,
-                         0, stream, a, (int)tiles_m, tiles_n);
+      hipLaunchKernelGGL((gemm_i8_dma_kernel<BM, BN, 128, ring_halves<BM, BN, 128>(), GROUPED>), grid,
+                         block, 0, stream, a, (int)tiles_m, tiles_n);
       break;
     case kK64:
-      hipLaunchKernelGGL((gemm_i8_dma_kernel<BM, BN, 64, 4, GROUPED>), grid, block, 0, stream, a,
-                         (int)tiles_m, tiles_n);
+      if constexpr (BN != 192)
+        hipLaunchKernelGGL((gemm_i8_dma_kernel<BM, BN, 64, ring_halves<BM, BN, 64>(), GROUPED>), grid,
+                           block, 0, stream, a, (int)tiles_m, tiles_n);
       break;
     default:
       hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, GROUPED>), grid, block, 0, stream, a, (int)tiles_m,
@@ -716,14 +763,14 @@ hipError_t launch_tiles(const GemmArgs& a, int64_t extra_m_tiles, hipStream_t st
 
 const char* kernel_name(int bm, int bn, bool grouped, int64_t K) {
   static const char* names[3][2][4] = {
-      {{"gemm_i8_dma_kernel<256, 256, 128, 2, false>", "gemm_i8_dma_kernel<256, 192, 128, 2, false>",
-        "gemm_i8_dma_kernel<256, 128, 128, 3, false>", "gemm_i8_dma_kernel<128, 128, 128, 4, false>"},
-       {"gemm_i8_dma_kernel<256, 256, 128, 2, true>", "gemm_i8_dma_kernel<256, 192, 128, 2, true>",
-        "gemm_i8_dma_kernel<256, 128, 128, 3, true>", "gemm_i8_dma_kernel<128, 128, 128, 4, true>"}},
-      {{"gemm_i8_dma_kernel<256, 256, 64, 4, false>", "gemm_i8_dma_kernel<256, 192, 64, 4, false>",
-        "gemm_i8_dma_kernel<256, 128, 64, 4, false>", "gemm_i8_dma_kernel<128, 128, 64, 4, false>"},
-       {"gemm_i8_dma_kernel<256, 256, 64, 4, true>", "gemm_i8_dma_kernel<256, 192, 64, 4, true>",
-        "gemm_i8_dma_kernel<256, 128, 64, 4, true>", "gemm_i8_dma_kernel<128, 128, 64, 4, true>"}},
+      {{"gemm_i8_dma_kernel<256, 256, 128, 5, false>", "gemm_i8_dma_kernel<256, 192, 128, 5, false>",
+        "gemm_i8_dma_kernel<256, 128, 128, 6, false>", "gemm_i8_dma_kernel<128, 128, 128, 10, false>"},
+       {"gemm_i8_dma_kernel<256, 256, 128, 5, true>", "gemm_i8_dma_kernel<256, 192, 128, 5, true>",
+        "gemm_i8_dma_kernel<256, 128, 128, 6, true>", "gemm_i8_dma_kernel<128, 128, 128, 10, true>"}},
+      {{"gemm_i8_dma_kernel<256, 256, 64, 10, false>", "gemm_i8_kernel<256, 192, false>",
+        "gemm_i8_dma_kernel<256, 128, 64, 10, false>", "gemm_i8_dma_kernel<128, 128, 64, 10, false>"},
+       {"gemm_i8_dma_kernel<256, 256, 64, 10, true>", "gemm_i8_kernel<256, 192, true>",
+        "gemm_i8_dma_kernel<256, 128, 64, 10, true>", "gemm_i8_dma_kernel<128, 128, 64, 10, true>"}},
       {{"gemm_i8_kernel<256, 256, false>", "gemm_i8_kernel<256, 192, false>", "gemm_i8_kernel<256, 128, false>",
         "gemm_i8_kernel<128, 128, false>"},
        {"gemm_i8_kernel<256, 256, true>", "gemm_i8_kernel<256, 192, true>", "gemm_i8_kernel<256, 128, true>",
@@ -735,7 +782,7 @@ const char* kernel_name(int bm, int bn, bool grouped, int64_t K) {
 }  // namespace
 
 hipError_t launch_scaled_mm(const GemmArgs& a, hipStream_t stream) {
-  const TileCfg t = pick_tile(a.M, a.N);
+  const TileCfg t = pick_tile(a.M, a.N, a.K);
   if (t.bm == 256 && t.bn == 256) return launch_tiles<256, 256, false>(a, 0, stream);
   if (t.bm == 256 && t.bn == 192) return launch_tiles<256, 192, false>(a, 0, stream);
   if (t.bm == 256) return launch_tiles<256, 128, false>(a, 0, stream);
@@ -743,7 +790,7 @@ hipError_t launch_scaled_mm(const GemmArgs& a, hipStream_t stream) {
 }
 
 const char* scaled_mm_kernel_name(int64_t M, int64_t N, int64_t K) {
-  const TileCfg t = pick_tile(M, N);
+  const TileCfg t = pick_tile(M, N, K);
   return kernel_name(t.bm, t.bn, false, K);
 }
 
