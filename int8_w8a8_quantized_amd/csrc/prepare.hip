@@ -183,21 +183,46 @@ __device__ __forceinline__ int group_or(int v) {
   return v;
 }
 
-// LPR lanes own one row (64, or 32 when that packs the row's chunks tighter);
-// CH = 16-code chunks per lane kept in registers; rows with K <= CH*LPR*16.
+// LPR lanes own one row at a time (64, or 32 when that packs the row's
+// chunks tighter); CH = 16-code chunks per lane; rows with K <= CH*LPR*16.
+// Each lane group walks rows group, group + groups, ... and has the codes
+// and block scales of the next row loading into registers while it converts
+// the current one, so a CU keeps two rows per group in flight (one row's
+// loads cannot cover the HBM latency) and the conversion arithmetic runs
+// under the next row's loads. A third row in flight measured no faster: the
+// conversion arithmetic (about 400 VALU operations per lane and row, at 3
+// waves per SIMD) is what remains.
+struct Fp8Row {
+  const float* srow;   // block scales of the row's block-row
+  int64_t row;
+};
+
 template <int CH, int LPR>
-__global__ __launch_bounds__(256) void fp8_rows_kernel(const uint8_t* __restrict__ W8,
-                                                       const float* __restrict__ S, int64_t E,
-                                                       int64_t N, int64_t K, int8_t* __restrict__ Wq,
-                                                       float* __restrict__ s_out,
-                                                       int32_t* __restrict__ err_flag) {
-  const int lane = threadIdx.x % LPR;
-  const int64_t row = (int64_t)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;  // over E*N rows
-  if (row >= E * N) return;  // a whole row group leaves: the reductions stay inside groups
+__device__ __forceinline__ Fp8Row fp8_row_load(const uint8_t* __restrict__ W8, const float* __restrict__ S,
+                                               int64_t N, int64_t K, int64_t row, int lane,
+                                               uint4 (&raw)[CH], float (&sc)[CH]) {
+  Fp8Row r;
   const int64_t e = row / N, i = row - e * N;
   const int64_t nb = (N + 127) >> 7, kb = (K + 127) >> 7;
-  const float* srow = S + (e * nb + (i >> 7)) * kb;
+  r.srow = S + (e * nb + (i >> 7)) * kb;
+  r.row = row;
   const uint8_t* codes = W8 + row * K;
+  const int64_t nchunk = K >> 4;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int64_t j = (int64_t)c * LPR + lane;
+    const int64_t jj = j < nchunk ? j : nchunk - 1;  // past the row: a reload, never used
+    raw[c] = ld16(codes + jj * 16);
+    sc[c] = r.srow[(jj * 16) >> 7];
+  }
+  return r;
+}
+
+template <int CH, int LPR>
+__device__ __forceinline__ void fp8_row_convert(const uint8_t* __restrict__ W8, int64_t K,
+                                                int8_t* __restrict__ Wq, float* __restrict__ s_out,
+                                                int32_t* __restrict__ err_flag, const Fp8Row& r, int lane,
+                                                const uint4 (&raw)[CH], const float (&sc)[CH]) {
   const int64_t nchunk = K >> 4;
   float w32[CH][16];
   bool nan_code = false, bad_scale = false;
@@ -206,11 +231,10 @@ __global__ __launch_bounds__(256) void fp8_rows_kernel(const uint8_t* __restrict
   for (int c = 0; c < CH; ++c) {
     const int64_t j = (int64_t)c * LPR + lane;
     if (j < nchunk) {
-      const uint4 v = ld16(codes + j * 16);
-      const float sc = srow[(j * 16) >> 7];
+      const uint4 v = raw[c];
       nan_code |= has_nan_code(v.x) | has_nan_code(v.y) | has_nan_code(v.z) | has_nan_code(v.w);
-      bad_scale |= !legal_block_scale(sc);
-      decode16(v, sc, w32[c]);
+      bad_scale |= !legal_block_scale(sc[c]);
+      decode16(v, sc[c], w32[c]);
 #pragma unroll
       for (int b = 0; b < 16; ++b) amax = fmaxf(amax, fabsf(w32[c][b]));
     } else {
@@ -221,18 +245,45 @@ __global__ __launch_bounds__(256) void fp8_rows_kernel(const uint8_t* __restrict
   amax = group_max<LPR>(amax);
   const int any_nan = group_or<LPR>((int)nan_code), any_bad = group_or<LPR>((int)bad_scale);
   int flags = (any_nan ? 1 : 0) | (any_bad ? 2 : 0);
-  if (!(amax <= 3.402823466e38f)) flags |= group_or<LPR>(row_flags_slow(RowCtx{codes, srow, K}, lane, LPR));
+  if (!(amax <= 3.402823466e38f))
+    flags |= group_or<LPR>(row_flags_slow(RowCtx{W8 + r.row * K, r.srow, K}, lane, LPR));
   const float s = (amax == 0.0f) ? 1.0f : amax / 127.0f;
   const RowParams rp = finish_params(s, 0);
-  int8_t* orow = Wq + row * K;
+  int8_t* orow = Wq + r.row * K;
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const int64_t j = (int64_t)c * LPR + lane;
     if (j < nchunk) st16(orow + j * 16, encode16(w32[c], rp));
   }
   if (lane == 0) {
-    s_out[row] = s;
+    s_out[r.row] = s;
     if (flags) atomicOr(err_flag, flags);
+  }
+}
+
+template <int CH, int LPR>
+__global__ __launch_bounds__(256) void fp8_rows_kernel(const uint8_t* __restrict__ W8,
+                                                       const float* __restrict__ S, int64_t E,
+                                                       int64_t N, int64_t K, int8_t* __restrict__ Wq,
+                                                       float* __restrict__ s_out,
+                                                       int32_t* __restrict__ err_flag) {
+  const int lane = threadIdx.x % LPR;
+  const int64_t group = (int64_t)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
+  const int64_t groups = (int64_t)gridDim.x * (256 / LPR);
+  const int64_t rows = E * N;
+  if (group >= rows) return;  // a whole row group leaves: the reductions stay inside groups
+  uint4 rawA[CH], rawB[CH];
+  float scA[CH], scB[CH];
+  // rows past the end are clamped to the last row for their (unused) loads
+  Fp8Row ra = fp8_row_load<CH, LPR>(W8, S, N, K, group, lane, rawA, scA);
+  for (int64_t row = group; row < rows; row += 2 * groups) {
+    const int64_t r1 = row + groups;
+    const Fp8Row rb = fp8_row_load<CH, LPR>(W8, S, N, K, r1 < rows ? r1 : rows - 1, lane, rawB, scB);
+    fp8_row_convert<CH, LPR>(W8, K, Wq, s_out, err_flag, ra, lane, rawA, scA);
+    if (r1 >= rows) break;
+    const int64_t r2 = row + 2 * groups;
+    ra = fp8_row_load<CH, LPR>(W8, S, N, K, r2 < rows ? r2 : rows - 1, lane, rawA, scA);
+    fp8_row_convert<CH, LPR>(W8, K, Wq, s_out, err_flag, rb, lane, rawB, scB);
   }
 }
 
@@ -289,9 +340,15 @@ hipError_t launch_fp8_block_to_int8(const uint8_t* W8, const float* S, int64_t E
   // chunks fill 3 x 32 exactly, but only 96 of 2 x 64)
   const bool half = ch32 <= 4 && 32 * ch32 < 64 * ch64;
   const dim3 block(256);
+  // enough lane groups for every CU to hold its resident waves (3 per SIMD at
+  // this register use) twice over; each group walks its rows
+  const auto grid_for = [&](int lpr) {
+    const int64_t need = (rows + 256 / lpr - 1) / (256 / lpr);
+    return (unsigned)(need < 256 * 6 ? need : 256 * 6);
+  };
 #define W8A8_FP8(CHV, LPRV)                                                                         \
-  hipLaunchKernelGGL((fp8_rows_kernel<CHV, LPRV>), dim3((unsigned)((rows + 256 / LPRV - 1) / (256 / LPRV))), \
-                     block, 0, stream, W8, S, E, N, K, Wq, s, err_flag)
+  hipLaunchKernelGGL((fp8_rows_kernel<CHV, LPRV>), dim3(grid_for(LPRV)), block, 0, stream, W8, S, E, N, K, \
+                     Wq, s, err_flag)
   if (half) {
     switch (ch32) {
       case 1: W8A8_FP8(1, 32); break;
