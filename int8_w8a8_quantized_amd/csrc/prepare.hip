@@ -138,7 +138,7 @@ __device__ __forceinline__ void decode16(uint4 v, float scale, float* w32) {
 // Codes clamp(rint(fl(w32 / s)), -127, 127) of one chunk (rounding.h).
 __device__ __forceinline__ uint4 encode16(const float* w32, const RowParams& p) {
   uint32_t m[16];
-  round_quotients<16, 127>(w32, p, m);
+  round_quotients<16, 127, false>(w32, p, m);  // s = fl(row absmax / 127)
   return make_uint4(low_bytes4(m[0], m[1], m[2], m[3]), low_bytes4(m[4], m[5], m[6], m[7]),
                     low_bytes4(m[8], m[9], m[10], m[11]), low_bytes4(m[12], m[13], m[14], m[15]));
 }
@@ -174,6 +174,14 @@ template <int LPR>
 __device__ __forceinline__ float group_max(float v) {
 #pragma unroll
   for (int o = LPR / 2; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+// As group_max, but NaN-propagating (v_maximum: a NaN anywhere in the group
+// gives NaN).
+template <int LPR>
+__device__ __forceinline__ float group_maximum(float v) {
+#pragma unroll
+  for (int o = LPR / 2; o >= 1; o >>= 1) v = __builtin_elementwise_maximum(v, __shfl_xor(v, o, kWave));
   return v;
 }
 template <int LPR>
@@ -225,28 +233,38 @@ __device__ __forceinline__ void fp8_row_convert(const uint8_t* __restrict__ W8, 
                                                 const uint4 (&raw)[CH], const float (&sc)[CH]) {
   const int64_t nchunk = K >> 4;
   float w32[CH][16];
-  bool nan_code = false, bad_scale = false;
+  bool bad_scale = false;
   float amax = 0.0f;
+  // The absmax propagates NaN (a NaN code decodes to NaN, and so does any
+  // code under a NaN scale), so NaN codes are looked for in the raw words
+  // only for rows whose absmax is NaN.
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const int64_t j = (int64_t)c * LPR + lane;
     if (j < nchunk) {
-      const uint4 v = raw[c];
-      nan_code |= has_nan_code(v.x) | has_nan_code(v.y) | has_nan_code(v.z) | has_nan_code(v.w);
       bad_scale |= !legal_block_scale(sc[c]);
-      decode16(v, sc[c], w32[c]);
+      decode16(raw[c], sc[c], w32[c]);
 #pragma unroll
-      for (int b = 0; b < 16; ++b) amax = fmaxf(amax, fabsf(w32[c][b]));
+      for (int b = 0; b < 16; ++b) amax = __builtin_elementwise_maximum(amax, fabsf(w32[c][b]));
     } else {
 #pragma unroll
       for (int b = 0; b < 16; ++b) w32[c][b] = 0.0f;
     }
   }
-  amax = group_max<LPR>(amax);
-  const int any_nan = group_or<LPR>((int)nan_code), any_bad = group_or<LPR>((int)bad_scale);
-  int flags = (any_nan ? 1 : 0) | (any_bad ? 2 : 0);
-  if (!(amax <= 3.402823466e38f))
+  amax = group_maximum<LPR>(amax);
+  const int any_bad = group_or<LPR>((int)bad_scale);
+  int flags = any_bad ? 2 : 0;
+  if (!(amax <= 3.402823466e38f)) {  // NaN or infinite: the exact flags
+    bool nan_code = false;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int64_t j = (int64_t)c * LPR + lane;
+      const uint4 v = raw[c];
+      if (j < nchunk) nan_code |= has_nan_code(v.x) | has_nan_code(v.y) | has_nan_code(v.z) | has_nan_code(v.w);
+    }
+    flags |= group_or<LPR>((int)nan_code) ? 1 : 0;
     flags |= group_or<LPR>(row_flags_slow(RowCtx{W8 + r.row * K, r.srow, K}, lane, LPR));
+  }
   const float s = (amax == 0.0f) ? 1.0f : amax / 127.0f;
   const RowParams rp = finish_params(s, 0);
   int8_t* orow = Wq + r.row * K;

@@ -43,8 +43,10 @@ __device__ __forceinline__ uint2 codes8(uint4 v, const RowParams& p) {
     xs[2 * i] = bf16_lo(w[i]);
     xs[2 * i + 1] = bf16_hi(w[i]);
   }
-  // range of rint(x/s): the int8 codes, or +-512 before an asymmetric zero point
-  round_quotients<8, kSym ? 127 : 512>(xs, p, m);
+  // range of rint(x/s): the int8 codes, or +-512 before an asymmetric zero
+  // point; dynamic symmetric scales come from the row's own absmax, so the
+  // quotients cannot leave the range and need no clamp
+  round_quotients<8, kSym ? 127 : 512, MODE != kDynSym>(xs, p, m);
   if (!kSym) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) m[e] = (uint32_t)clampi((int)(m[e] - kMagicBits) + p.zp, -128, 127);

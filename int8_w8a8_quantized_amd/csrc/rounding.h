@@ -42,14 +42,18 @@ constexpr uint32_t kMagicBits = 0x4B400000u;
 
 // m[e] = bits of clamp(rint(fl(x[e] / s)), -L, L) + kMagic: the integer is
 // m[e] - kMagicBits, and its low byte is the int8 code when |integer| <= 127.
-template <int NV, int L>
+// CLAMP = false: the caller guarantees s = fl(amax / L) with amax >= |x[e]|
+// for every e. Then |fl(x * fl(1/s))| <= L * (1 + 2^-24)^3 < L + 1/2, so the
+// clamp cannot change the result and is left out (scales outside the fast
+// range still take the clamped true division).
+template <int NV, int L, bool CLAMP = true>
 __device__ __forceinline__ void round_quotients(const float* x, const RowParams& p, uint32_t* m) {
   constexpr float kLim = (float)L;
   constexpr float kTie = 0.5f - kLim * 0x1p-22f;  // |t| <= L: t, fl(x/s) differ by < L * 2^-22
   bool fix = !p.fast;
 #pragma unroll
   for (int e = 0; e < NV; ++e) {
-    const float t = fminf(fmaxf(x[e] * p.r, -kLim), kLim);
+    const float t = CLAMP ? fminf(fmaxf(x[e] * p.r, -kLim), kLim) : x[e] * p.r;
     const float r = t + kMagic;
     fix |= fabsf(t - (r - kMagic)) >= kTie;
     m[e] = __float_as_uint(r);
