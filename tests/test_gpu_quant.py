@@ -83,6 +83,27 @@ def test_edge_rows():
         _check(rows, mode)
 
 
+def test_sym_absmax_boundary():
+    """Rows whose elements sit at and just below the row's absmax, over
+    absmax magnitudes from near the smallest normal scale to near the largest
+    float: the quotients come closest to the code range there (+-127), and
+    the scale's rounding goes either way."""
+    rng = np.random.default_rng(7)
+    K = 256
+    exps = np.concatenate([np.arange(-120, 121, 7), [-126, -125, 125, 126]])
+    rows = []
+    for ex in exps:
+        for mant in rng.integers(0, 128, 3):
+            top = (np.uint16(((int(ex) + 127) << 7) | int(mant)))  # bf16 bits of the absmax
+            below = np.array([top - d for d in range(12)], np.uint16)  # the absmax and the next smaller values
+            r = np.empty(K, np.uint16)
+            r[:] = below[rng.integers(0, len(below), K)]
+            r ^= (rng.integers(0, 2, K) << 15).astype(np.uint16)  # random signs
+            r[rng.integers(0, K)] = top  # the absmax itself, positive
+            rows.append(r)
+    _check(np.stack(rows), W.QUANT_DYN_SYM)
+
+
 @pytest.mark.parametrize("symmetric", [True, False])
 def test_static(symmetric):
     x = _x(129, 4096, 0.3, 20, seed=3)
