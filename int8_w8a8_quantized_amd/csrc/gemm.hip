@@ -15,18 +15,19 @@
 //
 // Main kernel (K a multiple of 64): tiles travel HBM -> LDS with the gfx950
 // direct-to-LDS load (global_load_lds_dwordx4: each lane's 16 bytes land at
-// the wave's LDS base + 16 * lane, no registers involved) into a ring of NS
-// LDS stages of BK = 128 (or 64) bytes of K, so NS - 1 K steps are in flight
-// while the MFMAs of another run. One wave instruction fills 64 / (BK / 16)
-// rows of BK bytes; the 16-byte chunks of row r sit at a chunk position
-// XOR-swizzled by bits of r (swz), which makes the MFMA fragment reads (32
-// rows x one chunk per wave) hit distinct banks whether the LDS serves 8 or
-// 16 lanes of a 16-byte read per cycle. Rows past the end of the matrix
-// load a valid row instead; they only feed outputs the epilogue never
-// stores. One barrier per K step both publishes the stage that just landed
-// and retires the stage the next load overwrites, and the step's
-// instructions are ordered explicitly (sched_group_barrier) so that LDS
-// reads and the next stage's loads slot in between MFMAs.
+// the wave's LDS base + 16 * lane, no registers involved) into a ring of
+// half-stages: half-stage 2s + p holds K step s (BK = 128 or 64 bytes) of the
+// A and B rows of tile half p, and the ring fills the LDS (1.5 K steps in
+// flight at 256 x 256). One wave instruction fills 64 / (BK / 16) rows of BK
+// bytes; the 16-byte chunks of row r sit at a chunk position XOR-swizzled by
+// bits of r (swz), which makes the MFMA fragment reads (32 rows x one chunk
+// per wave) hit distinct banks whether the LDS serves 8 or 16 lanes of a
+// 16-byte read per cycle. Rows past the end of the matrix load a valid row
+// instead; they only feed outputs the epilogue never stores. One barrier per
+// K step, before its last k slice, both publishes the next step and retires
+// this one, and the instructions are ordered explicitly
+// (sched_group_barrier) so that fragment reads and loads slot in between
+// MFMAs.
 //
 // General kernel (any K that is a multiple of 16): the same tile and
 // epilogue, with tiles staged through registers (zero-filled past K) into two
