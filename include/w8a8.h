@@ -136,7 +136,9 @@ w8a8_status w8a8_check_scheme(const w8a8_scheme* scheme, int32_t* quant_mode,
  * nearest even), so the codes are exactly determined.
  * s_x: float [M], written in the dynamic modes (else ignored, may be NULL).
  * zp: int32 [M], written in DYN_ASYM (else may be NULL).
- * s_in / zp_in: device scalars read in the static modes (else may be NULL).
+ * s_in / zp_in: device scalars read in the static modes (else may be NULL);
+ * zp_in is an int8 zero point, in [-128, 127] (outside that range the codes
+ * are unspecified).
  * Requires K % 16 == 0, K <= W8A8_MAX_K, x and xq 16-byte aligned,
  * ldx % 8 == 0, ldq % 16 == 0, ldx >= K, ldq >= K. */
 w8a8_status w8a8_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,

@@ -47,6 +47,31 @@ __device__ __forceinline__ float wave_min(float v) {
   for (int o = 32; o >= 1; o >>= 1) v = fminf(v, __shfl_xor(v, o, kWave));
   return v;
 }
+
+// Wave-wide IEEE-754 maximum / minimum without LDS traffic: within each row
+// of 16 lanes by DPP moves (swap neighbours, swap pairs, half-row mirror, row
+// mirror), then across the four rows by lane reads; every lane gets the
+// result. NaN propagates.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <bool MAX>
+__device__ __forceinline__ float wave_extreme(float v) {
+  auto op = [](float a, float b) {
+    return MAX ? __builtin_elementwise_maximum(a, b) : __builtin_elementwise_minimum(a, b);
+  };
+  v = op(v, dpp_move<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = op(v, dpp_move<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = op(v, dpp_move<0x141>(v));  // row_half_mirror
+  v = op(v, dpp_move<0x140>(v));  // row_mirror
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return op(op(r0, r1), op(r2, r3));
+}
+
 __device__ __forceinline__ int wave_sum(int v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);

@@ -138,7 +138,7 @@ __device__ __forceinline__ void decode16(uint4 v, float scale, float* w32) {
 // Codes clamp(rint(fl(w32 / s)), -127, 127) of one chunk (rounding.h).
 __device__ __forceinline__ uint4 encode16(const float* w32, const RowParams& p) {
   uint32_t m[16];
-  round_quotients<16, 127, false>(w32, p, m);  // s = fl(row absmax / 127)
+  round_quotients<16, false>(w32, p, m);  // s = fl(row absmax / 127): |quotients| < 127.5
   return make_uint4(low_bytes4(m[0], m[1], m[2], m[3]), low_bytes4(m[4], m[5], m[6], m[7]),
                     low_bytes4(m[8], m[9], m[10], m[11]), low_bytes4(m[12], m[13], m[14], m[15]));
 }
@@ -266,7 +266,7 @@ __device__ __forceinline__ void fp8_row_convert(const uint8_t* __restrict__ W8, 
     flags |= group_or<LPR>(row_flags_slow(RowCtx{W8 + r.row * K, r.srow, K}, lane, LPR));
   }
   const float s = (amax == 0.0f) ? 1.0f : amax / 127.0f;
-  const RowParams rp = finish_params(s, 0);
+  const RowParams rp = finish_params(s, 0, -127.0f, 127.0f);
   int8_t* orow = Wq + r.row * K;
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
@@ -336,7 +336,7 @@ __global__ __launch_bounds__(256) void fp8_rows_loop_kernel(const uint8_t* __res
   int flags = (any_nan ? 1 : 0) | (any_bad ? 2 : 0);
   if (!(amax <= 3.402823466e38f)) flags |= wave_or(row_flags_slow(RowCtx{codes, srow, K}, lane, 64));
   const float s = (amax == 0.0f) ? 1.0f : amax / 127.0f;
-  const RowParams rp = finish_params(s, 0);
+  const RowParams rp = finish_params(s, 0, -127.0f, 127.0f);
   int8_t* orow = Wq + row * K;
   for (int64_t j = lane; j < nchunk; j += 64) {
     decode16(ld16(codes + j * 16), srow[(j * 16) >> 7], w32);

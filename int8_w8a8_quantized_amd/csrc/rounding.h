@@ -4,63 +4,90 @@
 // and round half to even ("[SGLang] W4A8, W8A8, W4A4: 혼합 정밀도 양자화 스킴",
 // 핵심 코드 분석 §3; "MiniMax-M2.7 FP8 转昆仑芯 INT8", 转换关系).
 //
-// The division is replaced by t = fl(x * r) with r = fl(1 / s). Whenever 1/s
-// is a normal number, |t - fl(x/s)| < |t| * 2^-22 (two roundings of relative
-// size 2^-24 in t, one in fl(x/s)). t is clamped to the code range L first
-// (the bounds are integers, so clamping and rounding commute, and a clamped t
-// saturates either way), so if t is farther than L * 2^-22 from every
-// half-integer both round to the same integer. t is rounded by adding
-// 1.5 * 2^23, which leaves rint(t) in the low mantissa bits (two's complement
-// in the low byte). A group with a value near a half-integer, and a scale
+// The division is replaced by the product with r = fl(1 / s). A float of
+// magnitude <= 2^22 added to c = 1.5 * 2^23 + z (z a small integer) rounds to
+// an integer and leaves n + z in the low mantissa bits of the sum, n the
+// nearest integer to the addend (two's complement in the low byte): the code
+// with its zero point comes out of one addition. The result is the exact
+// rint(fl(x/s)) whenever the value being rounded is not within
+// L * 2^-22 + 2^-24 of a half-integer, L bounding |x/s|: the product differs
+// from fl(x/s) by less than L * 2^-23 (one rounding in r, one in the quotient),
+// the measured distance is itself rounded once (2^-25). Each group of values
+// checks that distance; a group with a value near a half-integer, or a scale
 // outside (2^-100, 2^100), takes the true division.
+//
+// Two forms:
+//  - bounded (CLAMP = false), for scales derived from the values themselves
+//    (s = fl(amax / 127), or fl((max - min) / 255) with the zero point of the
+//    minimum): every x/s lies within 1 of [lo, hi], so no clamp is needed and
+//    the product and rounding fuse: n from fma(x, r, c), the distance from
+//    fma(x, r, c - sum) (exact product, one rounding; c - sum = -n exactly).
+//  - clamped (CLAMP = true), for a given scale: t = fl(x r) is first clamped
+//    to the integer range [lo, hi] of the codes before the zero point
+//    (clamping and rounding commute for integer bounds, and a clamped t
+//    saturates either way), so every sum lands in the code range.
 #pragma once
 
 #include "device_common.h"
 
 namespace w8a8 {
 
-struct RowParams {
-  float s;     // scale
-  float r;     // fl(1/s)
-  int zp;      // zero point (0 for symmetric rules)
-  bool fast;   // 1/s is comfortably normal: the multiply-and-check path applies
-};
-
-__device__ __forceinline__ RowParams finish_params(float s, int zp) {
-  RowParams p;
-  p.s = s;
-  p.zp = zp;
-  p.fast = s > 0x1p-100f && s < 0x1p100f;
-  p.r = 1.0f / s;
-  return p;
-}
-
 // Adding kMagic = 1.5 * 2^23 to a float of magnitude <= 2^22 rounds it to an
 // integer (ties to even) and leaves that integer + 0x400000 in the mantissa.
 constexpr float kMagic = 12582912.0f;
 constexpr uint32_t kMagicBits = 0x4B400000u;
 
-// m[e] = bits of clamp(rint(fl(x[e] / s)), -L, L) + kMagic: the integer is
-// m[e] - kMagicBits, and its low byte is the int8 code when |integer| <= 127.
-// CLAMP = false: the caller guarantees s = fl(amax / L) with amax >= |x[e]|
-// for every e. Then |fl(x * fl(1/s))| <= L * (1 + 2^-24)^3 < L + 1/2, so the
-// clamp cannot change the result and is left out (scales outside the fast
-// range still take the clamped true division).
-template <int NV, int L, bool CLAMP = true>
+struct RowParams {
+  float s;       // scale
+  float r;       // fl(1/s)
+  float c;       // kMagic + zero point
+  float lo, hi;  // range of rint(x/s) that maps into the codes: [qmin - zp, qmax - zp]
+  float tie;     // the fast path is exact while every |value - n| < tie
+  int zp;        // zero point (0 for symmetric rules)
+  bool fast;     // 1/s is comfortably normal: the multiply-and-check path applies
+};
+
+// lo, hi: integers with max(|lo|, |hi|) <= 2^21 (the tie margin below is then
+// exact in binary32 and positive).
+__device__ __forceinline__ RowParams finish_params(float s, int zp, float lo, float hi) {
+  RowParams p;
+  p.s = s;
+  p.zp = zp;
+  p.c = kMagic + (float)zp;
+  p.lo = lo;
+  p.hi = hi;
+  p.tie = 0.5f - fmaxf(-lo, hi) * 0x1p-22f - 0x1p-24f;
+  p.fast = s > 0x1p-100f && s < 0x1p100f;
+  p.r = 1.0f / s;
+  return p;
+}
+
+// m[e] = bits of p.c + n[e], n[e] = rint(fl(x[e] / s)) (clamped to [lo, hi]
+// when CLAMP): the integer n[e] + zp is m[e] - kMagicBits, and its low byte
+// is the int8 code when it lies in [-128, 127].
+// CLAMP = false: the caller guarantees lo - 1 <= x[e] / s <= hi + 1 for every
+// e (exact quotient); n[e] is not clamped and can then be one outside
+// [lo, hi], which the caller clamps where the rule allows it.
+template <int NV, bool CLAMP>
 __device__ __forceinline__ void round_quotients(const float* x, const RowParams& p, uint32_t* m) {
-  constexpr float kLim = (float)L;
-  constexpr float kTie = 0.5f - kLim * 0x1p-22f;  // |t| <= L: t, fl(x/s) differ by < L * 2^-22
-  bool fix = !p.fast;
+  float dev = 0.0f;  // largest distance to the rounded integer
 #pragma unroll
   for (int e = 0; e < NV; ++e) {
-    const float t = CLAMP ? fminf(fmaxf(x[e] * p.r, -kLim), kLim) : x[e] * p.r;
-    const float r = t + kMagic;
-    fix |= fabsf(t - (r - kMagic)) >= kTie;
-    m[e] = __float_as_uint(r);
+    float sum, d;
+    if (CLAMP) {
+      const float t = fminf(fmaxf(x[e] * p.r, p.lo), p.hi);
+      sum = t + p.c;
+      d = t - (sum - p.c);
+    } else {
+      sum = fmaf(x[e], p.r, p.c);
+      d = fmaf(x[e], p.r, p.c - sum);
+    }
+    dev = fmaxf(dev, fabsf(d));
+    m[e] = __float_as_uint(sum);
   }
-  if (__builtin_expect(fix, 0)) {
+  if (__builtin_expect(!p.fast || !(dev < p.tie), 0)) {
 #pragma unroll
-    for (int e = 0; e < NV; ++e) m[e] = __float_as_uint(fminf(fmaxf(rne(x[e] / p.s), -kLim), kLim) + kMagic);
+    for (int e = 0; e < NV; ++e) m[e] = __float_as_uint(fminf(fmaxf(rne(x[e] / p.s), p.lo), p.hi) + p.c);
   }
 }
 

@@ -111,6 +111,16 @@ def test_static(symmetric):
     _check(x, mode, s_in=0.0213, zp_in=None if symmetric else -17)
 
 
+@pytest.mark.parametrize("s_in,zp_in", [(0.0213, -128), (0.0213, 127), (0.0213, 0),
+                                         (1e-30, 5),    # quotients overflow binary32: saturate
+                                         (1e-35, -3),   # 1/s beyond 2^100: the true division
+                                         (1e35, 100)])  # every quotient rounds to zero
+def test_static_asym_extremes(s_in, zp_in):
+    x = _x(33, 1024, 2.0, 20, seed=11)
+    _check(x, W.QUANT_STATIC_ASYM, s_in=s_in, zp_in=zp_in)
+    _check(x, W.QUANT_STATIC_SYM, s_in=s_in)
+
+
 def test_static_workload():
     d = synth.static_qkv()
     _check(d["x"], W.QUANT_STATIC_ASYM, s_in=float(d["s_in"]), zp_in=int(d["zp_in"]))
