@@ -15,13 +15,14 @@
 // owns 16 * RG weight rows; the waves split K into interleaved 128-byte steps.
 // Each wave keeps a ring of U steps of loads in flight in registers: the
 // weight rows as whole lines (2 * RG instructions per step), and the
-// activation fragments already in MFMA operand order (rows past M repeat row
-// M - 1, so they cost cache hits, not HBM). A step's weight lines go through a
-// 2 KiB-per-row-group LDS buffer of the wave to reach operand order (one
-// 16-byte write and one 16-byte read per lane per 8 rows; XOR-swizzled chunks
-// keep both conflict-free), then v_mfma_i32_16x16x64_i8 accumulates. At the
-// end the waves' partial tiles are added in LDS and the epilogue, whose
-// per-row / per-column operands were loaded before the K loop, writes out.
+// activation (2 * MF instructions; rows past M repeat row M - 1, so they cost
+// cache hits, not HBM): with one token block already in MFMA operand order,
+// with more as whole lines too. A step's lines go through a 2 KiB-per-16-rows
+// LDS buffer of the wave to reach operand order (one 16-byte write and one
+// 16-byte read per lane per 8 rows; XOR-swizzled chunks keep both
+// conflict-free), then v_mfma_i32_16x16x64_i8 accumulates. At the end the
+// waves' partial tiles are added in LDS and the epilogue, whose per-row /
+// per-column operands were loaded before the K loop, writes out.
 //
 // Direct-to-LDS kernel, gemv_dma_kernel (K a multiple of 128; used for M > 16
 // with many weight rows, where one workgroup's activation stage serves 64
@@ -88,7 +89,14 @@ template <int MF, int RG, int W, int U>
 __global__ __launch_bounds__(W * 64) void gemv_reg_kernel(GemmArgs a) {
   constexpr int BN = 16 * RG, BK = 128;
   constexpr int PER = RG * MF * 256;  // accumulator ints of one wave
-  constexpr int TB = BN * BK;         // the wave's transpose buffer
+  // Two or more token blocks: the activation also travels as whole lines and
+  // is transposed in LDS (16 * MF more rows in the wave's buffer). Its
+  // fragment-order loads (16 rows x 64 bytes per instruction) miss L1 at a
+  // third of the line rate, and with 16 weight rows per workgroup every CU
+  // reads the whole activation, M / 16 times the weight bytes.
+  constexpr bool XL = MF >= 2;
+  constexpr int XR = XL ? 16 * MF : 0;
+  constexpr int TB = (BN + XR) * BK;  // the wave's transpose buffer: weight rows, then token rows
   constexpr int SM = (W * TB > W * PER * 4) ? W * TB : W * PER * 4;
   constexpr int EP = (PER + W * 64 - 1) / (W * 64);
   __shared__ __attribute__((aligned(1024))) int8_t smem[SM];
@@ -106,17 +114,21 @@ __global__ __launch_bounds__(W * 64) void gemv_reg_kernel(GemmArgs a) {
 #pragma unroll
   for (int h = 0; h < 2 * RG; ++h)
     wsrc[h] = a.B + gemv_min(n0 + 8 * h + (lane >> 3), a.N - 1) * a.ldb + (lane & 7) * 16;
-  // activation fragments of token block f: lane l reads token 16f + l%16
-  // (rows past M repeat row M-1), k-group l/16 of each 64-byte half step
-  const int8_t* asrc[MF];
+  // activation, 2 * MF instructions per step (rows past M repeat row M-1):
+  // XL: instruction h reads token rows 8h .. 8h+7 as whole lines (lane l: row
+  // 8h + l/8, bytes 16 (l%8) .. +15); otherwise instruction 2f + kb is the
+  // fragment of token block f, half step kb (lane l: token 16f + l%16,
+  // k-group l/16)
+  const int8_t* asrc[2 * MF];
 #pragma unroll
-  for (int f = 0; f < MF; ++f)
-    asrc[f] = a.A + gemv_min(16 * f + (lane & 15), a.M - 1) * a.lda + 16 * (lane >> 4);
+  for (int h = 0; h < 2 * MF; ++h)
+    asrc[h] = XL ? a.A + gemv_min(8 * h + (lane >> 3), a.M - 1) * a.lda + (lane & 7) * 16
+                 : a.A + gemv_min(16 * (h >> 1) + (lane & 15), a.M - 1) * a.lda + 16 * (lane >> 4) + 64 * (h & 1);
 
   GemvEpi<MF, EP> epi;
   epi.load(a, n0, tid, W * 64, PER);
 
-  u32x4 wr[U][2 * RG], ar[U][MF][2];
+  u32x4 wr[U][2 * RG], ar[U][2 * MF];
   // Loads of the wave's step j into ring slot u; a step past the end reloads
   // the last one (a cache hit), so every slot issues the same loads and the
   // compiler's in-order wait counts stay exact.
@@ -126,10 +138,7 @@ __global__ __launch_bounds__(W * 64) void gemv_reg_kernel(GemmArgs a) {
     for (int h = 0; h < 2 * RG; ++h)
       wr[u][h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wsrc[h] + k0));
 #pragma unroll
-    for (int f = 0; f < MF; ++f)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        ar[u][f][kb] = *reinterpret_cast<const u32x4*>(asrc[f] + k0 + 64 * kb);
+    for (int h = 0; h < 2 * MF; ++h) ar[u][h] = *reinterpret_cast<const u32x4*>(asrc[h] + k0);
   };
   i32x4 acc[MF][RG];
 #pragma unroll
@@ -145,24 +154,38 @@ __global__ __launch_bounds__(W * 64) void gemv_reg_kernel(GemmArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (i0 + u < nkw) {
-        // weight lines -> operand order through the wave's LDS buffer (the
-        // wave's LDS accesses execute in order, so no wait is needed between
-        // this step's writes and reads, nor against the previous step's reads)
+        // weight (and XL: token) lines -> operand order through the wave's
+        // LDS buffer (the wave's LDS accesses execute in order, so no wait is
+        // needed between this step's writes and reads, nor against the
+        // previous step's reads)
 #pragma unroll
         for (int h = 0; h < 2 * RG; ++h) {
           const int row = 8 * h + (lane >> 3);
           *reinterpret_cast<u32x4*>(tb + row * BK + (((lane & 7) ^ gemv_swz(row)) * 16)) = wr[u][h];
         }
+        if (XL) {
+#pragma unroll
+          for (int h = 0; h < 2 * MF; ++h) {
+            const int row = BN + 8 * h + (lane >> 3);
+            *reinterpret_cast<u32x4*>(tb + row * BK + (((lane & 7) ^ gemv_swz(row)) * 16)) = ar[u][h];
+          }
+        }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           const int c = 4 * kb + (lane >> 4);
+          i32x4 xf[MF];
+#pragma unroll
+          for (int f = 0; f < MF; ++f) {
+            const int row = BN + 16 * f + (lane & 15);
+            xf[f] = XL ? *reinterpret_cast<const i32x4*>(tb + row * BK + ((c ^ gemv_swz(row)) * 16))
+                       : __builtin_bit_cast(i32x4, ar[u][2 * f + kb]);
+          }
 #pragma unroll
           for (int g = 0; g < RG; ++g) {
             const int row = 16 * g + (lane & 15);
             const i32x4 wf = *reinterpret_cast<const i32x4*>(tb + row * BK + ((c ^ gemv_swz(row)) * 16));
 #pragma unroll
-            for (int f = 0; f < MF; ++f)
-              acc[f][g] = mfma16x16x64(__builtin_bit_cast(i32x4, ar[u][f][kb]), wf, acc[f][g]);
+            for (int f = 0; f < MF; ++f) acc[f][g] = mfma16x16x64(xf[f], wf, acc[f][g]);
           }
         }
       }
