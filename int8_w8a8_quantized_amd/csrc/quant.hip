@@ -8,8 +8,8 @@
 // (§3-§4) and "vLLM INT8 W8A8 量化实战" (4.2) describe; static: one calibrated
 // scale (and zero point) for the whole tensor ("vLLM INT8 W8A8 量化实战" 4.1).
 //
-// Layout: TPR threads own one row (TPR = 64, 256 or 1024; several rows share a
-// 256-thread workgroup when TPR = 64). The row is read once with 16-byte
+// Layout: TPR threads own one row (TPR = 64, 256, 512 or 1024; several rows
+// share a 256-thread workgroup when TPR = 64). The row is read once with 16-byte
 // loads (8 bf16 per chunk, consecutive threads on consecutive chunks, so a
 // wave instruction moves 1 KiB of contiguous HBM), held in registers (CH
 // chunks per thread) while the extremes are reduced across lanes with DPP
@@ -204,9 +204,11 @@ static hipError_t launch_mode(const uint16_t* x, int64_t M, int64_t K, int64_t l
   // single round of waves on the chip at 8192 rows, which then load together
   // and compute together (8192 x 4096: 20 us at 4 waves per row against
   // 24 us at one, symmetric).
+  // (Decode rows, input from HBM, M = 1..64: K = 4096 takes 2.2-2.9 us at 512
+  // threads per row against 2.3-3.1 us at 256; K = 14336 is fastest at 1024.)
   int tpr;
   if (M <= 256)
-    tpr = nchunk <= 64 ? 64 : (nchunk <= 512 ? 256 : 1024);
+    tpr = nchunk <= 64 ? 64 : (nchunk <= 256 ? 256 : (nchunk <= 512 ? 512 : 1024));
   else
     tpr = nchunk <= 128 ? 64 : (nchunk <= 2048 ? 256 : 1024);
   const int ch = (int)((nchunk + tpr - 1) / tpr);  // <= 8 since K <= 65536
@@ -215,6 +217,9 @@ static hipError_t launch_mode(const uint16_t* x, int64_t M, int64_t K, int64_t l
                          ldq, s_x, zp);
   } else if (tpr == 256) {
     launch_tpr<MODE, 256>(ch, dim3((unsigned)M), stream, x, M, K, ldx, s_in, zp_in, xq, ldq, s_x,
+                          zp);
+  } else if (tpr == 512) {
+    launch_tpr<MODE, 512>(ch, dim3((unsigned)M), stream, x, M, K, ldx, s_in, zp_in, xq, ldq, s_x,
                           zp);
   } else {
     launch_tpr<MODE, 1024>(ch, dim3((unsigned)M), stream, x, M, K, ldx, s_in, zp_in, xq, ldq, s_x,
