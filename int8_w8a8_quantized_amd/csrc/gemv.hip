@@ -433,15 +433,25 @@ __global__ __launch_bounds__(256) void gemv_reduce_kernel(GemmArgs a, int splits
   const int64_t n = rb * 16 * W + 16 * wave + (lane & 15);
   const int64_t m = 16 * f + 4 * (lane >> 4) + r;
   if (n >= a.N || m >= a.M) return;
-  const int32_t* src = part + (rb * splits * W + wave) * PER + pe;
-  int v = 0;
-  for (int s = 0; s < splits; ++s) v += src[(int64_t)s * W * PER];
+  // the epilogue operands go out first, so their round trip overlaps the
+  // partial tiles' instead of following it
   EpiRow er;
   er.ok = true;
   er.out_row = m;
   er.sx = a.s_x[a.sx_per_token ? m : 0];
-  er.zp = (a.azp_mode == 1) ? a.zp[m] : 0;
-  epilogue_store(a, er, load_col(a, n, a.s_w, a.bias), n, v);
+  er.zp = *(a.azp_mode == 1 ? a.zp + m : reinterpret_cast<const int32_t*>(a.s_x));
+  const EpiCol col = load_col(a, n, a.s_w, a.bias);
+  const int32_t* src = part + (rb * splits * W + wave) * PER + pe;
+  int32_t pv[8];
+  int v = 0;
+  for (int s0 = 0; s0 < splits; s0 += 8) {  // splits <= 8 in practice: one batch of loads
+    // ranges past the last one reload it (a valid address) and are not added
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pv[j] = src[(int64_t)min(s0 + j, splits - 1) * W * PER];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v += (s0 + j < splits) ? pv[j] : 0;
+  }
+  epilogue_store(a, er, col, n, v);
 }
 
 // ------------------------------------------------------------- general kernel
