@@ -64,10 +64,43 @@ struct TileLoc {
   int64_t expert;              // -1: no work for this workgroup
 };
 
+// One block of 64 experts of the grouped tile scan (lane l: expert base + l):
+// the clamped segment [s0, s1), its tile count span and the running tile
+// count cum (inclusive), continuing from the previous block's carries.
+struct ExpertScan {
+  int64_t s0, s1, span, cum;
+};
+template <int BM>
+__device__ __forceinline__ ExpertScan scan_experts(const GemmArgs& a, int64_t base, int64_t carry_s0,
+                                                   int64_t carry_cum, int tiles_n) {
+  const int64_t T = a.M;
+  const int lane = threadIdx.x & 63;
+  const int64_t e = base + lane;
+  const bool live = e < a.E;
+  ExpertScan r;
+  r.s0 = live ? (int64_t)a.expert_offsets[e] : T;
+  const int64_t raw1 = live ? (int64_t)a.expert_offsets[e + 1] : T;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t v = __shfl_up(r.s0, o, 64);
+    if (lane >= o) r.s0 = max(r.s0, v);
+  }
+  r.s0 = min(max(r.s0, carry_s0), T);
+  r.s1 = min(max(raw1, r.s0), T);
+  r.span = live ? ((r.s1 - r.s0 + BM - 1) / BM) * tiles_n : 0;
+  r.cum = r.span;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t v = __shfl_up(r.cum, o, 64);
+    if (lane >= o) r.cum += v;
+  }
+  r.cum += carry_cum;
+  return r;
+}
+
 template <int BM, int BN, bool GROUPED>
 __device__ __forceinline__ TileLoc locate_tile(const GemmArgs& a, int tiles_m, int tiles_n) {
   TileLoc t;
-  const int pid = xcd_remap(blockIdx.x, gridDim.x);
   if (GROUPED) {
     // expert by expert; within an expert, n-tile by n-tile with its m-tiles
     // consecutive, so the workgroups that share a weight tile run together on
@@ -76,37 +109,34 @@ __device__ __forceinline__ TileLoc locate_tile(const GemmArgs& a, int tiles_m, i
     // segment starts are a running max of the offsets (capped at T), each
     // expert's tile count a running sum, and the expert holding tile `pid` is
     // the lowest lane whose running range contains it.
+    // The grid is sized for the most tiles any routing can need; the real
+    // count R is known only here. The first R workgroups take the tiles (so
+    // every XCD gets an equal share of them: the hardware deals workgroups to
+    // the XCDs round-robin), the rest have no work.
     t.n_begin = 0;
     t.expert = -1;
     t.row_begin = t.row_end = 0;
-    const int64_t T = a.M;
+    int64_t total = 0;
+    {
+      int64_t carry_s0 = 0;
+      for (int64_t base = 0; base < a.E; base += 64) {
+        const ExpertScan r = scan_experts<BM>(a, base, carry_s0, total, tiles_n);
+        carry_s0 = __shfl(r.s0, 63, 64);
+        total = __shfl(r.cum, 63, 64);
+      }
+    }
+    if ((int64_t)blockIdx.x >= total) return t;
+    const int pid = xcd_remap(blockIdx.x, (int)total);
     const int lane = threadIdx.x & 63;
     int64_t carry_s0 = 0, carry_cum = 0;
     for (int64_t base = 0; base < a.E; base += 64) {
-      const int64_t e = base + lane;
-      const bool live = e < a.E;
-      int64_t s0 = live ? (int64_t)a.expert_offsets[e] : T;
-      const int64_t raw1 = live ? (int64_t)a.expert_offsets[e + 1] : T;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int64_t v = __shfl_up(s0, o, 64);
-        if (lane >= o) s0 = max(s0, v);
-      }
-      s0 = min(max(s0, carry_s0), T);
-      const int64_t s1 = min(max(raw1, s0), T);
-      const int64_t span = live ? ((s1 - s0 + BM - 1) / BM) * tiles_n : 0;
-      int64_t cum = span;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int64_t v = __shfl_up(cum, o, 64);
-        if (lane >= o) cum += v;
-      }
-      cum += carry_cum;
-      const uint64_t hit = __ballot(live && pid >= cum - span && pid < cum);
+      const ExpertScan r = scan_experts<BM>(a, base, carry_s0, carry_cum, tiles_n);
+      const bool live = base + lane < a.E;
+      const uint64_t hit = __ballot(live && pid >= r.cum - r.span && pid < r.cum);
       if (hit) {
         const int src = __builtin_ctzll(hit);
-        const int64_t e_s0 = __shfl(s0, src, 64), e_s1 = __shfl(s1, src, 64);
-        const int64_t e_first = __shfl(cum - span, src, 64);
+        const int64_t e_s0 = __shfl(r.s0, src, 64), e_s1 = __shfl(r.s1, src, 64);
+        const int64_t e_first = __shfl(r.cum - r.span, src, 64);
         const int64_t t_e = (e_s1 - e_s0 + BM - 1) / BM;
         const int64_t local = pid - e_first;
         t.expert = base + src;
@@ -115,10 +145,11 @@ __device__ __forceinline__ TileLoc locate_tile(const GemmArgs& a, int tiles_m, i
         t.n_begin = (local / t_e) * BN;
         break;
       }
-      carry_s0 = __shfl(s0, 63, 64);
-      carry_cum = __shfl(cum, 63, 64);
+      carry_s0 = __shfl(r.s0, 63, 64);
+      carry_cum = __shfl(r.cum, 63, 64);
     }
   } else {
+    const int pid = xcd_remap(blockIdx.x, gridDim.x);
     constexpr int GM = 8;
     const int group = pid / (GM * tiles_n);
     const int first_m = group * GM;
