@@ -232,12 +232,18 @@ __device__ __forceinline__ EpiFetch epilogue_fetch(const GemmArgs& a, const Tile
 }
 
 // MASKED: rows may read as all zeros (gathered rows). OUT_I32: int32
-// output, else bf16. AZP: 0 none, 1 per-token, 2 static,
-// 3 either (read from the tables). FULL: every row of the tile and every
-// column of the wave's sub-tile is inside the output and ldo allows 8- /
-// 16-byte stores; the passes then carry no predicate, so the compiler is
-// free to run the LDS reads of later passes ahead of earlier stores.
-template <int BM, int BN, bool MASKED, bool OUT_I32, int AZP, bool FULL>
+// output, else bf16. AZP: 0 none, 1 per-token, 2 static, 3 either (read
+// from the tables). ST, the store form: per-element stores with row and
+// column checks (kStoreScalar); 16-byte (int32) / 8-byte (bf16) stores of
+// 4-column groups under a per-row check, when every column of the wave's
+// sub-tile is inside the output and ldo allows them (kStoreVecRows: the
+// last m-tile of an expert, a ragged M); the same with no check when every
+// row is inside too (kStoreVec: the passes then carry no predicate, so the
+// compiler is free to run the LDS reads of later passes ahead of earlier
+// stores).
+enum { kStoreScalar = 0, kStoreVecRows = 1, kStoreVec = 2 };
+
+template <int BM, int BN, bool MASKED, bool OUT_I32, int AZP, int ST>
 __device__ __forceinline__ void epilogue_store_tile(const GemmArgs& a, const TileLoc& t, int8_t* smem,
                                                     i32x16 (&acc)[BM / 64][BN / 64]) {
   constexpr int TM = BM / 2, TN = BN / 2, FM = TM / 32, FN = TN / 32;
@@ -308,11 +314,13 @@ __device__ __forceinline__ void epilogue_store_tile(const GemmArgs& a, const Til
         if (AZP == 2 || AZP == 3) c[k] -= adj8[k];
       }
       OutT* o = o_lane + (int64_t)dr * a.ldo;
-      const bool row_ok = FULL || t.row_begin + lrow0 + dr < t.row_end;
+      const bool row_ok = ST == kStoreVec || t.row_begin + lrow0 + dr < t.row_end;
       if (OUT_I32) {
-        if (FULL) {
-          *reinterpret_cast<int4*>(o) = make_int4(c[0], c[1], c[2], c[3]);
-          *reinterpret_cast<int4*>(o + TN / 2) = make_int4(c[4], c[5], c[6], c[7]);
+        if (ST != kStoreScalar) {
+          if (row_ok) {
+            *reinterpret_cast<int4*>(o) = make_int4(c[0], c[1], c[2], c[3]);
+            *reinterpret_cast<int4*>(o + TN / 2) = make_int4(c[4], c[5], c[6], c[7]);
+          }
         } else if (row_ok) {
 #pragma unroll
           for (int k = 0; k < 8; ++k)
@@ -327,9 +335,11 @@ __device__ __forceinline__ void epilogue_store_tile(const GemmArgs& a, const Til
           const float y1 = __builtin_fmaf((float)c[k + 1] * sx, sw8[k + 1], bias8[k + 1]);
           h[k / 2] = pack_bf16x2(y0, y1);
         }
-        if (FULL) {
-          *reinterpret_cast<uint2*>(o) = make_uint2(h[0], h[1]);
-          *reinterpret_cast<uint2*>(o + TN / 2) = make_uint2(h[2], h[3]);
+        if (ST != kStoreScalar) {
+          if (row_ok) {
+            *reinterpret_cast<uint2*>(o) = make_uint2(h[0], h[1]);
+            *reinterpret_cast<uint2*>(o + TN / 2) = make_uint2(h[2], h[3]);
+          }
         } else if (row_ok) {
 #pragma unroll
           for (int k = 0; k < 8; ++k)
@@ -338,6 +348,20 @@ __device__ __forceinline__ void epilogue_store_tile(const GemmArgs& a, const Til
         }
       }
     }
+  }
+}
+
+template <int BM, int BN, bool GROUPED, int ST>
+__device__ __forceinline__ void epilogue_dispatch(const GemmArgs& a, const TileLoc& t, int8_t* smem,
+                                                  i32x16 (&acc)[BM / 64][BN / 64]) {
+  if (a.out_i32) {
+    if (a.azp_mode == 1) epilogue_store_tile<BM, BN, GROUPED, true, 1, ST>(a, t, smem, acc);
+    else if (a.azp_mode == 2) epilogue_store_tile<BM, BN, GROUPED, true, 2, ST>(a, t, smem, acc);
+    else epilogue_store_tile<BM, BN, GROUPED, true, 0, ST>(a, t, smem, acc);
+  } else {
+    if (a.azp_mode == 1) epilogue_store_tile<BM, BN, GROUPED, false, 1, ST>(a, t, smem, acc);
+    else if (a.azp_mode == 2) epilogue_store_tile<BM, BN, GROUPED, false, 2, ST>(a, t, smem, acc);
+    else epilogue_store_tile<BM, BN, GROUPED, false, 0, ST>(a, t, smem, acc);
   }
 }
 
@@ -362,19 +386,18 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const TileLoc& 
   // the tables are visible to every wave; no wait for global stores
   __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   const int wn = (threadIdx.x >> 6) & 1;
-  // groups of 4 columns leave as 16-byte (int32) or 8-byte (bf16) stores
-  const bool full = t.n_begin + (wn + 1) * TN <= a.N && a.ldo % 4 == 0 && t.row_begin + BM <= t.row_end;
-  if (!full) {
-    if (a.out_i32) epilogue_store_tile<BM, BN, GROUPED, true, 3, false>(a, t, smem, acc);
-    else epilogue_store_tile<BM, BN, GROUPED, false, 3, false>(a, t, smem, acc);
-  } else if (a.out_i32) {
-    if (a.azp_mode == 1) epilogue_store_tile<BM, BN, GROUPED, true, 1, true>(a, t, smem, acc);
-    else if (a.azp_mode == 2) epilogue_store_tile<BM, BN, GROUPED, true, 2, true>(a, t, smem, acc);
-    else epilogue_store_tile<BM, BN, GROUPED, true, 0, true>(a, t, smem, acc);
+  // groups of 4 columns leave as 16-byte (int32) or 8-byte (bf16) stores when
+  // the wave's columns are all inside the output; rows past the tile's end
+  // (the last m-tile of an expert, a ragged M) only switch those stores off
+  const bool vec = t.n_begin + (wn + 1) * TN <= a.N && a.ldo % 4 == 0;
+  const bool rows = t.row_begin + BM <= t.row_end;
+  if (!vec) {
+    if (a.out_i32) epilogue_store_tile<BM, BN, GROUPED, true, 3, kStoreScalar>(a, t, smem, acc);
+    else epilogue_store_tile<BM, BN, GROUPED, false, 3, kStoreScalar>(a, t, smem, acc);
+  } else if (rows) {
+    epilogue_dispatch<BM, BN, GROUPED, kStoreVec>(a, t, smem, acc);
   } else {
-    if (a.azp_mode == 1) epilogue_store_tile<BM, BN, GROUPED, false, 1, true>(a, t, smem, acc);
-    else if (a.azp_mode == 2) epilogue_store_tile<BM, BN, GROUPED, false, 2, true>(a, t, smem, acc);
-    else epilogue_store_tile<BM, BN, GROUPED, false, 0, true>(a, t, smem, acc);
+    epilogue_dispatch<BM, BN, GROUPED, kStoreVecRows>(a, t, smem, acc);
   }
 }
 
