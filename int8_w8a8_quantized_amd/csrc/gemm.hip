@@ -64,37 +64,49 @@ struct TileLoc {
   int64_t expert;              // -1: no work for this workgroup
 };
 
+// Inclusive prefix (sum or maximum) over the 64 lanes of a wave by DPP row
+// shifts (1, 2, 4, 8 within each row of 16 lanes) and row broadcasts (lane
+// 15 into rows 1 and 3, lane 31 into rows 2 and 3). Lanes with no source take
+// the identity 0, so the maximum is over values >= 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_src(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, false);
+}
+template <bool MAX>
+__device__ __forceinline__ int wave_prefix(int v) {
+  auto op = [](int a, int b) { return MAX ? max(a, b) : a + b; };
+  v = op(v, dpp_src<0x111, 0xF>(v));  // row_shr:1
+  v = op(v, dpp_src<0x112, 0xF>(v));  // row_shr:2
+  v = op(v, dpp_src<0x114, 0xF>(v));  // row_shr:4
+  v = op(v, dpp_src<0x118, 0xF>(v));  // row_shr:8
+  v = op(v, dpp_src<0x142, 0xA>(v));  // row_bcast:15
+  v = op(v, dpp_src<0x143, 0xC>(v));  // row_bcast:31
+  return v;
+}
+__device__ __forceinline__ int lane_value(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
+
 // One block of 64 experts of the grouped tile scan (lane l: expert base + l):
 // the clamped segment [s0, s1), its tile count span and the running tile
-// count cum (inclusive), continuing from the previous block's carries.
+// count cum (inclusive), continuing from the previous block's carries. Row
+// counts fit 32 bits (T < 2^26) and tile counts too (< 2^24, both checked on
+// the host).
 struct ExpertScan {
-  int64_t s0, s1, span, cum;
+  int s0, s1, span, cum;
 };
 template <int BM>
-__device__ __forceinline__ ExpertScan scan_experts(const GemmArgs& a, int64_t base, int64_t carry_s0,
-                                                   int64_t carry_cum, int tiles_n) {
-  const int64_t T = a.M;
+__device__ __forceinline__ ExpertScan scan_experts(const GemmArgs& a, int64_t base, int carry_s0,
+                                                   int carry_cum, int tiles_n) {
+  const int T = (int)a.M;
   const int lane = threadIdx.x & 63;
   const int64_t e = base + lane;
   const bool live = e < a.E;
   ExpertScan r;
-  r.s0 = live ? (int64_t)a.expert_offsets[e] : T;
-  const int64_t raw1 = live ? (int64_t)a.expert_offsets[e + 1] : T;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int64_t v = __shfl_up(r.s0, o, 64);
-    if (lane >= o) r.s0 = max(r.s0, v);
-  }
-  r.s0 = min(max(r.s0, carry_s0), T);
+  const int raw0 = live ? a.expert_offsets[e] : T;
+  const int raw1 = live ? a.expert_offsets[e + 1] : T;
+  r.s0 = min(max(wave_prefix<true>(max(raw0, 0)), carry_s0), T);
   r.s1 = min(max(raw1, r.s0), T);
   r.span = live ? ((r.s1 - r.s0 + BM - 1) / BM) * tiles_n : 0;
-  r.cum = r.span;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int64_t v = __shfl_up(r.cum, o, 64);
-    if (lane >= o) r.cum += v;
-  }
-  r.cum += carry_cum;
+  r.cum = wave_prefix<false>(r.span) + carry_cum;
   return r;
 }
 
@@ -116,37 +128,37 @@ __device__ __forceinline__ TileLoc locate_tile(const GemmArgs& a, int tiles_m, i
     t.n_begin = 0;
     t.expert = -1;
     t.row_begin = t.row_end = 0;
-    int64_t total = 0;
+    int total = 0;
     {
-      int64_t carry_s0 = 0;
+      int carry_s0 = 0;
       for (int64_t base = 0; base < a.E; base += 64) {
         const ExpertScan r = scan_experts<BM>(a, base, carry_s0, total, tiles_n);
-        carry_s0 = __shfl(r.s0, 63, 64);
-        total = __shfl(r.cum, 63, 64);
+        carry_s0 = lane_value(r.s0, 63);
+        total = lane_value(r.cum, 63);
       }
     }
-    if ((int64_t)blockIdx.x >= total) return t;
-    const int pid = xcd_remap(blockIdx.x, (int)total);
+    if ((int)blockIdx.x >= total) return t;
+    const int pid = xcd_remap(blockIdx.x, total);
     const int lane = threadIdx.x & 63;
-    int64_t carry_s0 = 0, carry_cum = 0;
+    int carry_s0 = 0, carry_cum = 0;
     for (int64_t base = 0; base < a.E; base += 64) {
       const ExpertScan r = scan_experts<BM>(a, base, carry_s0, carry_cum, tiles_n);
       const bool live = base + lane < a.E;
       const uint64_t hit = __ballot(live && pid >= r.cum - r.span && pid < r.cum);
       if (hit) {
         const int src = __builtin_ctzll(hit);
-        const int64_t e_s0 = __shfl(r.s0, src, 64), e_s1 = __shfl(r.s1, src, 64);
-        const int64_t e_first = __shfl(r.cum - r.span, src, 64);
-        const int64_t t_e = (e_s1 - e_s0 + BM - 1) / BM;
-        const int64_t local = pid - e_first;
+        const int e_s0 = lane_value(r.s0, src), e_s1 = lane_value(r.s1, src);
+        const int e_first = lane_value(r.cum - r.span, src);
+        const int t_e = (e_s1 - e_s0 + BM - 1) / BM;
+        const int local = pid - e_first;
         t.expert = base + src;
-        t.row_begin = e_s0 + (local % t_e) * BM;
+        t.row_begin = e_s0 + (int64_t)(local % t_e) * BM;
         t.row_end = e_s1;
-        t.n_begin = (local / t_e) * BN;
+        t.n_begin = (int64_t)(local / t_e) * BN;
         break;
       }
-      carry_s0 = __shfl(r.s0, 63, 64);
-      carry_cum = __shfl(r.cum, 63, 64);
+      carry_s0 = lane_value(r.s0, 63);
+      carry_cum = lane_value(r.cum, 63);
     }
   } else {
     const int pid = xcd_remap(blockIdx.x, gridDim.x);

@@ -59,6 +59,8 @@ def _run(d, bias, out_dtype):
     ([1] * 40, 96, 64, 7),
     ([300, 513, 7, 0, 260], 640, 300, 1000),
     ([257, 0, 511], 192, 520, None),
+    ([(i * 37) % 11 for i in range(130)], 128, 96, None),  # three blocks of the 64-expert scan
+    ([0] * 64 + [5, 300], 64, 64, 20),                     # every row in the second block
 ])
 def test_grouped(counts, K, N, M_src):
     d = _case(counts, K, N, M_src)
