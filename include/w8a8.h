@@ -169,6 +169,20 @@ w8a8_status w8a8_prepare_requant_max(int8_t* W, int64_t N, int64_t K, int64_t ld
                                      const int64_t* logical_widths /* host */, int32_t P,
                                      float* s_max, int32_t* err_flag, void* stream);
 
+/* Expand the per-tensor scales of a fused weight's P row partitions (device
+ * part_scales [P], host logical_widths [P] summing to N) into per-output-
+ * channel scales s_w [N] (device): s_w[n] = part_scales[p] for the rows n of
+ * partition p. With s_w_per_channel = 1 the GEMM then applies each
+ * partition's own scale, so the fused weight needs no requantisation: the
+ * lossless alternative to w8a8_prepare_requant_max for the fused partitions
+ * that [SGLang] 핵심 코드 분석 §7 tracks through logical_widths (the page's
+ * is_channelwise flag, §4, selects the per-channel path). A scale that is
+ * not finite and > 0 sets W8A8_FLAG_BAD_SCALE in *err_flag (device int32,
+ * nullable). 1 <= P <= W8A8_MAX_PARTITIONS; zero-width partitions are legal. */
+w8a8_status w8a8_prepare_expand_scales(const float* part_scales,
+                                       const int64_t* logical_widths /* host */, int32_t P,
+                                       int64_t N, float* s_w, int32_t* err_flag, void* stream);
+
 /* Convert E FP8 E4M3FN weights W8 [E,N,K] (OCP encoding) with float block
  * scales S [E, ceil(N/128), ceil(K/128)] to per-row symmetric int8
  * ([Kunlun] 转换关系):

@@ -204,6 +204,31 @@ w8a8_status w8a8_prepare_requant_max(int8_t* W, int64_t N, int64_t K, int64_t ld
                     "requant_max launch");
 }
 
+w8a8_status w8a8_prepare_expand_scales(const float* part_scales, const int64_t* logical_widths,
+                                       int32_t P, int64_t N, float* s_w, int32_t* err_flag,
+                                       void* stream) {
+  w8a8_status st;
+  if ((st = check_dim(N, "N")) != W8A8_OK) return st;
+  W8A8_REQUIRE(P >= 1 && P <= W8A8_MAX_PARTITIONS, "P=%d outside [1, %d]", P, W8A8_MAX_PARTITIONS);
+  W8A8_REQUIRE(logical_widths != nullptr, "logical_widths must not be NULL");
+  w8a8::RequantParts parts{};
+  parts.P = P;
+  int64_t sum = 0;
+  for (int p = 0; p < P; ++p) {
+    W8A8_REQUIRE(logical_widths[p] >= 0, "logical_widths[%d]=%lld is negative", p, (long long)logical_widths[p]);
+    parts.row_start[p] = sum;
+    sum += logical_widths[p];
+  }
+  parts.row_start[P] = sum;
+  W8A8_REQUIRE(sum == N, "logical widths sum to %lld, not N=%lld", (long long)sum, (long long)N);
+  if (N == 0) return ok();
+  W8A8_REQUIRE(part_scales && s_w, "part_scales and s_w must not be NULL");
+  if ((st = check_current_device()) != W8A8_OK) return st;
+  return hip_status(w8a8::launch_expand_scales(part_scales, parts, N, s_w, err_flag,
+                                               static_cast<hipStream_t>(stream)),
+                    "expand_scales launch");
+}
+
 w8a8_status w8a8_prepare_fp8_block_to_int8(const uint8_t* W8, const float* S, int64_t E, int64_t N,
                                            int64_t K, int8_t* Wq, float* s, int32_t* err_flag,
                                            void* stream) {

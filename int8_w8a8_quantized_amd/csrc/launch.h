@@ -23,6 +23,9 @@ hipError_t launch_requant_max(int8_t* W, int64_t N, int64_t K, int64_t ldw,
                               const float* part_scales, const RequantParts& parts, float* s_max,
                               int32_t* err_flag, hipStream_t stream);
 
+hipError_t launch_expand_scales(const float* part_scales, const RequantParts& parts, int64_t N,
+                                float* s_w, int32_t* err_flag, hipStream_t stream);
+
 hipError_t launch_fp8_block_to_int8(const uint8_t* W8, const float* S, int64_t E, int64_t N,
                                     int64_t K, int8_t* Wq, float* s, int32_t* err_flag,
                                     hipStream_t stream);

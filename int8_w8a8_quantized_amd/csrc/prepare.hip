@@ -4,13 +4,14 @@
 //    times the static input zero point when one is given
 //    ("[SGLang] W4A8, W8A8, W4A4: 혼합 정밀도 양자화 스킴", 핵심 코드 분석 §4).
 //  * requantise a fused weight whose partitions carry their own per-tensor
-//    scales to the largest of them (same page, §7, requantize_with_max_scale).
+//    scales to the largest of them (same page, §7, requantize_with_max_scale),
+//    or expand those scales into per-channel ones (the lossless alternative).
 //  * FP8 E4M3FN with 128x128 block scales -> per-row absmax/127 int8
 //    ("MiniMax-M2.7 FP8 转昆仑芯 INT8", 转换关系): the block scale multiplies the
 //    decoded value, an all-zero row gives q = 0 and s = 1.
 //
-// All three stream the weight once from HBM with 16-byte loads; one wave owns
-// one row where a row reduction is needed.
+// The passes over a weight stream it once from HBM with 16-byte loads; one
+// wave owns one row where a row reduction is needed.
 
 #include "device_common.h"
 #include "launch.h"
@@ -38,6 +39,33 @@ hipError_t launch_colsum(const int8_t* W, int64_t N, int64_t K, int64_t ldw, con
                          int32_t* out, hipStream_t stream) {
   hipLaunchKernelGGL(colsum_kernel, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, stream, W, N, K,
                      ldw, zp_in, out);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------ per-channel scale expansion
+
+// Thread n writes the scale of the partition that holds row n.
+__global__ __launch_bounds__(256) void expand_scales_kernel(const float* __restrict__ part_scales,
+                                                            RequantParts parts, int64_t N,
+                                                            float* __restrict__ s_w,
+                                                            int32_t* __restrict__ err_flag) {
+  const int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (n == 0 && err_flag) {
+    bool bad = false;
+    for (int p = 0; p < parts.P; ++p) bad |= !(part_scales[p] > 0.0f && part_scales[p] <= 3.402823466e38f);
+    if (bad) atomicOr(err_flag, (int)2 /* W8A8_FLAG_BAD_SCALE */);
+  }
+  if (n >= N) return;
+  int p = 0;
+  while (p + 1 < parts.P && n >= parts.row_start[p + 1]) ++p;
+  s_w[n] = part_scales[p];
+}
+
+hipError_t launch_expand_scales(const float* part_scales, const RequantParts& parts, int64_t N,
+                                float* s_w, int32_t* err_flag, hipStream_t stream) {
+  const int64_t blocks = N > 0 ? (N + 255) / 256 : 1;  // one block checks the scales
+  hipLaunchKernelGGL(expand_scales_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, part_scales,
+                     parts, N, s_w, err_flag);
   return hipGetLastError();
 }
 

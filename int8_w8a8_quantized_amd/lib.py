@@ -48,6 +48,7 @@ _SIGS = {
     "w8a8_quantize_act": (_i32, [_p, _i64, _i64, _i64, _i32, _p, _p, _p, _i64, _p, _p, _p]),
     "w8a8_prepare_colsum": (_i32, [_p, _i64, _i64, _i64, _p, _p, _p]),
     "w8a8_prepare_requant_max": (_i32, [_p, _i64, _i64, _i64, _p, ctypes.POINTER(_i64), _i32, _p, _p, _p]),
+    "w8a8_prepare_expand_scales": (_i32, [_p, ctypes.POINTER(_i64), _i32, _i64, _p, _p, _p]),
     "w8a8_prepare_fp8_block_to_int8": (_i32, [_p, _p, _i64, _i64, _i64, _p, _p, _p, _p]),
     "w8a8_scaled_mm_workspace_size": (ctypes.c_size_t, [_i64, _i64, _i64]),
     "w8a8_scaled_mm_int8": (_i32, [_p, _i64, _i64, _i64, _p, _i64, _i64, _p, _i32, _p, _i32,
@@ -170,6 +171,19 @@ def prepare_requant_max(W, part_scales, logical_widths: Sequence[int], err_flag=
                                            len(logical_widths), _ptr(s_max), _ptr(err_flag), _stream()),
            "w8a8_prepare_requant_max")
     return s_max
+
+
+def prepare_expand_scales(part_scales, logical_widths: Sequence[int], err_flag=None, s_w=None):
+    """Per-channel scales float [N] from one scale per fused partition."""
+    import torch
+    N = int(sum(int(v) for v in logical_widths))
+    if s_w is None:
+        s_w = torch.empty(N, dtype=torch.float32, device=part_scales.device)
+    widths = (_i64 * len(logical_widths))(*[int(v) for v in logical_widths])
+    _raise(load().w8a8_prepare_expand_scales(_ptr(part_scales), widths, len(logical_widths), N,
+                                             _ptr(s_w), _ptr(err_flag), _stream()),
+           "w8a8_prepare_expand_scales")
+    return s_w
 
 
 def prepare_fp8_block_to_int8(W8, S, Wq=None, s=None, err_flag=None):

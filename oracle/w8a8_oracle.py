@@ -60,6 +60,7 @@ __all__ = [
     "epilogue_bf16",
     "scaled_mm",
     "requant_max",
+    "expand_scales",
     "e4m3fn_table",
     "fp8_block_to_int8",
     "grouped_scaled_mm",
@@ -310,6 +311,22 @@ def requant_max(w, part_scales, logical_widths):
         out[r0:r0 + width] = np.clip(np.rint(d / s_max), -128, 127).astype(np.int8)
         r0 += width
     return out, s_max
+
+
+def expand_scales(part_scales, logical_widths):
+    """Per-output-channel scales of a fused weight from its per-partition scales.
+
+    [SGLang] §7 tracks each partition's rows through logical_widths, and §4's
+    is_channelwise selects a per-channel weight scale; giving every row of
+    partition p the scale s_p keeps each partition's own dequantisation
+    W * s_p exactly (no requantisation to the largest scale):
+        s_w[n] = s_p  for the rows n of partition p.
+    Returns float32 [N].
+    """
+    ps = np.asarray(part_scales, dtype=np.float32)
+    widths = [int(v) for v in logical_widths]
+    assert len(widths) == ps.shape[0] and all(v >= 0 for v in widths)
+    return np.repeat(ps, widths).astype(np.float32)
 
 
 def e4m3fn_table() -> np.ndarray:

@@ -16,7 +16,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = W.header_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -132,6 +132,13 @@ def test_prepare_rejects_before_device_work(L):
     assert L.w8a8_prepare_requant_max(FAKE, 6144, 64, 64, FAKE, widths, 17, FAKE, None, None) == W.ERR_INVALID_ARG
     neg = (ctypes.c_int64 * 2)(-1, 6145)
     assert L.w8a8_prepare_requant_max(FAKE, 6144, 64, 64, FAKE, neg, 2, FAKE, None, None) == W.ERR_INVALID_ARG
+    assert L.w8a8_prepare_expand_scales(FAKE, widths, 3, 6000, FAKE, None, None) == W.ERR_INVALID_ARG
+    assert L.w8a8_prepare_expand_scales(FAKE, widths, 0, 6144, FAKE, None, None) == W.ERR_INVALID_ARG
+    assert L.w8a8_prepare_expand_scales(FAKE, widths, 17, 6144, FAKE, None, None) == W.ERR_INVALID_ARG
+    assert L.w8a8_prepare_expand_scales(FAKE, neg, 2, 6144, FAKE, None, None) == W.ERR_INVALID_ARG
+    assert L.w8a8_prepare_expand_scales(None, widths, 3, 6144, FAKE, None, None) == W.ERR_INVALID_ARG
+    zero = (ctypes.c_int64 * 2)(0, 0)
+    assert L.w8a8_prepare_expand_scales(None, zero, 2, 0, None, None, None) == W.OK
     assert L.w8a8_prepare_fp8_block_to_int8(FAKE, FAKE, 2, 64, 72, FAKE, FAKE, FAKE, None) == W.ERR_INVALID_ARG
     assert L.w8a8_prepare_fp8_block_to_int8(FAKE, FAKE, 2, 64, 64, FAKE, FAKE, None, None) == W.ERR_INVALID_ARG
     assert L.w8a8_prepare_fp8_block_to_int8(FAKE, FAKE, 0, 64, 64, FAKE, FAKE, FAKE, None) == W.OK

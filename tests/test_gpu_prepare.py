@@ -1,12 +1,13 @@
 """GPU parity of the weight-preparation calls: column sums, requantise to the
-max per-tensor scale, FP8 128x128-block -> per-row int8 (all bit-exact)."""
+max per-tensor scale or expand it per channel, FP8 128x128-block -> per-row
+int8 (all bit-exact)."""
 
 import numpy as np
 import pytest
 import torch
 
 import oracle as O
-from gpu_util import assert_equal, host, note, to_dev
+from gpu_util import assert_bf16_close, assert_equal, bf16_bits, host, note, to_dev
 from int8_w8a8_quantized_amd import lib as W
 from int8_w8a8_quantized_amd import synth
 
@@ -41,6 +42,39 @@ def test_requant_max(widths, K):
     assert_equal(host(wd), rw, "requantised weight")
     assert host(smax)[0] == rs
     assert host(flag)[0] == 0
+
+
+@pytest.mark.parametrize("widths", [(4096, 1024, 1024), (0, 5, 0, 3), (1,), tuple(range(16)), (300, 0)])
+def test_expand_scales(widths):
+    note(f"expand_scales widths={widths}")
+    rng = synth.rng_for(913, sum(widths), len(widths))
+    s = rng.uniform(1e-3, 1e-2, len(widths)).astype(np.float32)
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    got = W.prepare_expand_scales(to_dev(s), widths, err_flag=flag)
+    torch.cuda.synchronize()
+    assert_equal(host(got), O.expand_scales(s, widths), "per-channel scales")
+    assert host(flag)[0] == 0
+    bad = s.copy()
+    bad[-1] = -1.0
+    W.prepare_expand_scales(to_dev(bad), widths, err_flag=flag)
+    torch.cuda.synchronize()
+    assert host(flag)[0] & W.FLAG_BAD_SCALE
+
+
+def test_expand_scales_then_gemm():
+    """Static workload's fused QKV with its own per-partition scales, applied per channel."""
+    d = synth.static_qkv()
+    s_w = W.prepare_expand_scales(to_dev(d["part_scales"]), d["widths"])
+    M = 37
+    x = synth.rng_for(914, M, d["w"].shape[1]).integers(-128, 128, (M, d["w"].shape[1]), dtype=np.int8)
+    sx = np.full(M, 0.0173, np.float32)
+    out = W.scaled_mm_int8(to_dev(x), to_dev(d["w"]), to_dev(sx), s_w, out_dtype=W.OUT_I32)
+    outb = W.scaled_mm_int8(to_dev(x), to_dev(d["w"]), to_dev(sx), s_w)
+    torch.cuda.synchronize()
+    acc = O.int_gemm(x, d["w"])
+    assert_equal(host(out), acc, "accumulator")
+    want = O.epilogue_bf16(acc, sx, O.expand_scales(d["part_scales"], d["widths"]))
+    assert_bf16_close(bf16_bits(outb), want)
 
 
 def test_requant_bad_scale_flag():

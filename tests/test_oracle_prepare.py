@@ -1,5 +1,6 @@
 """Pins of the oracle's load-time weight preparation: column sums, requantise
-to the max per-tensor scale, and FP8 128x128-block -> per-row int8 (CPU only)."""
+to the max per-tensor scale or expand it per channel, and FP8 128x128-block ->
+per-row int8 (CPU only)."""
 
 from fractions import Fraction
 
@@ -33,6 +34,35 @@ def test_requant_identities():
     wq, smax = O.requant_max(w, s, [10, 20, 10])
     assert smax == np.float32(0.007)
     assert np.array_equal(wq[10:30], w[10:30])  # the max-scale partition is unchanged
+
+
+# ------------------------------------------------------ scale expansion
+
+def test_expand_scales_hand_example():
+    got = O.expand_scales(np.array([0.5, 0.25, 2.0, 3.0], np.float32), [2, 1, 0, 3])
+    assert got.dtype == np.float32 and list(got) == [0.5, 0.5, 0.25, 3.0, 3.0, 3.0]
+
+
+def test_expand_scales_brute_force_and_lossless():
+    rng = np.random.default_rng(5)
+    widths = [7, 0, 13, 1, 9]
+    s = rng.uniform(1e-3, 1e-2, len(widths)).astype(np.float32)
+    got = O.expand_scales(s, widths)
+    # row by row: the partition whose cumulative range holds the row
+    want, start = [], [0]
+    for v in widths:
+        start.append(start[-1] + v)
+    for n in range(sum(widths)):
+        p = max(i for i in range(len(widths)) if start[i] <= n < start[i + 1])
+        want.append(s[p])
+    assert np.array_equal(got, np.array(want, np.float32))
+    # every partition keeps its own dequantisation exactly; requantising to the
+    # largest scale does not
+    w = rng.integers(-128, 128, (sum(widths), 24), dtype=np.int8)
+    per_part = np.concatenate([w[start[p]:start[p + 1]].astype(np.float32) * s[p] for p in range(len(widths))])
+    assert np.array_equal(w.astype(np.float32) * got[:, None], per_part)
+    wq, smax = O.requant_max(w, s, widths)
+    assert not np.array_equal(wq.astype(np.float32) * smax, per_part)
 
 
 def test_requant_bound_and_brute_force():
