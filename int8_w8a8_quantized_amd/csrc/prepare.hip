@@ -307,7 +307,7 @@ __device__ __forceinline__ void fp8_row_convert(const uint8_t* __restrict__ W8, 
   }
 }
 
-template <int CH, int LPR>
+template <int CH, int LPR, int NS>
 __global__ __launch_bounds__(256) void fp8_rows_kernel(const uint8_t* __restrict__ W8,
                                                        const float* __restrict__ S, int64_t E,
                                                        int64_t N, int64_t K, int8_t* __restrict__ Wq,
@@ -318,18 +318,27 @@ __global__ __launch_bounds__(256) void fp8_rows_kernel(const uint8_t* __restrict
   const int64_t groups = (int64_t)gridDim.x * (256 / LPR);
   const int64_t rows = E * N;
   if (group >= rows) return;  // a whole row group leaves: the reductions stay inside groups
-  uint4 rawA[CH], rawB[CH];
-  float scA[CH], scB[CH];
-  // rows past the end are clamped to the last row for their (unused) loads
-  Fp8Row ra = fp8_row_load<CH, LPR>(W8, S, N, K, group, lane, rawA, scA);
-  for (int64_t row = group; row < rows; row += 2 * groups) {
-    const int64_t r1 = row + groups;
-    const Fp8Row rb = fp8_row_load<CH, LPR>(W8, S, N, K, r1 < rows ? r1 : rows - 1, lane, rawB, scB);
-    fp8_row_convert<CH, LPR>(W8, K, Wq, s_out, err_flag, ra, lane, rawA, scA);
-    if (r1 >= rows) break;
-    const int64_t r2 = row + 2 * groups;
-    ra = fp8_row_load<CH, LPR>(W8, S, N, K, r2 < rows ? r2 : rows - 1, lane, rawA, scA);
-    fp8_row_convert<CH, LPR>(W8, K, Wq, s_out, err_flag, rb, lane, rawB, scB);
+  // A ring of NS row slots: the group's rows are group, group + groups, ...;
+  // while one row is converted the next NS - 1 are in flight. Rows past the
+  // end are clamped to the last row for their (unused) loads.
+  uint4 raw[NS][CH];
+  float sc[NS][CH];
+  Fp8Row rr[NS];
+#pragma unroll
+  for (int t = 0; t < NS - 1; ++t) {
+    const int64_t r = group + t * groups;
+    rr[t] = fp8_row_load<CH, LPR>(W8, S, N, K, r < rows ? r : rows - 1, lane, raw[t], sc[t]);
+  }
+  for (int64_t base = group;; base += NS * groups) {
+#pragma unroll
+    for (int t = 0; t < NS; ++t) {
+      const int64_t cur = base + t * groups;
+      if (cur >= rows) return;
+      const int64_t nxt = cur + (NS - 1) * groups;
+      const int q = (t + NS - 1) % NS;
+      rr[q] = fp8_row_load<CH, LPR>(W8, S, N, K, nxt < rows ? nxt : rows - 1, lane, raw[q], sc[q]);
+      fp8_row_convert<CH, LPR>(W8, K, Wq, s_out, err_flag, rr[t], lane, raw[t], sc[t]);
+    }
   }
 }
 
@@ -376,6 +385,8 @@ __global__ __launch_bounds__(256) void fp8_rows_loop_kernel(const uint8_t* __res
   }
 }
 
+constexpr int kFp8Slots = 2;  // rows per lane group in the load ring
+
 hipError_t launch_fp8_block_to_int8(const uint8_t* W8, const float* S, int64_t E, int64_t N,
                                     int64_t K, int8_t* Wq, float* s, int32_t* err_flag,
                                     hipStream_t stream) {
@@ -393,7 +404,7 @@ hipError_t launch_fp8_block_to_int8(const uint8_t* W8, const float* S, int64_t E
     return (unsigned)(need < 256 * 6 ? need : 256 * 6);
   };
 #define W8A8_FP8(CHV, LPRV)                                                                         \
-  hipLaunchKernelGGL((fp8_rows_kernel<CHV, LPRV>), dim3(grid_for(LPRV)), block, 0, stream, W8, S, E, N, K, \
+  hipLaunchKernelGGL((fp8_rows_kernel<CHV, LPRV, kFp8Slots>), dim3(grid_for(LPRV)), block, 0, stream, W8, S, E, N, K, \
                      Wq, s, err_flag)
   if (half) {
     switch (ch32) {
