@@ -38,7 +38,9 @@
 // are then walked in groups of 8 tile-rows so that the workgroups running
 // together on one XCD share A and B tiles in its L2. The grouped variant maps
 // each workgroup to (expert, n-tile, m-tile of that expert's row range), m
-// fastest, by scanning expert_offsets; rows may be gathered through row_ids.
+// fastest, by scanning expert_offsets (only the first R workgroups have a
+// tile, R known on the device; they are the ones remapped across the XCDs);
+// rows may be gathered through row_ids.
 
 #include <type_traits>
 
