@@ -14,10 +14,9 @@
 // Main kernel, gemv_reg_kernel (K a multiple of 128): a workgroup of W waves
 // owns 16 * RG weight rows; the waves split K into interleaved 128-byte steps.
 // Each wave keeps a ring of U steps of loads in flight in registers: the
-// weight rows as whole lines (2 * RG instructions per step), and the
-// activation (2 * MF instructions; rows past M repeat row M - 1, so they cost
-// cache hits, not HBM): with one token block already in MFMA operand order,
-// with more as whole lines too. A step's lines go through a 2 KiB-per-16-rows
+// weight rows and the activation rows as whole lines (2 * RG and 2 * MF
+// instructions per step; activation rows past M repeat row M - 1, so they
+// cost cache hits, not HBM). A step's lines go through a 2 KiB-per-16-rows
 // LDS buffer of the wave to reach operand order (one 16-byte write and one
 // 16-byte read per lane per 8 rows; XOR-swizzled chunks keep both
 // conflict-free), then v_mfma_i32_16x16x64_i8 accumulates. At the end the
@@ -89,13 +88,11 @@ template <int MF, int RG, int W, int U>
 __global__ __launch_bounds__(W * 64) void gemv_reg_kernel(GemmArgs a) {
   constexpr int BN = 16 * RG, BK = 128;
   constexpr int PER = RG * MF * 256;  // accumulator ints of one wave
-  // Two or more token blocks: the activation also travels as whole lines and
-  // is transposed in LDS (16 * MF more rows in the wave's buffer). Its
-  // fragment-order loads (16 rows x 64 bytes per instruction) miss L1 at a
-  // third of the line rate, and with 16 weight rows per workgroup every CU
-  // reads the whole activation, M / 16 times the weight bytes.
-  constexpr bool XL = MF >= 2;
-  constexpr int XR = XL ? 16 * MF : 0;
+  // The activation travels as whole lines too and is transposed in LDS
+  // (16 * MF more rows in the wave's buffer): fragment-order loads (16 rows x
+  // 64 bytes per instruction) miss L1 at a third of the line rate, and with
+  // 16 weight rows per workgroup every CU reads the whole activation.
+  constexpr int XR = 16 * MF;
   constexpr int TB = (BN + XR) * BK;  // the wave's transpose buffer: weight rows, then token rows
   constexpr int SM = (W * TB > W * PER * 4) ? W * TB : W * PER * 4;
   constexpr int EP = (PER + W * 64 - 1) / (W * 64);
@@ -114,16 +111,13 @@ __global__ __launch_bounds__(W * 64) void gemv_reg_kernel(GemmArgs a) {
 #pragma unroll
   for (int h = 0; h < 2 * RG; ++h)
     wsrc[h] = a.B + gemv_min(n0 + 8 * h + (lane >> 3), a.N - 1) * a.ldb + (lane & 7) * 16;
-  // activation, 2 * MF instructions per step (rows past M repeat row M-1):
-  // XL: instruction h reads token rows 8h .. 8h+7 as whole lines (lane l: row
-  // 8h + l/8, bytes 16 (l%8) .. +15); otherwise instruction 2f + kb is the
-  // fragment of token block f, half step kb (lane l: token 16f + l%16,
-  // k-group l/16)
+  // activation lines, 2 * MF instructions per step: instruction h reads token
+  // rows 8h .. 8h+7 (lane l: row 8h + l/8, bytes 16 (l%8) .. +15); rows past
+  // M repeat row M-1
   const int8_t* asrc[2 * MF];
 #pragma unroll
   for (int h = 0; h < 2 * MF; ++h)
-    asrc[h] = XL ? a.A + gemv_min(8 * h + (lane >> 3), a.M - 1) * a.lda + (lane & 7) * 16
-                 : a.A + gemv_min(16 * (h >> 1) + (lane & 15), a.M - 1) * a.lda + 16 * (lane >> 4) + 64 * (h & 1);
+    asrc[h] = a.A + gemv_min(8 * h + (lane >> 3), a.M - 1) * a.lda + (lane & 7) * 16;
 
   GemvEpi<MF, EP> epi;
   epi.load(a, n0, tid, W * 64, PER);
@@ -154,8 +148,8 @@ __global__ __launch_bounds__(W * 64) void gemv_reg_kernel(GemmArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (i0 + u < nkw) {
-        // weight (and XL: token) lines -> operand order through the wave's
-        // LDS buffer (the wave's LDS accesses execute in order, so no wait is
+        // weight and token lines -> operand order through the wave's LDS
+        // buffer (the wave's LDS accesses execute in order, so no wait is
         // needed between this step's writes and reads, nor against the
         // previous step's reads)
 #pragma unroll
@@ -163,12 +157,10 @@ __global__ __launch_bounds__(W * 64) void gemv_reg_kernel(GemmArgs a) {
           const int row = 8 * h + (lane >> 3);
           *reinterpret_cast<u32x4*>(tb + row * BK + (((lane & 7) ^ gemv_swz(row)) * 16)) = wr[u][h];
         }
-        if (XL) {
 #pragma unroll
-          for (int h = 0; h < 2 * MF; ++h) {
-            const int row = BN + 8 * h + (lane >> 3);
-            *reinterpret_cast<u32x4*>(tb + row * BK + (((lane & 7) ^ gemv_swz(row)) * 16)) = ar[u][h];
-          }
+        for (int h = 0; h < 2 * MF; ++h) {
+          const int row = BN + 8 * h + (lane >> 3);
+          *reinterpret_cast<u32x4*>(tb + row * BK + (((lane & 7) ^ gemv_swz(row)) * 16)) = ar[u][h];
         }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -177,8 +169,7 @@ __global__ __launch_bounds__(W * 64) void gemv_reg_kernel(GemmArgs a) {
 #pragma unroll
           for (int f = 0; f < MF; ++f) {
             const int row = BN + 16 * f + (lane & 15);
-            xf[f] = XL ? *reinterpret_cast<const i32x4*>(tb + row * BK + ((c ^ gemv_swz(row)) * 16))
-                       : __builtin_bit_cast(i32x4, ar[u][2 * f + kb]);
+            xf[f] = *reinterpret_cast<const i32x4*>(tb + row * BK + ((c ^ gemv_swz(row)) * 16));
           }
 #pragma unroll
           for (int g = 0; g < RG; ++g) {
