@@ -23,12 +23,10 @@
 // waves' partial tiles are added in LDS and the epilogue, whose per-row /
 // per-column operands were loaded before the K loop, writes out.
 //
-// Direct-to-LDS kernel, gemv_dma_kernel (K a multiple of 128; used for M > 16
-// with many weight rows, where one workgroup's activation stage serves 64
-// weight rows): a workgroup of 4 waves owns 64 weight rows; weights and
-// activations travel HBM/L2 -> LDS with the direct-to-LDS load (8 rows x 128
-// bytes per instruction) into a ring of NS stages; wave w multiplies weight
-// rows 16w..16w+15 with all activation blocks.
+// Shared-activation kernel, gemv_shared_kernel (K a multiple of 128; M > 16
+// with many weight rows or a long K): a workgroup of 4 waves owns 64 weight
+// rows; one activation stage per K step serves all of them through LDS. With
+// a long K the workgroups take K ranges and a second kernel adds them.
 //
 // General kernel (any K that is a multiple of 16), gemv_i8_kernel: operands
 // go straight from memory into MFMA registers, as described above it.
@@ -39,15 +37,6 @@
 
 namespace w8a8 {
 
-typedef __attribute__((address_space(3))) void* lds_void_ptr_g;
-typedef __attribute__((address_space(1))) void* global_void_ptr_g;
-
-template <int N>
-__device__ __forceinline__ void gemv_wait_vmcnt() {
-  static_assert(N >= 0 && N <= 63, "vmcnt range");
-  __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-__device__ __forceinline__ void gemv_barrier() { __asm__ volatile("s_barrier" ::: "memory"); }
 __device__ __forceinline__ int64_t gemv_min(int64_t a, int64_t b) { return a < b ? a : b; }
 
 // Chunk position of logical 16-byte chunk c of an 8-chunk (128-byte) row r:
@@ -205,105 +194,8 @@ __global__ __launch_bounds__(W * 64) void gemv_reg_kernel(GemmArgs a) {
   }
 }
 
-// ------------------------------------------------------ direct-to-LDS kernel
-template <int MF, int NS>
-__global__ __launch_bounds__(256) void gemv_dma_kernel(GemmArgs a) {
-  constexpr int BN = 64, BK = 128;
-  constexpr int XR = MF * 16;                    // activation rows held in LDS
-  constexpr int STAGE = (BN + XR) * BK;
-  constexpr int NI = (BN + XR) / 8;              // 1-KiB load instructions per stage
-  constexpr int Q = (NI + 3) / 4;                // per wave (the last ones may repeat)
-  static_assert((NS - 2) * Q <= 63, "vmcnt range");
-  __shared__ __attribute__((aligned(1024))) int8_t smem[NS * STAGE];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t n0 = (int64_t)blockIdx.x * BN;
-  const int nk = (int)(a.K / BK);
-
-  // ---- DMA sources: instruction j (this wave's q-th) fills tile rows
-  // 8j..8j+7 (weights for j < BN/8, activations after); lane l writes row
-  // +l/8, physical chunk l%8, which holds logical chunk (l%8) ^ swz(row).
-  const int8_t* src[Q];
-  int dst[Q];
-#pragma unroll
-  for (int q = 0; q < Q; ++q) {
-    const int j = min(wave * Q + q, NI - 1);
-    const int trow = 8 * j + (lane >> 3);        // row within the stage
-    const int lch = (lane & 7) ^ gemv_swz(trow);
-    if (trow < BN) {
-      src[q] = a.B + gemv_min(n0 + trow, a.N - 1) * a.ldb + lch * 16;
-    } else {
-      const int64_t m = gemv_min(trow - BN, a.M - 1);  // rows past M repeat the last one
-      src[q] = a.A + m * a.lda + lch * 16;
-    }
-    dst[q] = j * 1024;
-  }
-  auto issue = [&](int kt_src, int kt_dst) __attribute__((always_inline)) {
-    int8_t* st = smem + (kt_dst % NS) * STAGE;
-    const int64_t k0 = (int64_t)kt_src * BK;
-#pragma unroll
-    for (int q = 0; q < Q; ++q)
-      __builtin_amdgcn_global_load_lds((global_void_ptr_g)(src[q] + k0), (lds_void_ptr_g)(st + dst[q]),
-                                       16, 0, 0);
-  };
-
-  // ---- epilogue operands (lane holds tokens 16f + 4*(lane/16) + r of
-  // weight row n0 + 16w + lane%16)
-  const int fr = lane & 15;
-  const int64_t n = n0 + 16 * wave + fr;
-  const EpiCol col = load_col(a, n, a.s_w, a.bias);
-  EpiRow er[MF][4];
-#pragma unroll
-  for (int f = 0; f < MF; ++f)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t m = 16 * f + 4 * (lane >> 4) + r;
-      er[f][r].ok = m < a.M;
-      const int64_t mm = er[f][r].ok ? m : 0;
-      er[f][r].out_row = mm;
-      er[f][r].sx = a.s_x[a.sx_per_token ? mm : 0];
-      er[f][r].zp = *(a.azp_mode == 1 ? a.zp + mm : reinterpret_cast<const int32_t*>(a.s_x));
-    }
-
-  // ---- fragments: wave w reads weight rows 16w + lane%16, activation rows
-  // 16f + lane%16, logical chunk 4*ks + lane/16
-  const int w_off = (16 * wave + fr) * BK;
-  const int w_sw = gemv_swz(16 * wave + fr);
-  i32x4 acc[MF];
-#pragma unroll
-  for (int f = 0; f < MF; ++f) acc[f] = i32x4{0, 0, 0, 0};
-
-  if (nk > 0) {
-#pragma unroll
-    for (int s = 0; s < NS - 1; ++s) issue(min(s, nk - 1), s);
-  }
-  for (int kt = 0; kt < nk; ++kt) {
-    gemv_wait_vmcnt<(NS - 2) * Q>();
-    gemv_barrier();  // stage kt has landed everywhere; stage kt-1 is retired
-    issue(min(kt + NS - 1, nk - 1), kt + NS - 1);  // past the end: a harmless reload
-    const int8_t* st = smem + (kt % NS) * STAGE;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int c = 4 * ks + (lane >> 4);
-      const i32x4 wf = *reinterpret_cast<const i32x4*>(st + w_off + ((c ^ w_sw) * 16));
-#pragma unroll
-      for (int f = 0; f < MF; ++f) {
-        const int xr = BN + 16 * f + fr;
-        const i32x4 xf = *reinterpret_cast<const i32x4*>(st + xr * BK + ((c ^ gemv_swz(xr)) * 16));
-        acc[f] = mfma16x16x64(xf, wf, acc[f]);
-      }
-    }
-  }
-  gemv_wait_vmcnt<0>();  // the trailing reloads land before the workgroup ends
-
-#pragma unroll
-  for (int f = 0; f < MF; ++f)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) epilogue_store(a, er[f][r], col, n, acc[f][r]);
-}
-
-// ---------------------------------------------- shared-activation split kernel
-// For M > 16 with a long K and few weight rows. The L1 fill of a CU (HBM and
+// ---------------------------------------------- shared-activation kernel
+// For M > 16 with many weight rows or a long K. The L1 fill of a CU (HBM and
 // L2 traffic together) is the limit there: the register kernel's 16-row
 // workgroups each read the whole activation, four times the weight bytes at
 // M = 64. Here the 4 waves of a workgroup own 16 weight rows each and walk
@@ -312,14 +204,15 @@ __global__ __launch_bounds__(256) void gemv_dma_kernel(GemmArgs a) {
 // weight rows: it is written to a double-buffered LDS stage and, after a
 // barrier, every wave reads its fragments there. Weight lines ride each
 // wave's register ring and LDS transpose as in the register kernel. K is cut
-// into `splits` ranges, one per workgroup; each workgroup stores its int32
-// tile in accumulator order (256 contiguous bytes per wave instruction) to
-// the caller's workspace, and gemv_reduce_kernel adds the ranges and applies
-// the epilogue. The stage buffer written at step i was last read at step
-// i - 2, before every wave passed the barrier of step i - 1.
+// into `splits` ranges, one per workgroup. With one range (DIRECT) the
+// epilogue runs in the kernel; otherwise each workgroup stores its int32 tile
+// in accumulator order (256 contiguous bytes per wave instruction) to the
+// caller's workspace, and gemv_reduce_kernel adds the ranges and applies the
+// epilogue. The stage buffer written at step i was last read at step i - 2,
+// before every wave passed the barrier of step i - 1.
 constexpr int kSharedWaves = 4;
 
-template <int MF, int U>
+template <int MF, int U, bool DIRECT>
 __global__ __launch_bounds__(kSharedWaves * 64) void gemv_shared_kernel(GemmArgs a, int splits,
                                                                         int steps_per_split,
                                                                         int32_t* __restrict__ part) {
@@ -351,6 +244,25 @@ __global__ __launch_bounds__(kSharedWaves * 64) void gemv_shared_kernel(GemmArgs
     const int row = 8 * j + (lane >> 3);
     asrc[q] = a.A + gemv_min(row, a.M - 1) * a.lda + (lane & 7) * 16;
     adst[q] = row * BK + (((lane & 7) ^ gemv_swz(row)) * 16);
+  }
+  // DIRECT (one K range): the epilogue's operands, loaded before the K loop
+  // (lane holds tokens 16f + 4*(lane/16) + r of weight row n0 + lane%16)
+  const int64_t n = n0 + (lane & 15);
+  EpiCol col;
+  EpiRow er[MF][4];
+  if (DIRECT) {
+    col = load_col(a, n, a.s_w, a.bias);
+#pragma unroll
+    for (int f = 0; f < MF; ++f)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t m = 16 * f + 4 * (lane >> 4) + r;
+        er[f][r].ok = m < a.M;
+        const int64_t mm = er[f][r].ok ? m : 0;
+        er[f][r].out_row = mm;
+        er[f][r].sx = a.s_x[a.sx_per_token ? mm : 0];
+        er[f][r].zp = *(a.azp_mode == 1 ? a.zp + mm : reinterpret_cast<const int32_t*>(a.s_x));
+      }
   }
   u32x4 wr[U][2], xr[U][AQ];
   // step j of this range into ring slot u; past the end: a reload of the last step
@@ -400,6 +312,13 @@ __global__ __launch_bounds__(kSharedWaves * 64) void gemv_shared_kernel(GemmArgs
       }
       issue(u, i + U);
     }
+  }
+  if (DIRECT) {
+#pragma unroll
+    for (int f = 0; f < MF; ++f)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) epilogue_store(a, er[f][r], col, n, acc[f][r]);
+    return;
   }
   // lane holds tokens 16f + 4*(lane/16) + r of weight row n0 + lane%16
   int32_t* dst = part + (((int64_t)rb * splits + sp) * W + wave) * PER + lane;
@@ -567,19 +486,24 @@ namespace {
 // rotated over 1 GiB:
 //  - M <= 16: the register kernel, 16 rows per workgroup; 4 waves split K,
 //    2 once there are 1024+ row groups (the waves then live long enough);
-//  - M > 16 with 16384+ weight rows: the direct-to-LDS kernel (one
-//    activation stage serves 64 weight rows);
+//  - M > 16 with 16384+ weight rows: the shared-activation kernel over the
+//    whole K with the epilogue in the kernel (its 64-row workgroups fill the
+//    chip; 4096 x 28672: 25.5 / 30.3 us at M = 32 / 64, where an LDS ring
+//    for the weights as well took 28.1 / 32.7);
 //  - M > 16, 64 steps of K or more and a workspace: the shared-activation
 //    kernel over about 256 workgroups (K ranges of at least 16 steps), then
 //    the reduction;
+//  - the shared kernel keeps 4 steps in flight per wave (14336 x 4096 with
+//    the reduction: 14.8 / 18.1 us at M = 32 / 64; 8 and 6 steps took
+//    16.9 / 20.4);
 //  - otherwise the register kernel, with 32 rows per workgroup when 16-row
 //    groups would need between one and two workgroups per CU (a half-empty
 //    second round costs more than the larger tile).
-enum class GemvKind { kReg, kDma, kShared, kGeneral };
+enum class GemvKind { kReg, kShared, kGeneral };
 struct GemvCfg {
   GemvKind kind;
-  int mf, rg, w, u;  // u: ring steps (register / shared kernels) or LDS stages (DMA kernel)
-  int splits;        // K ranges of the shared kernel
+  int mf, rg, w, u;  // u: ring steps in flight per wave
+  int splits;        // K ranges of the shared kernel (1: the epilogue runs in it)
 };
 
 int gemv_mf(int64_t M) { return (int)std::min<int64_t>((M + 15) / 16, 4); }
@@ -603,10 +527,9 @@ GemvCfg gemv_cfg(int64_t M, int64_t N, int64_t K, size_t ws_bytes) {
   if (K % 128 != 0) return {GemvKind::kGeneral, mf, 2, 4, 8, 1};
   const int64_t groups = (N + 15) / 16;
   if (mf == 1) return {GemvKind::kReg, 1, 1, groups >= 1024 ? 2 : 4, 4, 1};
-  if (N >= 16384) return {GemvKind::kDma, mf, 4, 4, mf == 2 ? 6 : 5, 1};
+  if (N >= 16384) return {GemvKind::kShared, mf, 1, kSharedWaves, 4, 1};
   const int s = shared_splits(M, N, K);
-  if (s > 0 && ws_bytes >= shared_workspace_bytes(M, N, s))
-    return {GemvKind::kShared, mf, 1, kSharedWaves, mf == 2 ? 8 : 6, s};
+  if (s > 0 && ws_bytes >= shared_workspace_bytes(M, N, s)) return {GemvKind::kShared, mf, 1, kSharedWaves, 4, s};
   if (groups > 256 && groups <= 512) return {GemvKind::kReg, mf, 2, 4, mf == 2 ? 4 : 3, 1};
   return {GemvKind::kReg, mf, 1, 4, 4, 1};
 }
@@ -618,19 +541,17 @@ hipError_t launch_reg(const GemmArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int MF, int NS>
-hipError_t launch_dma(const GemmArgs& a, hipStream_t stream) {
-  static_assert((64 + MF * 16) * 128 * NS <= 80 * 1024, "two workgroups per CU");
-  hipLaunchKernelGGL((gemv_dma_kernel<MF, NS>), dim3((unsigned)((a.N + 63) / 64)), dim3(256), 0, stream, a);
-  return hipGetLastError();
-}
-
 template <int MF, int U>
 hipError_t launch_shared(const GemmArgs& a, int splits, int32_t* part, hipStream_t stream) {
   const int64_t rbs = (a.N + 63) / 64;
   const int64_t nsteps = a.K / 128;
   const int sps = (int)((nsteps + splits - 1) / splits);
-  hipLaunchKernelGGL((gemv_shared_kernel<MF, U>), dim3((unsigned)(rbs * splits)), dim3(kSharedWaves * 64), 0,
+  if (splits == 1) {  // one K range: the epilogue runs in the kernel, no workspace
+    hipLaunchKernelGGL((gemv_shared_kernel<MF, U, true>), dim3((unsigned)rbs), dim3(kSharedWaves * 64), 0,
+                       stream, a, 1, sps, nullptr);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((gemv_shared_kernel<MF, U, false>), dim3((unsigned)(rbs * splits)), dim3(kSharedWaves * 64), 0,
                      stream, a, splits, sps, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -662,14 +583,12 @@ const char* decode_kernel_name(int64_t M, int64_t N, int64_t K, size_t ws_bytes)
                                    "gemv_i8_kernel<3, 2, 4, 8>", "gemv_i8_kernel<4, 2, 4, 8>"};
       return gen[c.mf - 1];
     }
-    case GemvKind::kDma: {
-      static const char* dma[3] = {"gemv_dma_kernel<2, 6>", "gemv_dma_kernel<3, 5>", "gemv_dma_kernel<4, 5>"};
-      return dma[c.mf - 2];
-    }
     case GemvKind::kShared: {
-      static const char* shr[3] = {"gemv_shared_kernel<2, 8>", "gemv_shared_kernel<3, 6>",
-                                   "gemv_shared_kernel<4, 6>"};
-      return shr[c.mf - 2];
+      static const char* split[3] = {"gemv_shared_kernel<2, 4, false>", "gemv_shared_kernel<3, 4, false>",
+                                     "gemv_shared_kernel<4, 4, false>"};
+      static const char* direct[3] = {"gemv_shared_kernel<2, 4, true>", "gemv_shared_kernel<3, 4, true>",
+                                      "gemv_shared_kernel<4, 4, true>"};
+      return c.splits == 1 ? direct[c.mf - 2] : split[c.mf - 2];
     }
     default: break;
   }
@@ -692,17 +611,11 @@ hipError_t launch_decode_mm(const GemmArgs& a, void* workspace, size_t ws_bytes,
         case 3: return launch_general<3>(a, stream);
         default: return launch_general<4>(a, stream);
       }
-    case GemvKind::kDma:
-      switch (c.mf) {
-        case 2: return launch_dma<2, 6>(a, stream);
-        case 3: return launch_dma<3, 5>(a, stream);
-        default: return launch_dma<4, 5>(a, stream);
-      }
     case GemvKind::kShared:
       switch (c.mf) {
-        case 2: return launch_shared<2, 8>(a, c.splits, part, stream);
-        case 3: return launch_shared<3, 6>(a, c.splits, part, stream);
-        default: return launch_shared<4, 6>(a, c.splits, part, stream);
+        case 2: return launch_shared<2, 4>(a, c.splits, part, stream);
+        case 3: return launch_shared<3, 4>(a, c.splits, part, stream);
+        default: return launch_shared<4, 4>(a, c.splits, part, stream);
       }
     default: break;
   }

@@ -134,13 +134,14 @@ DECODE_CASES = [
     (33, 2048, 6000, "gemv_reg_kernel<3, 2, 4, 3>"),
     (64, 4096, 4096, "gemv_reg_kernel<4, 1, 4, 4>"),
     (60, 4096, 6144, "gemv_reg_kernel<4, 2, 4, 3>"),
-    (20, 256, 16400, "gemv_dma_kernel<2, 6>"),
-    (40, 512, 16390, "gemv_dma_kernel<3, 5>"),
-    (64, 384, 16384, "gemv_dma_kernel<4, 5>"),
-    (64, 14336, 4096, "gemv_shared_kernel<4, 6>"),
-    (48, 8192, 1000, "gemv_shared_kernel<3, 6>"),
-    (17, 8192, 100, "gemv_shared_kernel<2, 8>"),
-    (30, 8320, 300, "gemv_shared_kernel<2, 8>"),
+    (20, 256, 16400, "gemv_shared_kernel<2, 4, true>"),
+    (40, 512, 16390, "gemv_shared_kernel<3, 4, true>"),
+    (64, 384, 16384, "gemv_shared_kernel<4, 4, true>"),
+    (33, 4096, 16391, "gemv_shared_kernel<3, 4, true>"),
+    (64, 14336, 4096, "gemv_shared_kernel<4, 4, false>"),
+    (48, 8192, 1000, "gemv_shared_kernel<3, 4, false>"),
+    (17, 8192, 100, "gemv_shared_kernel<2, 4, false>"),
+    (30, 8320, 300, "gemv_shared_kernel<2, 4, false>"),
     (3, 272, 64, "gemv_i8_kernel<1, 2, 4, 8>"),
     (64, 4112, 200, "gemv_i8_kernel<4, 2, 4, 8>"),
 ]
