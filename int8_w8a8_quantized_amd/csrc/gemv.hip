@@ -522,14 +522,31 @@ size_t shared_workspace_bytes(int64_t M, int64_t N, int splits) {
   return (size_t)splits * rbs * kSharedWaves * gemv_mf(M) * 256 * sizeof(int32_t);
 }
 
+// Every register-kernel instance the table below can choose:
+// (token blocks, row groups, waves, ring steps).
+#define W8A8_GEMV_REG_INSTANCES(X)                                                    \
+  X(1, 1, 4, 4) X(1, 1, 2, 4) X(1, 1, 8, 2) X(1, 2, 8, 2) X(2, 1, 4, 4) X(2, 1, 8, 1) \
+  X(2, 2, 4, 4) X(2, 2, 8, 1) X(3, 1, 4, 4) X(3, 1, 8, 1) X(3, 2, 4, 3) X(4, 1, 4, 4) \
+  X(4, 1, 8, 1) X(4, 2, 4, 3) X(4, 2, 8, 1)
+
 GemvCfg gemv_cfg(int64_t M, int64_t N, int64_t K, size_t ws_bytes) {
   const int mf = gemv_mf(M);
   if (K % 128 != 0) return {GemvKind::kGeneral, mf, 2, 4, 8, 1};
   const int64_t groups = (N + 15) / 16;
-  if (mf == 1) return {GemvKind::kReg, 1, 1, groups >= 1024 ? 2 : 4, 4, 1};
+  // A short K (at most 40 steps) over 256 - 512 row groups leaves one
+  // workgroup per CU: 8 waves with a shallower ring then beat 4 waves with a
+  // deep one (measured 0.4 - 1.4 us per launch at K = 4096 - 5120; with a
+  // longer K, or more or fewer groups, the 4-wave table is as fast or faster).
+  const bool short_k = K / 128 <= 40 && groups >= 256 && groups <= 512;
+  const int rg_short = groups > 256 ? 2 : 1;
+  if (mf == 1) {
+    if (short_k) return {GemvKind::kReg, 1, rg_short, 8, 2, 1};
+    return {GemvKind::kReg, 1, 1, groups >= 1024 ? 2 : 4, 4, 1};
+  }
   if (N >= 16384) return {GemvKind::kShared, mf, 1, kSharedWaves, 4, 1};
   const int s = shared_splits(M, N, K);
   if (s > 0 && ws_bytes >= shared_workspace_bytes(M, N, s)) return {GemvKind::kShared, mf, 1, kSharedWaves, 4, s};
+  if (short_k && !(mf == 3 && rg_short == 2)) return {GemvKind::kReg, mf, rg_short, 8, 1, 1};
   if (groups > 256 && groups <= 512) return {GemvKind::kReg, mf, 2, 4, mf == 2 ? 4 : 3, 1};
   return {GemvKind::kReg, mf, 1, 4, 4, 1};
 }
@@ -592,12 +609,11 @@ const char* decode_kernel_name(int64_t M, int64_t N, int64_t K, size_t ws_bytes)
     }
     default: break;
   }
-  if (c.mf == 1) return c.w == 2 ? "gemv_reg_kernel<1, 1, 2, 4>" : "gemv_reg_kernel<1, 1, 4, 4>";
-  static const char* reg1[3] = {"gemv_reg_kernel<2, 1, 4, 4>", "gemv_reg_kernel<3, 1, 4, 4>",
-                                "gemv_reg_kernel<4, 1, 4, 4>"};
-  static const char* reg2[3] = {"gemv_reg_kernel<2, 2, 4, 4>", "gemv_reg_kernel<3, 2, 4, 3>",
-                                "gemv_reg_kernel<4, 2, 4, 3>"};
-  return c.rg == 2 ? reg2[c.mf - 2] : reg1[c.mf - 2];
+#define W8A8_REG_NAME(MF, RG, W, U) \
+  if (c.mf == MF && c.rg == RG && c.w == W && c.u == U) return "gemv_reg_kernel<" #MF ", " #RG ", " #W ", " #U ">";
+  W8A8_GEMV_REG_INSTANCES(W8A8_REG_NAME)
+#undef W8A8_REG_NAME
+  return "unknown";
 }
 
 hipError_t launch_decode_mm(const GemmArgs& a, void* workspace, size_t ws_bytes, hipStream_t stream) {
@@ -619,12 +635,11 @@ hipError_t launch_decode_mm(const GemmArgs& a, void* workspace, size_t ws_bytes,
       }
     default: break;
   }
-  switch (c.mf) {
-    case 1: return c.w == 2 ? launch_reg<1, 1, 2, 4>(a, stream) : launch_reg<1, 1, 4, 4>(a, stream);
-    case 2: return c.rg == 2 ? launch_reg<2, 2, 4, 4>(a, stream) : launch_reg<2, 1, 4, 4>(a, stream);
-    case 3: return c.rg == 2 ? launch_reg<3, 2, 4, 3>(a, stream) : launch_reg<3, 1, 4, 4>(a, stream);
-    default: return c.rg == 2 ? launch_reg<4, 2, 4, 3>(a, stream) : launch_reg<4, 1, 4, 4>(a, stream);
-  }
+#define W8A8_REG_LAUNCH(MF, RG, W, U) \
+  if (c.mf == MF && c.rg == RG && c.w == W && c.u == U) return launch_reg<MF, RG, W, U>(a, stream);
+  W8A8_GEMV_REG_INSTANCES(W8A8_REG_LAUNCH)
+#undef W8A8_REG_LAUNCH
+  return hipErrorInvalidValue;  // not reached: the table picks only listed instances
 }
 
 }  // namespace w8a8

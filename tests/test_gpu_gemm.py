@@ -125,15 +125,22 @@ def test_empty():
 # Every decode (M <= 64) kernel instance, with ragged M and N, K = 128 (one
 # step: three of four waves hold no K), and K not a multiple of 128.
 DECODE_CASES = [
-    (1, 4096, 4096, "gemv_reg_kernel<1, 1, 4, 4>"),
+    (1, 14336, 4096, "gemv_reg_kernel<1, 1, 4, 4>"),
     (7, 128, 300, "gemv_reg_kernel<1, 1, 4, 4>"),
     (16, 4096, 16400, "gemv_reg_kernel<1, 1, 2, 4>"),
+    (1, 4096, 4096, "gemv_reg_kernel<1, 1, 8, 2>"),
+    (5, 2048, 5000, "gemv_reg_kernel<1, 2, 8, 2>"),
     (32, 1024, 200, "gemv_reg_kernel<2, 1, 4, 4>"),
-    (17, 4096, 4100, "gemv_reg_kernel<2, 2, 4, 4>"),
+    (32, 2048, 4096, "gemv_reg_kernel<2, 1, 8, 1>"),
+    (17, 6144, 4100, "gemv_reg_kernel<2, 2, 4, 4>"),
+    (17, 4096, 4100, "gemv_reg_kernel<2, 2, 8, 1>"),
     (48, 4096, 1000, "gemv_reg_kernel<3, 1, 4, 4>"),
+    (48, 1024, 4090, "gemv_reg_kernel<3, 1, 8, 1>"),
     (33, 2048, 6000, "gemv_reg_kernel<3, 2, 4, 3>"),
-    (64, 4096, 4096, "gemv_reg_kernel<4, 1, 4, 4>"),
-    (60, 4096, 6144, "gemv_reg_kernel<4, 2, 4, 3>"),
+    (64, 2048, 9000, "gemv_reg_kernel<4, 1, 4, 4>"),
+    (64, 4096, 4096, "gemv_reg_kernel<4, 1, 8, 1>"),
+    (64, 6144, 4200, "gemv_reg_kernel<4, 2, 4, 3>"),
+    (60, 4096, 6130, "gemv_reg_kernel<4, 2, 8, 1>"),
     (20, 256, 16400, "gemv_shared_kernel<2, 4, true>"),
     (40, 512, 16390, "gemv_shared_kernel<3, 4, true>"),
     (64, 384, 16384, "gemv_shared_kernel<4, 4, true>"),
