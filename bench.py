@@ -55,6 +55,28 @@ def gemm_bytes(M, K, N, bias=False, asym=False):
     return b
 
 
+def vendor_int32(torch, W, timer, xq, w, s_x, s_w, R):
+    """Context for the prefill figure: the plain int8 x int8 -> int32 product
+    (no epilogue) by this library and by PyTorch's own int8 matrix product
+    (hipBLASLt on ROCm) on the same codes, with whether the two agree."""
+    M, N = xq.shape[0], w.shape[0]
+    i32 = torch.empty((M, N), dtype=torch.int32, device=xq.device)
+    g = capture(torch, lambda: [W.scaled_mm_int8(xq, w, s_x, s_w, out_dtype=W.OUT_I32, out=i32)
+                                for _ in range(R)])
+    ours = timer.graph_us(g, R)
+    del g
+    res = {"us": round(ours, 1)}
+    try:
+        wt = w.t()
+        equal = bool(torch.equal(torch._int_mm(xq, wt), i32))
+        g = capture(torch, lambda: [torch._int_mm(xq, wt) for _ in range(R)])
+        res.update(torch_int_mm_us=round(timer.graph_us(g, R), 1), torch_int_mm_equal=equal)
+        del g
+    except (RuntimeError, AttributeError) as e:
+        res["torch_int_mm"] = f"unavailable: {type(e).__name__}"
+    return res
+
+
 def quant_bytes(M, K, asym=False):
     return 3 * M * K + 4 * M + (4 * M if asym else 0)
 
@@ -300,6 +322,7 @@ def main():
                                            "frac": round(tops / INT8_PEAK_TOPS, 4),
                                            "quant_us": round(qus, 1),
                                            "quant_GBs": round(quant_bytes(M, K, True) / (qus * 1e-6) / 1e9, 1)}
+                prefill[f"{M}x{K}x{N}"]["plain_int32"] = vendor_int32(torch, W, timer, xq, w, s_x, s_w, R)
                 del x, w, xq, out
         torch.cuda.synchronize()
 
