@@ -232,6 +232,29 @@ w8a8_status w8a8_scaled_mm_int8(const int8_t* xq, int64_t M, int64_t K, int64_t 
                                 int64_t ldo, void* workspace, size_t workspace_bytes,
                                 void* stream);
 
+/* The dynamic per-token symmetric linear layer in one call: w8a8_quantize_act
+ * (W8A8_QUANT_DYN_SYM) of x into xq / s_x, then w8a8_scaled_mm_int8 with
+ * s_x per token, no zero points and a bf16 out -- the per-token quantiser
+ * followed by the scaled GEMM of [SGLang] 핵심 코드 분석 §3, with the
+ * quantiser fused into the GEMM's prologue as the same page's data flow
+ * (quantise right before the GEMM) allows. Results are identical to the two
+ * calls: xq int8 [M,K] (ldq) and s_x float [M] are written as
+ * w8a8_quantize_act writes them (both caller-owned and required), out bf16
+ * [M,N] (ldo) as w8a8_scaled_mm_int8 writes it. For M <= 2, N <= 4096,
+ * K % 128 == 0 and M * K <= 16384 it is one kernel, in which every
+ * workgroup quantises the activation itself (where that measured faster
+ * than two launches); otherwise the two launches run in order on the
+ * stream. x bf16 [M,K] (ldx % 8 == 0), Wq int8 [N,K] (ldw % 16 == 0),
+ * s_w float [N] if s_w_per_channel else [1], bias bf16 [N] or NULL;
+ * workspace as for w8a8_scaled_mm_int8. Requires K % 16 == 0,
+ * 1 <= K <= W8A8_MAX_K, x/xq/Wq/out 16-byte aligned, ldq % 16 == 0. With
+ * N == 0 only xq and s_x are written. */
+w8a8_status w8a8_linear_dyn_sym(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                const int8_t* Wq, int64_t N, int64_t ldw, const float* s_w,
+                                int32_t s_w_per_channel, const uint16_t* bias, uint16_t* out,
+                                int64_t ldo, int8_t* xq, int64_t ldq, float* s_x, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 /* Grouped (MoE) scaled GEMM: the rows of the expert-sorted activation are
  * split by expert_offsets (device int32 [E+1], non-decreasing, [0] == 0,
  * [E] == T); rows [off[e], off[e+1]) take the symmetric scaled GEMM above
@@ -260,6 +283,12 @@ w8a8_status w8a8_grouped_scaled_mm_int8(const int8_t* xq, int64_t ldx, int64_t M
  * for an M x N x K problem (static storage; "" for an empty or invalid
  * shape). Profilers list kernels by these names; no device is touched. */
 const char* w8a8_scaled_mm_kernel_name(int64_t M, int64_t N, int64_t K);
+
+/* Name of the kernel that w8a8_linear_dyn_sym runs for the GEMM of an
+ * M x N x K problem: the fused kernel, or the one w8a8_scaled_mm_int8 runs
+ * after a separate quantiser launch (static storage; "" for an empty or
+ * invalid shape). No device is touched. */
+const char* w8a8_linear_dyn_sym_kernel_name(int64_t M, int64_t N, int64_t K);
 
 /* Human-readable name of a status code (static storage). */
 const char* w8a8_status_string(w8a8_status status);

@@ -307,6 +307,62 @@ w8a8_status w8a8_scaled_mm_int8(const int8_t* xq, int64_t M, int64_t K, int64_t 
   return hip_status(e, "scaled_mm launch");
 }
 
+w8a8_status w8a8_linear_dyn_sym(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const int8_t* Wq,
+                                int64_t N, int64_t ldw, const float* s_w, int32_t s_w_per_channel,
+                                const uint16_t* bias, uint16_t* out, int64_t ldo, int8_t* xq, int64_t ldq,
+                                float* s_x, void* workspace, size_t workspace_bytes, void* stream) {
+  w8a8_status st;
+  if ((st = check_dim(M, "M")) != W8A8_OK) return st;
+  if ((st = check_dim(N, "N")) != W8A8_OK) return st;
+  if ((st = check_k(K)) != W8A8_OK) return st;
+  if (M == 0) return ok();
+  W8A8_REQUIRE(x && xq && s_x, "x, xq and s_x must not be NULL");
+  W8A8_REQUIRE(aligned16(x) && aligned16(xq), "x and xq must be 16-byte aligned");
+  W8A8_REQUIRE(ldx >= K && ldx % 8 == 0, "ldx=%lld must be >= K and a multiple of 8", (long long)ldx);
+  W8A8_REQUIRE(ldq >= K && ldq % 16 == 0, "ldq=%lld must be >= K and a multiple of 16", (long long)ldq);
+  if (N > 0) {
+    if ((st = check_gemm_common(xq, ldq, Wq, K, out, W8A8_OUT_BF16, ldo, N)) != W8A8_OK) return st;
+    W8A8_REQUIRE(ldw >= K && ldw % 16 == 0, "ldw=%lld must be >= K and a multiple of 16", (long long)ldw);
+    W8A8_REQUIRE(s_w != nullptr, "s_w must not be NULL");
+    if ((st = check_tiles(M, 0, N)) != W8A8_OK) return st;
+  }
+  W8A8_REQUIRE(workspace == nullptr || aligned16(workspace), "workspace must be 16-byte aligned");
+  if ((st = check_current_device()) != W8A8_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  w8a8::GemmArgs a{};
+  a.A = xq;
+  a.lda = ldq;
+  a.B = Wq;
+  a.ldb = ldw;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.s_x = s_x;
+  a.sx_per_token = 1;
+  a.s_w = s_w;
+  a.sw_per_channel = s_w_per_channel != 0;
+  a.azp_mode = W8A8_AZP_NONE;
+  a.bias = bias;
+  a.out = out;
+  a.out_i32 = 0;
+  a.ldo = ldo;
+  if (w8a8::fused_linear_fits(M, N, K))
+    return hip_status(w8a8::launch_fused_linear(a, x, ldx, xq, ldq, s_x, s), "fused linear launch");
+  // otherwise the two launches, in order on the stream
+  hipError_t e = w8a8::launch_quantize_act(x, M, K, ldx, W8A8_QUANT_DYN_SYM, nullptr, nullptr, xq, ldq, s_x,
+                                           nullptr, s);
+  if (e != hipSuccess || N == 0) return hip_status(e, "quantize_act launch");
+  e = (M <= w8a8::kDecodeMaxM) ? w8a8::launch_decode_mm(a, workspace, workspace_bytes, s)
+                               : w8a8::launch_scaled_mm(a, s);
+  return hip_status(e, "scaled_mm launch");
+}
+
+const char* w8a8_linear_dyn_sym_kernel_name(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0) return "";
+  if (w8a8::fused_linear_fits(M, N, K)) return w8a8::fused_linear_kernel_name(M, N, K);
+  return w8a8_scaled_mm_kernel_name(M, N, K);
+}
+
 w8a8_status w8a8_grouped_scaled_mm_int8(const int8_t* xq, int64_t ldx, int64_t M_src, const int32_t* row_ids,
                                         const int32_t* expert_offsets, int64_t T, int64_t E, int64_t K,
                                         int64_t N, const int8_t* Wq, const float* s_x, const float* s_w,

@@ -34,6 +34,7 @@
 #include <algorithm>
 
 #include "gemm_common.h"
+#include "quant_common.h"
 
 namespace w8a8 {
 
@@ -478,6 +479,189 @@ __global__ __launch_bounds__(W * 64) void gemv_i8_kernel(GemmArgs a) {
   }
 }
 
+// ------------------------------------ fused activation quantisation
+// gemv_fused_kernel: the register kernel's weight stream (M = 1 token block)
+// on an activation the workgroup quantises itself, per token and symmetric,
+// so one launch does the work of the quantiser and the decode GEMM. It
+// serves M <= kFusedRows and M * K <= kFusedElems: each thread loads its
+// share of the bf16 rows (at most kFusedElems / 8 / threads 16-byte chunks);
+// the rows' absmax is reduced over the workgroup and each chunk is encoded by
+// the quantiser's own code path (identical codes and scales). The codes stay
+// in LDS for the whole K loop, rows padded by 16 bytes so the fragment reads
+// of the two rows fall in different banks. Every workgroup reads the same
+// bf16 rows (cache hits after the first) and computes the same codes;
+// workgroup 0 also writes them and the scales out. The prologue is paid by
+// every workgroup before its K loop can start, so the launch table uses this
+// kernel only where that costs less than a separate quantiser launch.
+constexpr int kFusedRows = 2;
+constexpr int kFusedElems = 16384;
+
+template <int RG, int W, int U>
+__global__ __launch_bounds__(W * 64) void gemv_fused_kernel(GemmArgs a, const uint16_t* __restrict__ x,
+                                                            int64_t ldx, int8_t* __restrict__ xq,
+                                                            int64_t ldq, float* __restrict__ sx) {
+  constexpr int BN = 16 * RG, BK = 128, NT = W * 64;
+  constexpr int PER = RG * 256;  // accumulator ints of one wave
+  constexpr int TB = BN * BK;    // the wave's weight transpose buffer
+  constexpr int SM = (W * TB > W * PER * 4) ? W * TB : W * PER * 4;
+  constexpr int EP = (PER + NT - 1) / NT;
+  constexpr int CHX = kFusedElems / 8 / NT;  // activation chunks per thread, at most
+  __shared__ __attribute__((aligned(1024))) int8_t smem[SM];
+  __shared__ __attribute__((aligned(16))) int8_t xs[kFusedElems + 16 * kFusedRows];
+  __shared__ float red_max[kFusedRows][W];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t n0 = (int64_t)blockIdx.x * BN;
+  const int M = (int)a.M, K = (int)a.K;
+  const int kc = K >> 3;        // 16-byte chunks per row
+  const int xst = K + 16;       // LDS row stride of the codes
+  const int nsteps = K / BK;
+  const int nkw = nsteps > wave ? (nsteps - wave + W - 1) / W : 0;
+  int8_t* tb = smem + wave * TB;
+
+  // the activation chunks: chunk j = c * NT + tid of the M x kc grid, row
+  // j / kc (M <= 2: one comparison); chunks past the grid read chunk 0
+  uint4 xv[CHX];
+#pragma unroll
+  for (int c = 0; c < CHX; ++c) {
+    const int j0 = c * NT + tid;
+    const int j = j0 < M * kc ? j0 : 0;
+    const int m = j >= kc;
+    xv[c] = ld16(x + (int64_t)m * ldx + (int64_t)(j - m * kc) * 8);
+  }
+  // per-row absmax over the workgroup
+  float am[kFusedRows] = {0.0f, 0.0f};
+#pragma unroll
+  for (int c = 0; c < CHX; ++c) {
+    const int j = c * NT + tid;
+    const int m = j >= kc;
+    float v = 0.0f;
+    absmax8(xv[c], v);
+    const bool in = j < M * kc;
+#pragma unroll
+    for (int r = 0; r < kFusedRows; ++r) am[r] = (in && m == r) ? max_ieee(am[r], v) : am[r];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // The weight ring goes out once this thread's activation chunks have
+  // arrived: issued first, the activation loads would queue behind every
+  // CU's weight loads. The ring then overlaps the reductions, the encoding
+  // and the two barriers.
+  // the weight ring, as in the register kernel (rows past N repeat row N-1)
+  const int8_t* wsrc[2 * RG];
+#pragma unroll
+  for (int h = 0; h < 2 * RG; ++h)
+    wsrc[h] = a.B + gemv_min(n0 + 8 * h + (lane >> 3), a.N - 1) * a.ldb + (lane & 7) * 16;
+  u32x4 wr[U][2 * RG];
+  // Step j of this wave (past its last step: the last one again; a wave with
+  // no steps reads step nsteps - 1 and never uses it). The prefill is
+  // unconditional, so the compiler's wait counts for the activation loads
+  // above see the ring as always in flight and do not wait for it.
+  auto issue = [&](int u, int j) __attribute__((always_inline)) {
+    const int step = min(wave + W * max(min(j, nkw - 1), 0), nsteps - 1);
+    const int64_t k0 = (int64_t)step * BK;
+#pragma unroll
+    for (int h = 0; h < 2 * RG; ++h)
+      wr[u][h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wsrc[h] + k0));
+  };
+#pragma unroll
+  for (int u = 0; u < U; ++u) issue(u, u);
+  GemvEpi<1, EP> epi;  // s_x is not read: the scales are set below
+  epi.load(a, n0, tid, NT, PER);
+
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int r = 0; r < kFusedRows; ++r) am[r] = wave_extreme<true>(am[r]);
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < kFusedRows; ++r) red_max[r][wave] = am[r];
+  }
+  // LDS only: the weight loads stay in flight across this barrier
+  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  RowParams rp[kFusedRows];
+#pragma unroll
+  for (int r = 0; r < kFusedRows; ++r) {
+    float v = red_max[r][0];
+#pragma unroll
+    for (int w = 1; w < W; ++w) v = max_ieee(v, red_max[r][w]);
+    rp[r] = row_params<kDynSym>(0.0f, v, nullptr, nullptr);
+  }
+
+  // codes into LDS (and out, from workgroup 0)
+  const bool writer = blockIdx.x == 0;
+#pragma unroll
+  for (int c = 0; c < CHX; ++c) {
+    const int j = c * NT + tid;
+    if (j < M * kc) {
+      const int m = j >= kc;
+      const RowParams q = m ? rp[1] : rp[0];
+      const uint2 code = codes8<kDynSym>(xv[c], q);
+      const int col = (j - m * kc) * 8;
+      *reinterpret_cast<uint2*>(xs + m * xst + col) = code;
+      if (writer) *reinterpret_cast<uint2*>(xq + (int64_t)m * ldq + col) = code;
+    }
+  }
+  if (writer && tid < M) sx[tid] = tid == 0 ? rp[0].s : rp[1].s;
+#pragma unroll
+  for (int j = 0; j < EP; ++j) {
+    const int64_t m = epi.er[j].out_row;  // 0 for elements outside the output
+    epi.er[j].sx = m == 0 ? rp[0].s : rp[1].s;
+  }
+  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+  // K loop: weight lines -> operand order through the wave's LDS buffer; the
+  // activation fragments straight from the resident codes (token rows past M
+  // repeat row M-1)
+  const int xrow = min(lane & 15, M - 1);
+  const int8_t* xbase = xs + xrow * xst + (lane >> 4) * 16;
+  i32x4 acc[RG];
+#pragma unroll
+  for (int g = 0; g < RG; ++g) acc[g] = i32x4{0, 0, 0, 0};
+  for (int i0 = 0; i0 < nkw; i0 += U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (i0 + u < nkw) {
+#pragma unroll
+        for (int h = 0; h < 2 * RG; ++h) {
+          const int row = 8 * h + (lane >> 3);
+          *reinterpret_cast<u32x4*>(tb + row * BK + (((lane & 7) ^ gemv_swz(row)) * 16)) = wr[u][h];
+        }
+        const int k0 = (wave + W * (i0 + u)) * BK;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int c = 4 * kb + (lane >> 4);
+          const i32x4 xf = *reinterpret_cast<const i32x4*>(xbase + k0 + 64 * kb);
+#pragma unroll
+          for (int g = 0; g < RG; ++g) {
+            const int row = 16 * g + (lane & 15);
+            const i32x4 wf = *reinterpret_cast<const i32x4*>(tb + row * BK + ((c ^ gemv_swz(row)) * 16));
+            acc[g] = mfma16x16x64(xf, wf, acc[g]);
+          }
+        }
+      }
+      issue(u, i0 + u + U);
+    }
+  }
+
+  // add the waves' partial tiles
+  __syncthreads();
+  int32_t* red = reinterpret_cast<int32_t*>(smem);
+#pragma unroll
+  for (int g = 0; g < RG; ++g)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[wave * PER + g * 256 + r * 64 + lane] = acc[g][r];
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < EP; ++j) {
+    const int e = tid + NT * j;
+    if (e >= PER) continue;
+    int v = 0;
+#pragma unroll
+    for (int w = 0; w < W; ++w) v += red[w * PER + e];
+    epilogue_store(a, epi.er[j], epi.ec[j], epi.n[j], v);
+  }
+}
+
 namespace {
 
 // Launch shape of the decode kernels, from sweeps over the Llama-3-8B decode
@@ -498,7 +682,10 @@ namespace {
 //    16.9 / 20.4);
 //  - otherwise the register kernel, with 32 rows per workgroup when 16-row
 //    groups would need between one and two workgroups per CU (a half-empty
-//    second round costs more than the larger tile).
+//    second round costs more than the larger tile);
+//  - a short K (at most 40 steps) over 256 - 512 row groups leaves one
+//    workgroup per CU: there 8 waves with a ring of 2 (M <= 16) or 1 steps
+//    beat 4 waves with 4 (0.4 - 1.4 us per launch at K = 4096 - 5120).
 enum class GemvKind { kReg, kShared, kGeneral };
 struct GemvCfg {
   GemvKind kind;
@@ -614,6 +801,49 @@ const char* decode_kernel_name(int64_t M, int64_t N, int64_t K, size_t ws_bytes)
   W8A8_GEMV_REG_INSTANCES(W8A8_REG_NAME)
 #undef W8A8_REG_NAME
   return "unknown";
+}
+
+// Where one fused launch beats the quantiser launch plus the GEMM (graph
+// replays, weights rotated over 1 GiB): with at most one 16-row workgroup per
+// CU (N <= 4096) and M <= 2 -- 1 x 4096 x 4096: 6.7 against 7.7 us, 2 x 4096
+// x 4096: 7.5 against 8.0, 1 x 14336 x 4096: 13.8 against 14.2. With more
+// workgroups each round pays the prologue again (1 x 4096 x 28672: 28.5
+// against 27.1 us; 4 x 4096 x 28672: 36.3 against 24.3), and 32-row
+// workgroups or more rows lose too (1 x 4096 x 6144: 9.7 against 9.3).
+bool fused_linear_fits(int64_t M, int64_t N, int64_t K) {
+  return M >= 1 && M <= kFusedRows && N >= 1 && N <= 4096 && K % 128 == 0 && M * K <= kFusedElems;
+}
+
+namespace {
+// The fused kernel takes the register kernel's launch shape for M <= 16.
+template <int RG, int W, int U>
+hipError_t launch_fused(const GemmArgs& a, const uint16_t* x, int64_t ldx, int8_t* xq, int64_t ldq,
+                        float* s_x, hipStream_t stream) {
+  const int64_t blocks = (a.N + 16 * RG - 1) / (16 * RG);
+  hipLaunchKernelGGL((gemv_fused_kernel<RG, W, U>), dim3((unsigned)blocks), dim3(W * 64), 0, stream, a, x, ldx,
+                     xq, ldq, s_x);
+  return hipGetLastError();
+}
+}  // namespace
+
+// N <= 4096 leaves two of the register kernel's launch shapes: 8 waves in
+// the short-K band (N = 4081 .. 4096), 4 otherwise.
+const char* fused_linear_kernel_name(int64_t M, int64_t N, int64_t K) {
+  return gemv_cfg(M, N, K, 0).w == 8 ? "gemv_fused_kernel<1, 8, 2>" : "gemv_fused_kernel<1, 4, 4>";
+}
+
+hipError_t launch_fused_linear(const GemmArgs& a, const uint16_t* x, int64_t ldx, int8_t* xq, int64_t ldq,
+                               float* s_x, hipStream_t stream) {
+  if (!fused_linear_fits(a.M, a.N, a.K)) return hipErrorInvalidValue;
+  GemmArgs f = a;
+  f.A = nullptr;                 // the codes come from x
+  f.s_x = a.s_w;                 // read by the epilogue set-up, then replaced
+  f.sx_per_token = 0;
+  f.azp_mode = 0;
+  f.out_i32 = 0;
+  const GemvCfg c = gemv_cfg(a.M, a.N, a.K, 0);  // the register kernel's row for M <= 16
+  return c.w == 8 ? launch_fused<1, 8, 2>(f, x, ldx, xq, ldq, s_x, stream)
+                  : launch_fused<1, 4, 4>(f, x, ldx, xq, ldq, s_x, stream);
 }
 
 hipError_t launch_decode_mm(const GemmArgs& a, void* workspace, size_t ws_bytes, hipStream_t stream) {

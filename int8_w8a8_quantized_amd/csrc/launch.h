@@ -65,6 +65,14 @@ size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K);
 const char* decode_kernel_name(int64_t M, int64_t N, int64_t K, size_t ws_bytes);
 const char* scaled_mm_kernel_name(int64_t M, int64_t N, int64_t K);
 constexpr int64_t kDecodeMaxM = 64;
+// Per-token symmetric quantisation of x (bf16 [M,K], ldx) fused with the
+// decode GEMM in one launch when fused_linear_fits(M, N, K): out = the bf16 GEMM
+// of a (a.A and a.s_x are not read; no zero points), and xq / s_x receive the
+// codes and scales exactly as launch_quantize_act writes them.
+bool fused_linear_fits(int64_t M, int64_t N, int64_t K);
+hipError_t launch_fused_linear(const GemmArgs& a, const uint16_t* x, int64_t ldx, int8_t* xq, int64_t ldq,
+                               float* s_x, hipStream_t stream);
+const char* fused_linear_kernel_name(int64_t M, int64_t N, int64_t K);
 hipError_t launch_grouped_mm(const GemmArgs& a, hipStream_t stream);
 const char* grouped_mm_kernel_name(int64_t K);
 

@@ -55,7 +55,10 @@ _SIGS = {
                                    _p, _p, _i32, _p, _p, _i32, _i64, _p, ctypes.c_size_t, _p]),
     "w8a8_grouped_scaled_mm_int8": (_i32, [_p, _i64, _i64, _p, _p, _i64, _i64, _i64, _i64, _p,
                                            _p, _p, _p, _p, _i32, _i64, _p]),
+    "w8a8_linear_dyn_sym": (_i32, [_p, _i64, _i64, _i64, _p, _i64, _i64, _p, _i32, _p, _p, _i64,
+                                   _p, _i64, _p, _p, ctypes.c_size_t, _p]),
     "w8a8_scaled_mm_kernel_name": (ctypes.c_char_p, [_i64, _i64, _i64]),
+    "w8a8_linear_dyn_sym_kernel_name": (ctypes.c_char_p, [_i64, _i64, _i64]),
     "w8a8_status_string": (ctypes.c_char_p, [_i32]),
     "w8a8_last_error": (ctypes.c_char_p, []),
 }
@@ -258,6 +261,41 @@ def scaled_mm_int8(xq, Wq, s_x, s_w, zp=None, colsum=None, azp_mode: int = AZP_N
                                     _ptr(workspace), ws_bytes, _stream())
     _raise(st, "w8a8_scaled_mm_int8")
     return out
+
+
+def linear_dyn_sym(x, Wq, s_w, bias=None, out=None, xq=None, s_x=None, workspace=None):
+    """The dynamic per-token symmetric linear layer in one call: x bf16 [M,K],
+    Wq int8 [N,K], s_w float [N] or [1], bias bf16 [N]. Returns (out bf16
+    [M,N], xq int8 [M,K], s_x float [M]), identical to quantize_act(x,
+    QUANT_DYN_SYM) followed by scaled_mm_int8. workspace as for
+    scaled_mm_int8."""
+    import torch
+    M, K = x.shape
+    N = Wq.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    if xq is None:
+        xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if s_x is None:
+        s_x = torch.empty((M,), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        need = scaled_mm_workspace_size(M, N, K)
+        workspace = _workspace(x.device, _stream(), need) if need else False
+    if workspace is False:
+        workspace = None
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().w8a8_linear_dyn_sym(_ptr(x), M, K, x.stride(0) if M else K, _ptr(Wq), N,
+                                    Wq.stride(0) if N else K, _ptr(s_w), int(s_w.numel() != 1 or N == 1),
+                                    _ptr(bias), _ptr(out), out.stride(0) if M else N, _ptr(xq),
+                                    xq.stride(0) if M else K, _ptr(s_x), _ptr(workspace), ws_bytes,
+                                    _stream())
+    _raise(st, "w8a8_linear_dyn_sym")
+    return out, xq, s_x
+
+
+def linear_dyn_sym_kernel_name(M: int, N: int, K: int) -> str:
+    """Kernel that linear_dyn_sym runs for the GEMM of an M x N x K shape."""
+    return load().w8a8_linear_dyn_sym_kernel_name(M, N, K).decode()
 
 
 def grouped_scaled_mm_int8(xq, expert_offsets, Wq, s_x, s_w, row_ids=None, bias=None, T=None,

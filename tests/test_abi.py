@@ -16,7 +16,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = W.header_functions()
-    assert len(names) == 13, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -111,6 +111,36 @@ def test_gemm_rejects_before_device_work(L):
     assert W.scaled_mm_workspace_size(64, 28672, 14336) == 0    # 16384+ weight rows
     assert W.scaled_mm_workspace_size(40, 4096, 8200) == 0      # K % 128 != 0
     assert W.scaled_mm_workspace_size(65, 4096, 14336) == 0     # not the decode path
+
+
+def test_linear_rejects_before_device_work(L):
+    def lin(M=1, K=128, N=32, ldx=128, ldw=128, ldo=32, ldq=128, x=FAKE, wq=FAKE, out=FAKE, xq=FAKE,
+            sx=FAKE, sw=FAKE):
+        return L.w8a8_linear_dyn_sym(x, M, K, ldx, wq, N, ldw, sw, 1, None, out, ldo, xq, ldq, sx, None, 0,
+                                     None)
+    assert lin(K=24) == W.ERR_INVALID_ARG
+    assert lin(ldx=132) == W.ERR_INVALID_ARG       # not a multiple of 8
+    assert lin(ldq=136) == W.ERR_INVALID_ARG       # not a multiple of 16
+    assert lin(ldw=136) == W.ERR_INVALID_ARG
+    assert lin(ldo=20) == W.ERR_INVALID_ARG
+    assert lin(x=FAKE + 4) == W.ERR_INVALID_ARG
+    for kw in ("x", "xq", "sx", "sw", "out", "wq"):
+        assert lin(**{kw: None}) == W.ERR_INVALID_ARG, kw
+    assert lin(M=-1) == W.ERR_INVALID_ARG
+    assert lin(M=0) == W.OK
+
+
+def test_linear_kernel_names():
+    """The fused kernel for M <= 2, N <= 4096, K % 128 == 0, M * K <= 16384,
+    in the register kernel's launch shape; otherwise the separate GEMM's."""
+    assert W.linear_dyn_sym_kernel_name(1, 4096, 4096) == "gemv_fused_kernel<1, 8, 2>"
+    assert W.linear_dyn_sym_kernel_name(2, 4096, 4096) == "gemv_fused_kernel<1, 8, 2>"
+    assert W.linear_dyn_sym_kernel_name(1, 4096, 14336) == "gemv_fused_kernel<1, 4, 4>"
+    assert W.linear_dyn_sym_kernel_name(1, 2048, 4096) == "gemv_fused_kernel<1, 4, 4>"
+    for (M, N, K) in [(1, 6144, 4096), (1, 28672, 4096), (3, 4096, 4096), (2, 4096, 14336),
+                      (1, 300, 4112), (64, 4096, 4096)]:
+        assert W.linear_dyn_sym_kernel_name(M, N, K) == W.scaled_mm_kernel_name(M, N, K), (M, N, K)
+    assert W.linear_dyn_sym_kernel_name(0, 300, 4096) == ""
 
 
 def test_grouped_rejects_before_device_work(L):
