@@ -24,9 +24,10 @@
 // per-column operands were loaded before the K loop, writes out.
 //
 // Shared-activation kernel, gemv_shared_kernel (K a multiple of 128; M > 16
-// with many weight rows or a long K): a workgroup of 4 waves owns 64 weight
-// rows; one activation stage per K step serves all of them through LDS. With
-// a long K the workgroups take K ranges and a second kernel adds them.
+// with many weight rows or a long K): a workgroup of W waves (4, or 7) owns
+// 16 W weight rows; one activation stage per K step serves all of them
+// through LDS. With a long K the workgroups take K ranges and a second kernel
+// adds them.
 //
 // General kernel (any K that is a multiple of 16), gemv_i8_kernel: operands
 // go straight from memory into MFMA registers, as described above it.
@@ -213,11 +214,13 @@ __global__ __launch_bounds__(W * 64) void gemv_reg_kernel(GemmArgs a) {
 // before every wave passed the barrier of step i - 1.
 constexpr int kSharedWaves = 4;
 
-template <int MF, int U, bool DIRECT>
-__global__ __launch_bounds__(kSharedWaves * 64) void gemv_shared_kernel(GemmArgs a, int splits,
-                                                                        int steps_per_split,
-                                                                        int32_t* __restrict__ part) {
-  constexpr int W = kSharedWaves, BK = 128, XR = 16 * MF;
+// W waves of 16 weight rows each; the split form (not DIRECT) always has
+// kSharedWaves, the layout gemv_reduce_kernel reads.
+template <int MF, int U, bool DIRECT, int W>
+__global__ __launch_bounds__(W * 64) void gemv_shared_kernel(GemmArgs a, int splits, int steps_per_split,
+                                                             int32_t* __restrict__ part) {
+  static_assert(DIRECT || W == kSharedWaves, "the reduction reads kSharedWaves tiles per row block");
+  constexpr int BK = 128, XR = 16 * MF;
   constexpr int AI = XR / 8;            // activation line instructions per step
   constexpr int AQ = (AI + W - 1) / W;  // per wave (the last may repeat)
   constexpr int PER = MF * 256;         // accumulator ints of one wave
@@ -670,10 +673,15 @@ namespace {
 // rotated over 1 GiB:
 //  - M <= 16: the register kernel, 16 rows per workgroup; 4 waves split K,
 //    2 once there are 1024+ row groups (the waves then live long enough);
-//  - M > 16 with 16384+ weight rows: the shared-activation kernel over the
-//    whole K with the epilogue in the kernel (its 64-row workgroups fill the
-//    chip; 4096 x 28672: 25.5 / 30.3 us at M = 32 / 64, where an LDS ring
-//    for the weights as well took 28.1 / 32.7);
+//  - M > 16 with more than 8192 weight rows: the shared-activation kernel
+//    over the whole K with the epilogue in the kernel (its 64-row workgroups
+//    fill the chip; 4096 x 28672: 25.5 / 30.3 us at M = 32 / 64, where an
+//    LDS ring for the weights as well took 28.1 / 32.7; 4096 x 14336 at
+//    M = 17 / 64: 13.7 / 17.4 us against 17.9 / 29.8 for the register
+//    kernel, whose 16-row workgroups each read the whole activation), with
+//    7 waves (112 rows) from M = 33 on where that makes whole rounds of 256
+//    workgroups (4096 x 28672 at M = 48 / 64: 27.3 / 29.3 us against 28.4 /
+//    31.3; 6 or 8 waves, or 7 with a partial round, are slower);
 //  - M > 16, 64 steps of K or more and a workspace: the shared-activation
 //    kernel over about 256 workgroups (K ranges of at least 16 steps), then
 //    the reduction;
@@ -697,7 +705,7 @@ int gemv_mf(int64_t M) { return (int)std::min<int64_t>((M + 15) / 16, 4); }
 
 // The shared kernel's K ranges for this shape (0: not used).
 int shared_splits(int64_t M, int64_t N, int64_t K) {
-  if (gemv_mf(M) == 1 || K % 128 != 0 || N >= 16384) return 0;
+  if (gemv_mf(M) == 1 || K % 128 != 0 || N > 8192) return 0;  // N > 8192: one K range
   const int64_t nsteps = K / 128, rbs = (N + 63) / 64;
   if (nsteps < 64) return 0;
   const int64_t s = std::min<int64_t>(std::max<int64_t>(256 / rbs, 1), std::min<int64_t>(8, nsteps / 16));
@@ -730,7 +738,13 @@ GemvCfg gemv_cfg(int64_t M, int64_t N, int64_t K, size_t ws_bytes) {
     if (short_k) return {GemvKind::kReg, 1, rg_short, 8, 2, 1};
     return {GemvKind::kReg, 1, 1, groups >= 1024 ? 2 : 4, 4, 1};
   }
-  if (N >= 16384) return {GemvKind::kShared, mf, 1, kSharedWaves, 4, 1};
+  if (N > 8192) {
+    // one K range over 64-row workgroups, or 112-row ones (7 waves) from
+    // M = 33 on when those make whole rounds over the CUs (4096 x 28672:
+    // 256 workgroups instead of 448 sharing each activation stage)
+    const bool seven = mf >= 3 && ((N + 111) / 112) % 256 == 0;
+    return {GemvKind::kShared, mf, 1, seven ? 7 : kSharedWaves, 4, 1};
+  }
   const int s = shared_splits(M, N, K);
   if (s > 0 && ws_bytes >= shared_workspace_bytes(M, N, s)) return {GemvKind::kShared, mf, 1, kSharedWaves, 4, s};
   if (short_k && !(mf == 3 && rg_short == 2)) return {GemvKind::kReg, mf, rg_short, 8, 1, 1};
@@ -746,17 +760,22 @@ hipError_t launch_reg(const GemmArgs& a, hipStream_t stream) {
 }
 
 template <int MF, int U>
-hipError_t launch_shared(const GemmArgs& a, int splits, int32_t* part, hipStream_t stream) {
-  const int64_t rbs = (a.N + 63) / 64;
+hipError_t launch_shared(const GemmArgs& a, int splits, int waves, int32_t* part, hipStream_t stream) {
   const int64_t nsteps = a.K / 128;
   const int sps = (int)((nsteps + splits - 1) / splits);
   if (splits == 1) {  // one K range: the epilogue runs in the kernel, no workspace
-    hipLaunchKernelGGL((gemv_shared_kernel<MF, U, true>), dim3((unsigned)rbs), dim3(kSharedWaves * 64), 0,
-                       stream, a, 1, sps, nullptr);
+    if (waves == 7) {
+      hipLaunchKernelGGL((gemv_shared_kernel<MF, U, true, 7>), dim3((unsigned)((a.N + 111) / 112)), dim3(7 * 64),
+                         0, stream, a, 1, sps, nullptr);
+    } else {
+      hipLaunchKernelGGL((gemv_shared_kernel<MF, U, true, kSharedWaves>), dim3((unsigned)((a.N + 63) / 64)),
+                         dim3(kSharedWaves * 64), 0, stream, a, 1, sps, nullptr);
+    }
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((gemv_shared_kernel<MF, U, false>), dim3((unsigned)(rbs * splits)), dim3(kSharedWaves * 64), 0,
-                     stream, a, splits, sps, part);
+  const int64_t rbs = (a.N + 63) / 64;
+  hipLaunchKernelGGL((gemv_shared_kernel<MF, U, false, kSharedWaves>), dim3((unsigned)(rbs * splits)),
+                     dim3(kSharedWaves * 64), 0, stream, a, splits, sps, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t elems = rbs * kSharedWaves * MF * 256;
@@ -788,11 +807,14 @@ const char* decode_kernel_name(int64_t M, int64_t N, int64_t K, size_t ws_bytes)
       return gen[c.mf - 1];
     }
     case GemvKind::kShared: {
-      static const char* split[3] = {"gemv_shared_kernel<2, 4, false>", "gemv_shared_kernel<3, 4, false>",
-                                     "gemv_shared_kernel<4, 4, false>"};
-      static const char* direct[3] = {"gemv_shared_kernel<2, 4, true>", "gemv_shared_kernel<3, 4, true>",
-                                      "gemv_shared_kernel<4, 4, true>"};
-      return c.splits == 1 ? direct[c.mf - 2] : split[c.mf - 2];
+      static const char* split[3] = {"gemv_shared_kernel<2, 4, false, 4>", "gemv_shared_kernel<3, 4, false, 4>",
+                                     "gemv_shared_kernel<4, 4, false, 4>"};
+      static const char* direct[3] = {"gemv_shared_kernel<2, 4, true, 4>", "gemv_shared_kernel<3, 4, true, 4>",
+                                      "gemv_shared_kernel<4, 4, true, 4>"};
+      static const char* direct7[3] = {"gemv_shared_kernel<2, 4, true, 7>", "gemv_shared_kernel<3, 4, true, 7>",
+                                       "gemv_shared_kernel<4, 4, true, 7>"};
+      if (c.splits != 1) return split[c.mf - 2];
+      return c.w == 7 ? direct7[c.mf - 2] : direct[c.mf - 2];
     }
     default: break;
   }
@@ -859,9 +881,9 @@ hipError_t launch_decode_mm(const GemmArgs& a, void* workspace, size_t ws_bytes,
       }
     case GemvKind::kShared:
       switch (c.mf) {
-        case 2: return launch_shared<2, 4>(a, c.splits, part, stream);
-        case 3: return launch_shared<3, 4>(a, c.splits, part, stream);
-        default: return launch_shared<4, 4>(a, c.splits, part, stream);
+        case 2: return launch_shared<2, 4>(a, c.splits, c.w, part, stream);
+        case 3: return launch_shared<3, 4>(a, c.splits, c.w, part, stream);
+        default: return launch_shared<4, 4>(a, c.splits, c.w, part, stream);
       }
     default: break;
   }

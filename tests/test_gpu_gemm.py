@@ -137,18 +137,23 @@ DECODE_CASES = [
     (48, 4096, 1000, "gemv_reg_kernel<3, 1, 4, 4>"),
     (48, 1024, 4090, "gemv_reg_kernel<3, 1, 8, 1>"),
     (33, 2048, 6000, "gemv_reg_kernel<3, 2, 4, 3>"),
-    (64, 2048, 9000, "gemv_reg_kernel<4, 1, 4, 4>"),
+    (64, 6144, 2000, "gemv_reg_kernel<4, 1, 4, 4>"),
     (64, 4096, 4096, "gemv_reg_kernel<4, 1, 8, 1>"),
     (64, 6144, 4200, "gemv_reg_kernel<4, 2, 4, 3>"),
     (60, 4096, 6130, "gemv_reg_kernel<4, 2, 8, 1>"),
-    (20, 256, 16400, "gemv_shared_kernel<2, 4, true>"),
-    (40, 512, 16390, "gemv_shared_kernel<3, 4, true>"),
-    (64, 384, 16384, "gemv_shared_kernel<4, 4, true>"),
-    (33, 4096, 16391, "gemv_shared_kernel<3, 4, true>"),
-    (64, 14336, 4096, "gemv_shared_kernel<4, 4, false>"),
-    (48, 8192, 1000, "gemv_shared_kernel<3, 4, false>"),
-    (17, 8192, 100, "gemv_shared_kernel<2, 4, false>"),
-    (30, 8320, 300, "gemv_shared_kernel<2, 4, false>"),
+    (20, 256, 16400, "gemv_shared_kernel<2, 4, true, 4>"),
+    (40, 512, 16390, "gemv_shared_kernel<3, 4, true, 4>"),
+    (64, 384, 16384, "gemv_shared_kernel<4, 4, true, 4>"),
+    (33, 4096, 16391, "gemv_shared_kernel<3, 4, true, 4>"),
+    (17, 1024, 8200, "gemv_shared_kernel<2, 4, true, 4>"),     # N just above 8192
+    (64, 4096, 14336, "gemv_shared_kernel<4, 4, true, 4>"),
+    (50, 8320, 9000, "gemv_shared_kernel<4, 4, true, 4>"),     # long K, N > 8192: one K range
+    (40, 256, 28600, "gemv_shared_kernel<3, 4, true, 7>"),     # 256 workgroups of 112 rows, ragged
+    (64, 4096, 28672, "gemv_shared_kernel<4, 4, true, 7>"),
+    (64, 14336, 4096, "gemv_shared_kernel<4, 4, false, 4>"),
+    (48, 8192, 1000, "gemv_shared_kernel<3, 4, false, 4>"),
+    (17, 8192, 100, "gemv_shared_kernel<2, 4, false, 4>"),
+    (30, 8320, 300, "gemv_shared_kernel<2, 4, false, 4>"),
     (3, 272, 64, "gemv_i8_kernel<1, 2, 4, 8>"),
     (64, 4112, 200, "gemv_i8_kernel<4, 2, 4, 8>"),
 ]
