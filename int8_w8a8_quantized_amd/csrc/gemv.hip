@@ -672,7 +672,9 @@ namespace {
 // 4096 x 28672, 14336 x 4096}) timed as graph replays with the weights
 // rotated over 1 GiB:
 //  - M <= 16: the register kernel, 16 rows per workgroup; 4 waves split K,
-//    2 once there are 1024+ row groups (the waves then live long enough);
+//    2 once there are more than 512 row groups (the waves then live long
+//    enough); from M = 12 on with more than 8192 weight rows, the
+//    shared-activation kernel below instead;
 //  - M > 16 with more than 8192 weight rows: the shared-activation kernel
 //    over the whole K with the epilogue in the kernel (its 64-row workgroups
 //    fill the chip; 4096 x 28672: 25.5 / 30.3 us at M = 32 / 64, where an
@@ -736,7 +738,13 @@ GemvCfg gemv_cfg(int64_t M, int64_t N, int64_t K, size_t ws_bytes) {
   const int rg_short = groups > 256 ? 2 : 1;
   if (mf == 1) {
     if (short_k) return {GemvKind::kReg, 1, rg_short, 8, 2, 1};
-    return {GemvKind::kReg, 1, 1, groups >= 1024 ? 2 : 4, 4, 1};
+    // from M = 12 on, wide weights read the activation once per 64 rows
+    // (bf16 out with bias: 16 x 4096 x 28672 23.5 us against 24.8, 16 x
+    // 14336 x 28672 63.8 against 72.8; at M = 8 the two are even)
+    if (M >= 12 && N > 8192) return {GemvKind::kShared, 1, 1, kSharedWaves, 4, 1};
+    // 2 waves once there are more than 512 row groups (8 x 4096 x 14336:
+    // 13.3 us against 15.0 with 4)
+    return {GemvKind::kReg, 1, 1, groups > 512 ? 2 : 4, 4, 1};
   }
   if (N > 8192) {
     // one K range over 64-row workgroups, or 112-row ones (7 waves) from
@@ -807,14 +815,14 @@ const char* decode_kernel_name(int64_t M, int64_t N, int64_t K, size_t ws_bytes)
       return gen[c.mf - 1];
     }
     case GemvKind::kShared: {
-      static const char* split[3] = {"gemv_shared_kernel<2, 4, false, 4>", "gemv_shared_kernel<3, 4, false, 4>",
-                                     "gemv_shared_kernel<4, 4, false, 4>"};
-      static const char* direct[3] = {"gemv_shared_kernel<2, 4, true, 4>", "gemv_shared_kernel<3, 4, true, 4>",
-                                      "gemv_shared_kernel<4, 4, true, 4>"};
-      static const char* direct7[3] = {"gemv_shared_kernel<2, 4, true, 7>", "gemv_shared_kernel<3, 4, true, 7>",
-                                       "gemv_shared_kernel<4, 4, true, 7>"};
-      if (c.splits != 1) return split[c.mf - 2];
-      return c.w == 7 ? direct7[c.mf - 2] : direct[c.mf - 2];
+      static const char* split[4] = {"gemv_shared_kernel<1, 4, false, 4>", "gemv_shared_kernel<2, 4, false, 4>",
+                                     "gemv_shared_kernel<3, 4, false, 4>", "gemv_shared_kernel<4, 4, false, 4>"};
+      static const char* direct[4] = {"gemv_shared_kernel<1, 4, true, 4>", "gemv_shared_kernel<2, 4, true, 4>",
+                                      "gemv_shared_kernel<3, 4, true, 4>", "gemv_shared_kernel<4, 4, true, 4>"};
+      static const char* direct7[4] = {"gemv_shared_kernel<1, 4, true, 7>", "gemv_shared_kernel<2, 4, true, 7>",
+                                       "gemv_shared_kernel<3, 4, true, 7>", "gemv_shared_kernel<4, 4, true, 7>"};
+      if (c.splits != 1) return split[c.mf - 1];
+      return c.w == 7 ? direct7[c.mf - 1] : direct[c.mf - 1];
     }
     default: break;
   }
@@ -881,6 +889,7 @@ hipError_t launch_decode_mm(const GemmArgs& a, void* workspace, size_t ws_bytes,
       }
     case GemvKind::kShared:
       switch (c.mf) {
+        case 1: return launch_shared<1, 4>(a, c.splits, c.w, part, stream);
         case 2: return launch_shared<2, 4>(a, c.splits, c.w, part, stream);
         case 3: return launch_shared<3, 4>(a, c.splits, c.w, part, stream);
         default: return launch_shared<4, 4>(a, c.splits, c.w, part, stream);

@@ -127,7 +127,10 @@ def test_empty():
 DECODE_CASES = [
     (1, 14336, 4096, "gemv_reg_kernel<1, 1, 4, 4>"),
     (7, 128, 300, "gemv_reg_kernel<1, 1, 4, 4>"),
-    (16, 4096, 16400, "gemv_reg_kernel<1, 1, 2, 4>"),
+    (5, 4096, 16400, "gemv_reg_kernel<1, 1, 2, 4>"),
+    (12, 4096, 28672, "gemv_shared_kernel<1, 4, true, 4>"),  # M >= 12, N > 8192
+    (8, 1024, 9000, "gemv_reg_kernel<1, 1, 2, 4>"),          # 563 row groups: 2 waves
+    (16, 640, 14000, "gemv_shared_kernel<1, 4, true, 4>"),   # ragged N
     (1, 4096, 4096, "gemv_reg_kernel<1, 1, 8, 2>"),
     (5, 2048, 5000, "gemv_reg_kernel<1, 2, 8, 2>"),
     (32, 1024, 200, "gemv_reg_kernel<2, 1, 4, 4>"),
