@@ -198,7 +198,7 @@ w8a8_status w8a8_prepare_fp8_block_to_int8(const uint8_t* W8, const float* S, in
                                            int32_t* err_flag, void* stream);
 
 /* Bytes of workspace w8a8_scaled_mm_int8 can use for this shape (0 when it
- * uses none). With at least this many bytes, decode shapes (M <= 64) with a
+ * uses none). With at least this many bytes, decode shapes (M <= 128) with a
  * long K split K over workgroups and add the ranges in a second kernel; with
  * fewer (or NULL) the call runs unsplit, with the same result. No state is
  * kept in it between calls, so any buffer serves; calls that may run at the

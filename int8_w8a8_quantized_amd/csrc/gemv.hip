@@ -1,4 +1,4 @@
-// Decode-shaped (M <= 64) int8 GEMM: weight-streaming kernels.
+// Decode-shaped (M <= 128) int8 GEMM: weight-streaming kernels.
 //
 // Same product and fused epilogue as the prefill GEMM ("[SGLang] W4A8, W8A8,
 // W4A4: 혼합 정밀도 양자화 스킴", 핵심 코드 분석 §3-§4), but with a handful of
@@ -696,19 +696,28 @@ namespace {
 //  - a short K (at most 40 steps) over 256 - 512 row groups leaves one
 //    workgroup per CU: there 8 waves with a ring of 2 (M <= 16) or 1 steps
 //    beat 4 waves with 4 (0.4 - 1.4 us per launch at K = 4096 - 5120).
-enum class GemvKind { kReg, kShared, kGeneral };
+enum class GemvKind { kReg, kShared, kGeneral, kTile };  // kTile: the MFMA tile kernel
 struct GemvCfg {
   GemvKind kind;
   int mf, rg, w, u;  // u: ring steps in flight per wave
   int splits;        // K ranges of the shared kernel (1: the epilogue runs in it)
 };
 
-int gemv_mf(int64_t M) { return (int)std::min<int64_t>((M + 15) / 16, 4); }
+// Token blocks of 16: up to 4 on every decode path, 5 - 8 (M = 65 - 128) on
+// the split shared kernel only.
+int gemv_mf(int64_t M) { return (int)std::min<int64_t>((M + 15) / 16, 8); }
 
 // The shared kernel's K ranges for this shape (0: not used).
 int shared_splits(int64_t M, int64_t N, int64_t K) {
   if (gemv_mf(M) == 1 || K % 128 != 0 || N > 8192) return 0;  // N > 8192: one K range
   const int64_t nsteps = K / 128, rbs = (N + 63) / 64;
+  if (gemv_mf(M) > 4) {
+    // M = 65 - 128: ranges of at least 8 steps (65 x 14336 x 4096: 21.3 us
+    // in 4 ranges against 57.8 on the MFMA tiles, 65 x 4096 x 4096 12.4
+    // against 20.5; 112 x 8192 x 2048: 15.0 in 8 ranges against 37.6)
+    const int64_t s = std::min<int64_t>(std::max<int64_t>(256 / rbs, 1), std::min<int64_t>(8, nsteps / 8));
+    return s >= 2 ? (int)s : 0;
+  }
   if (nsteps < 64) return 0;
   const int64_t s = std::min<int64_t>(std::max<int64_t>(256 / rbs, 1), std::min<int64_t>(8, nsteps / 16));
   return s >= 2 ? (int)s : 0;
@@ -728,6 +737,11 @@ size_t shared_workspace_bytes(int64_t M, int64_t N, int splits) {
 
 GemvCfg gemv_cfg(int64_t M, int64_t N, int64_t K, size_t ws_bytes) {
   const int mf = gemv_mf(M);
+  if (mf > 4) {  // M = 65 - 128: K ranges of the shared kernel, else the MFMA tiles
+    const int s = shared_splits(M, N, K);
+    if (s > 0 && ws_bytes >= shared_workspace_bytes(M, N, s)) return {GemvKind::kShared, mf, 1, kSharedWaves, 4, s};
+    return {GemvKind::kTile, mf, 0, 0, 0, 0};
+  }
   if (K % 128 != 0) return {GemvKind::kGeneral, mf, 2, 4, 8, 1};
   const int64_t groups = (N + 15) / 16;
   // A short K (at most 40 steps) over 256 - 512 row groups leaves one
@@ -792,6 +806,22 @@ hipError_t launch_shared(const GemmArgs& a, int splits, int waves, int32_t* part
   return hipGetLastError();
 }
 
+// 5 - 8 token blocks: the split form only (its epilogue runs in the
+// reduction, so the kernel holds no per-row epilogue operands).
+template <int MF>
+hipError_t launch_shared_split(const GemmArgs& a, int splits, int32_t* part, hipStream_t stream) {
+  const int64_t nsteps = a.K / 128, rbs = (a.N + 63) / 64;
+  const int sps = (int)((nsteps + splits - 1) / splits);
+  hipLaunchKernelGGL((gemv_shared_kernel<MF, 4, false, kSharedWaves>), dim3((unsigned)(rbs * splits)),
+                     dim3(kSharedWaves * 64), 0, stream, a, splits, sps, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t elems = rbs * kSharedWaves * MF * 256;
+  hipLaunchKernelGGL((gemv_reduce_kernel<MF>), dim3((unsigned)((elems + 255) / 256)), dim3(256), 0, stream, a,
+                     splits, part);
+  return hipGetLastError();
+}
+
 template <int MF>
 hipError_t launch_general(const GemmArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((gemv_i8_kernel<MF, 2, 4, 8>), dim3((unsigned)((a.N + 31) / 32)), dim3(256), 0,
@@ -814,9 +844,12 @@ const char* decode_kernel_name(int64_t M, int64_t N, int64_t K, size_t ws_bytes)
                                    "gemv_i8_kernel<3, 2, 4, 8>", "gemv_i8_kernel<4, 2, 4, 8>"};
       return gen[c.mf - 1];
     }
+    case GemvKind::kTile: return scaled_mm_kernel_name(M, N, K);
     case GemvKind::kShared: {
-      static const char* split[4] = {"gemv_shared_kernel<1, 4, false, 4>", "gemv_shared_kernel<2, 4, false, 4>",
-                                     "gemv_shared_kernel<3, 4, false, 4>", "gemv_shared_kernel<4, 4, false, 4>"};
+      static const char* split[8] = {"gemv_shared_kernel<1, 4, false, 4>", "gemv_shared_kernel<2, 4, false, 4>",
+                                     "gemv_shared_kernel<3, 4, false, 4>", "gemv_shared_kernel<4, 4, false, 4>",
+                                     "gemv_shared_kernel<5, 4, false, 4>", "gemv_shared_kernel<6, 4, false, 4>",
+                                     "gemv_shared_kernel<7, 4, false, 4>", "gemv_shared_kernel<8, 4, false, 4>"};
       static const char* direct[4] = {"gemv_shared_kernel<1, 4, true, 4>", "gemv_shared_kernel<2, 4, true, 4>",
                                       "gemv_shared_kernel<3, 4, true, 4>", "gemv_shared_kernel<4, 4, true, 4>"};
       static const char* direct7[4] = {"gemv_shared_kernel<1, 4, true, 7>", "gemv_shared_kernel<2, 4, true, 7>",
@@ -887,8 +920,13 @@ hipError_t launch_decode_mm(const GemmArgs& a, void* workspace, size_t ws_bytes,
         case 3: return launch_general<3>(a, stream);
         default: return launch_general<4>(a, stream);
       }
+    case GemvKind::kTile: return launch_scaled_mm(a, stream);
     case GemvKind::kShared:
       switch (c.mf) {
+        case 5: return launch_shared_split<5>(a, c.splits, part, stream);
+        case 6: return launch_shared_split<6>(a, c.splits, part, stream);
+        case 7: return launch_shared_split<7>(a, c.splits, part, stream);
+        case 8: return launch_shared_split<8>(a, c.splits, part, stream);
         case 1: return launch_shared<1, 4>(a, c.splits, c.w, part, stream);
         case 2: return launch_shared<2, 4>(a, c.splits, c.w, part, stream);
         case 3: return launch_shared<3, 4>(a, c.splits, c.w, part, stream);

@@ -56,15 +56,16 @@ struct GemmArgs {
 };
 
 hipError_t launch_scaled_mm(const GemmArgs& a, hipStream_t stream);  // MFMA tiles, any M
-// M <= 64: weight streaming. Some shapes split K over workgroups when a
+// M <= 128: weight streaming. Some shapes split K over workgroups when a
 // workspace of decode_workspace_bytes(M, N, K) bytes is given (no state is
-// kept in it between calls); without it they run unsplit.
+// kept in it between calls); without it they run unsplit. From M = 65 on only
+// the split form streams; every other shape runs launch_scaled_mm.
 hipError_t launch_decode_mm(const GemmArgs& a, void* workspace, size_t ws_bytes, hipStream_t stream);
 size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K);
 // Name of the kernel instance launch_decode_mm / launch_scaled_mm runs for a shape.
 const char* decode_kernel_name(int64_t M, int64_t N, int64_t K, size_t ws_bytes);
 const char* scaled_mm_kernel_name(int64_t M, int64_t N, int64_t K);
-constexpr int64_t kDecodeMaxM = 64;
+constexpr int64_t kDecodeMaxM = 128;
 // Per-token symmetric quantisation of x (bf16 [M,K], ldx) fused with the
 // decode GEMM in one launch when fused_linear_fits(M, N, K): out = the bf16 GEMM
 // of a (a.A and a.s_x are not read; no zero points), and xq / s_x receive the

@@ -110,7 +110,11 @@ def test_gemm_rejects_before_device_work(L):
     assert W.scaled_mm_workspace_size(64, 4096, 4096) == 0      # fewer than 64 steps
     assert W.scaled_mm_workspace_size(64, 28672, 14336) == 0    # 16384+ weight rows
     assert W.scaled_mm_workspace_size(40, 4096, 8200) == 0      # K % 128 != 0
-    assert W.scaled_mm_workspace_size(65, 4096, 14336) == 0     # not the decode path
+    # 65 - 128 rows: ranges of at least 8 steps, splits = min(256 / row blocks, 8, steps / 8)
+    assert W.scaled_mm_workspace_size(65, 4096, 14336) == 4 * 64 * 4 * 5 * 256 * 4
+    assert W.scaled_mm_workspace_size(128, 2048, 8192) == 8 * 32 * 4 * 8 * 256 * 4
+    assert W.scaled_mm_workspace_size(128, 8200, 4096) == 0     # N > 8192: MFMA tiles
+    assert W.scaled_mm_workspace_size(129, 4096, 14336) == 0    # not the decode path
 
 
 def test_linear_rejects_before_device_work(L):

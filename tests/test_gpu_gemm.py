@@ -157,6 +157,12 @@ DECODE_CASES = [
     (48, 8192, 1000, "gemv_shared_kernel<3, 4, false, 4>"),
     (17, 8192, 100, "gemv_shared_kernel<2, 4, false, 4>"),
     (30, 8320, 300, "gemv_shared_kernel<2, 4, false, 4>"),
+    (65, 14336, 4096, "gemv_shared_kernel<5, 4, false, 4>"),   # M = 65 - 128: K ranges
+    (96, 2048, 300, "gemv_shared_kernel<6, 4, false, 4>"),
+    (112, 8192, 2048, "gemv_shared_kernel<7, 4, false, 4>"),
+    (128, 2048, 1000, "gemv_shared_kernel<8, 4, false, 4>"),
+    (128, 4096, 8200, "gemm_i8_dma_kernel<128, 128, 128, 10, false>"),  # N > 8192: MFMA tiles
+    (100, 1024, 600, "gemm_i8_dma_kernel<128, 128, 128, 10, false>"),   # ranges too short
     (3, 272, 64, "gemv_i8_kernel<1, 2, 4, 8>"),
     (64, 4112, 200, "gemv_i8_kernel<4, 2, 4, 8>"),
 ]
@@ -177,7 +183,7 @@ def test_decode_paths(M, K, N, kernel):
     _run(d, W.AZP_PER_TOKEN, bias=True)
 
 
-@pytest.mark.parametrize("M,K,N", [(64, 14336, 4096), (48, 8192, 1000)])
+@pytest.mark.parametrize("M,K,N", [(64, 14336, 4096), (48, 8192, 1000), (96, 14336, 4096)])
 def test_decode_split_without_workspace(M, K, N):
     """Without a workspace (or with one too small) a split shape runs unsplit,
     with the same exact result."""
