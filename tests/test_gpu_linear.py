@@ -34,6 +34,8 @@ CASES = [
     (1, 4112, 300, "gemv_i8_kernel<1, 2, 4, 8>"),     # K % 128 != 0
     (64, 4096, 4096, "gemv_reg_kernel<4, 1, 8, 1>"),
     (80, 512, 256, "gemm_i8_dma_kernel<128, 128, 128, 10, false>"),  # the MFMA tile path
+    (96, 2048, 300, "gemv_shared_kernel<6, 4, false, 4>"),   # M = 65 - 128: K ranges
+    (128, 4096, 4096, "gemv_shared_kernel<8, 4, false, 4>"),
 ]
 
 
