@@ -308,10 +308,13 @@ def main():
     dom_name, dom = max(per_kernel.items(), key=lambda kv: kv[1]["us"])
     avg_us = dom["us"] / dom["launches"]
     achieved = dom["bytes"] / (dom["us"] * 1e-6) / 1e9
+    # frac is the dominant kernel's (achieved / peak); step_frac is the whole
+    # step's (value / peak), the figure to read against the decode target
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(dom_name),
                 "kernel": dom_name, "avg_launch_us": round(avg_us, 3),
-                "bytes_per_launch": int(dom["bytes"] / dom["launches"])}
+                "bytes_per_launch": int(dom["bytes"] / dom["launches"]),
+                "step_frac": round(value / HBM_PEAK_GBS, 4)}
     kernels = {k: {"launches_per_step": v["launches"], "avg_us": round(v["us"] / v["launches"], 3),
                    "GBs": round(v["bytes"] / (v["us"] * 1e-6) / 1e9, 1)} for k, v in per_kernel.items()}
     del graphs

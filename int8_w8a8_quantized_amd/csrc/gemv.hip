@@ -413,12 +413,16 @@ __global__ __launch_bounds__(W * 64) void gemv_i8_kernel(GemmArgs a) {
   u32x4 wb[U][NB], xb[U][MF];
   const u32x4 z = {0u, 0u, 0u, 0u};
   // Load step `step` into ring slot u; a step past the end reloads step 0.
+  // A lane whose 16 bytes start at or past K (the tail of a K that is not a
+  // multiple of 64) reads the start of its rows instead, so no load leaves a
+  // row; its activation is zero, so the product does not depend on it.
   auto load_step = [&](int u, int step) __attribute__((always_inline)) {
     const bool live = step < nsteps;
     const int64_t k = (int64_t)(live ? step : 0) * 64;
+    const int64_t kw = k + kgrp < a.K ? k : 0;
 #pragma unroll
     for (int j = 0; j < NB; ++j)
-      wb[u][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(bp[j] + k));
+      wb[u][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(bp[j] + kw));
 #pragma unroll
     for (int f = 0; f < MF; ++f) {
       const bool ok = a_ok[f] && live && k + kgrp < a.K;

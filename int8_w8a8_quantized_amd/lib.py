@@ -216,15 +216,20 @@ def scaled_mm_workspace_size(M: int, N: int, K: int) -> int:
 
 
 _ws_cache = {}
+_ws_retired = []
 
 
 def _workspace(device, stream: int, nbytes: int):
     """A workspace of at least nbytes kept per (device, stream); the library
-    keeps no state in it, so calls ordered on one stream can share it."""
+    keeps no state in it, so calls ordered on one stream can share it. A
+    buffer that a larger request replaces is kept alive (never freed), since
+    a HIP graph captured with it may still write there on replay."""
     import torch
     key = (device.index, stream)
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:
+        if ws is not None:
+            _ws_retired.append(ws)
         ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
         _ws_cache[key] = ws
     return ws

@@ -104,6 +104,24 @@ def test_extreme_values_exact():
     _run(d, W.AZP_PER_TOKEN, out_dtype=W.OUT_I32)
 
 
+@pytest.mark.parametrize("M,N", [(130, 64), (260, 520)])
+def test_tile_extreme_zero_point_product(M, N):
+    """The MFMA tile path's per-token correction zp * colsum at the top of its
+    range: K = 65536 codes of -128, weight rows of -128 (colsum = -2^23) and
+    of 127, zero points 127 and -128; every corrected sum fits int32 and must
+    come out exact."""
+    K = 65536
+    d = _inputs(M, K, N, seed=6)
+    d["xq"][:] = -128
+    d["w"][0::2] = -128
+    d["w"][1::2] = 127
+    d["zp"][0::2] = 127
+    d["zp"][1::2] = -128
+    assert W.scaled_mm_kernel_name(M, N, K).startswith("gemm_i8_dma_kernel")
+    _run(d, W.AZP_PER_TOKEN, out_dtype=W.OUT_I32)
+    _run(d, W.AZP_PER_TOKEN, bias=True)
+
+
 def test_deterministic_repeat():
     d = _inputs(64, 4096, 1000, seed=5)
     xq, w = to_dev(d["xq"]), to_dev(d["w"])

@@ -119,6 +119,15 @@ def test_fp8_convert(E, N, K):
     _fp8_check(codes, S)
 
 
+# More rows than the launch has lane groups: 6144 groups of 64 lanes (K = 3072)
+# or 12288 of 32 (K = 1536), so every group walks several rows through its
+# two-row ring (the next row's codes and scales load while one converts).
+@pytest.mark.parametrize("E,N,K", [(3, 2100, 3072), (4, 3200, 1536)])
+def test_fp8_convert_rows_past_the_grid(E, N, K):
+    codes, S = synth.fp8_block_weight(synth.rng_for(915, E, N, K), E, N, K)
+    _fp8_check(codes, S)
+
+
 def test_fp8_all_codes_and_zero_rows():
     """Every one of the 254 non-NaN codes under unit and odd scales, plus
     all-zero (and negative-zero) rows."""

@@ -59,6 +59,16 @@ def test_many_rows_ragged(mode):
     _check(_x(1027, 1536, 0.3, 4, seed=1), mode)
 
 
+# Batches past 256 rows take 256 threads per row up to K = 16384 (so 2, 7 -> 8
+# chunks per thread at K = 4096, 14336; 2 at 3072) and 1024 beyond: the
+# instances the prefill (2048 / 8192 x 4096 / 14336) and MoE (4096 x 3072)
+# activations run, compared in full.
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("M,K", [(2048, 4096), (2048, 14336), (4096, 3072), (300, 20480)])
+def test_dynamic_large_batches(mode, M, K):
+    _check(_x(M, K, 0.3 if mode == W.QUANT_DYN_ASYM else 0.0, int(round(0.005 * K)), seed=5), mode)
+
+
 @pytest.mark.parametrize("mode", MODES)
 def test_strided(mode):
     _check(_x(37, 272, 0.1, 2, seed=2), mode, ldx=288, ldq=304)
