@@ -15,8 +15,9 @@
  *
  * Conventions for every call:
  *  - Pointers are device pointers unless marked "host". Every buffer is owned
- *    by the caller; the library allocates no device memory and keeps no state
- *    besides a per-device property cache.
+ *    by the caller; the library allocates no device memory at run time and
+ *    keeps no state besides a per-device property cache and, for
+ *    w8a8_scaled_mm_int8_noalloc, one static scratch array per GPU.
  *  - "stream" is a hipStream_t (NULL = the null stream). Work is enqueued
  *    asynchronously on it; nothing synchronises.
  *  - Matrices are row-major; ld* are row strides in elements.
@@ -92,6 +93,9 @@ enum {
 #define W8A8_MAX_K 65536
 /* Largest number of partitions of a fused weight in w8a8_prepare_requant_max. */
 #define W8A8_MAX_PARTITIONS 16
+/* Bytes of the static scratch array behind w8a8_scaled_mm_int8_noalloc (8 MiB,
+ * one per GPU): the largest w8a8_scaled_mm_workspace_size of any shape. */
+#define W8A8_NOALLOC_SCRATCH_BYTES (8 << 20)
 
 /* The quantisation scheme of one linear layer, as its checkpoint declares it
  * ([vLLM] 4.1: bit widths, strategy, dynamic flag and symmetry of the weight
@@ -231,6 +235,27 @@ w8a8_status w8a8_scaled_mm_int8(const int8_t* xq, int64_t M, int64_t K, int64_t 
                                 const uint16_t* bias, void* out, int32_t out_dtype,
                                 int64_t ldo, void* workspace, size_t workspace_bytes,
                                 void* stream);
+
+/* w8a8_scaled_mm_int8 without a workspace argument and without allocating,
+ * for callers that cannot allocate device memory around the call (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ * Same arguments, requirements and results as w8a8_scaled_mm_int8 given a
+ * workspace of w8a8_scaled_mm_workspace_size(M, N, K) bytes: the split-K
+ * partial tiles of the decode shapes go to a static device array of
+ * W8A8_NOALLOC_SCRATCH_BYTES that the library holds on each GPU until the
+ * process ends (its address is looked up in w8a8_init, or on the first call
+ * on a device). A shape that would need more scratch than that returns
+ * W8A8_ERR_INVALID_ARG (no valid shape does today). Every call on one GPU
+ * shares that GPU's array and it keeps the last call's contents: calls that
+ * may overlap on one GPU (several streams, several host threads) race and
+ * must be ordered by the caller. Nothing in the array needs to start at zero. */
+w8a8_status w8a8_scaled_mm_int8_noalloc(const int8_t* xq, int64_t M, int64_t K, int64_t ldx,
+                                        const int8_t* Wq, int64_t N, int64_t ldw,
+                                        const float* s_x, int32_t s_x_per_token,
+                                        const float* s_w, int32_t s_w_per_channel,
+                                        const int32_t* zp, const int32_t* colsum,
+                                        int32_t azp_mode, const uint16_t* bias, void* out,
+                                        int32_t out_dtype, int64_t ldo, void* stream);
 
 /* The dynamic per-token symmetric linear layer in one call: w8a8_quantize_act
  * (W8A8_QUANT_DYN_SYM) of x into xq / s_x, then w8a8_scaled_mm_int8 with

@@ -1,6 +1,7 @@
 // The C ABI of libw8a8 (declared in include/w8a8.h): host-side validation,
 // scheme checking, kernel dispatch and error reporting. No device memory is
-// allocated here; all buffers belong to the caller.
+// allocated at run time: buffers belong to the caller, apart from the one
+// static scratch array of the no-allocation GEMM entry point below.
 
 #include <hip/hip_runtime.h>
 
@@ -8,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "launch.h"
@@ -67,6 +69,40 @@ w8a8_status check_current_device() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// The scratch buffer of w8a8_scaled_mm_int8_noalloc: the decode GEMM's split-K
+// partial tiles, in a device array the library owns (one copy per GPU, kept
+// until the process ends). Host code never uses the array's name as an
+// address: each device's copy is looked up once with hipGetSymbolAddress and
+// that pointer is what the kernels receive. The split kernels write every
+// partial they later read, so nothing in it needs to start at zero.
+static __device__ __align__(256) uint8_t scratch[W8A8_NOALLOC_SCRATCH_BYTES];
+
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `dev`'s copy of the scratch array, looked up with that
+// device current the first time it is asked for.
+w8a8_status scratch_for(int dev, void** out) {
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+      int cur = 0;
+      hipError_t e = hipGetDevice(&cur);
+      if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+      if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_status(e, "hipSetDevice");
+      const hipError_t eg = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (cur != dev && (e = hipSetDevice(cur)) != hipSuccess) return hip_status(e, "hipSetDevice");
+      if (eg != hipSuccess) return hip_status(eg, "hipGetSymbolAddress(scratch)");
+      if (p == nullptr) return fail(W8A8_ERR_HIP, "hipGetSymbolAddress(scratch) gave a null address");
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return W8A8_OK;
+}
+
 #define W8A8_REQUIRE(cond, ...) \
   do {                          \
     if (!(cond)) return fail(W8A8_ERR_INVALID_ARG, __VA_ARGS__); \
@@ -100,6 +136,9 @@ extern "C" {
 
 w8a8_status w8a8_init(int device) {
   w8a8_status st = check_device(device);
+  if (st != W8A8_OK) return st;
+  void* p = nullptr;
+  st = scratch_for(device, &p);  // the no-allocation entry point's buffer on this GPU
   return st == W8A8_OK ? ok() : st;
 }
 
@@ -261,12 +300,14 @@ static w8a8_status check_gemm_common(const int8_t* xq, int64_t ldx, const int8_t
   return W8A8_OK;
 }
 
-w8a8_status w8a8_scaled_mm_int8(const int8_t* xq, int64_t M, int64_t K, int64_t ldx, const int8_t* Wq,
-                                int64_t N, int64_t ldw, const float* s_x, int32_t s_x_per_token,
-                                const float* s_w, int32_t s_w_per_channel, const int32_t* zp,
-                                const int32_t* colsum, int32_t azp_mode, const uint16_t* bias, void* out,
-                                int32_t out_dtype, int64_t ldo, void* workspace, size_t workspace_bytes,
-                                void* stream) {
+// Shared body of w8a8_scaled_mm_int8 and w8a8_scaled_mm_int8_noalloc.
+// noalloc: the workspace is the current device's static scratch array.
+static w8a8_status scaled_mm_impl(const int8_t* xq, int64_t M, int64_t K, int64_t ldx, const int8_t* Wq,
+                                  int64_t N, int64_t ldw, const float* s_x, int32_t s_x_per_token,
+                                  const float* s_w, int32_t s_w_per_channel, const int32_t* zp,
+                                  const int32_t* colsum, int32_t azp_mode, const uint16_t* bias, void* out,
+                                  int32_t out_dtype, int64_t ldo, void* workspace, size_t workspace_bytes,
+                                  bool noalloc, void* stream) {
   w8a8_status st;
   if ((st = check_dim(M, "M")) != W8A8_OK) return st;
   if ((st = check_dim(N, "N")) != W8A8_OK) return st;
@@ -281,6 +322,17 @@ w8a8_status w8a8_scaled_mm_int8(const int8_t* xq, int64_t M, int64_t K, int64_t 
   if ((st = check_tiles(M, 0, N)) != W8A8_OK) return st;
   W8A8_REQUIRE(workspace == nullptr || aligned16(workspace), "workspace must be 16-byte aligned");
   if ((st = check_current_device()) != W8A8_OK) return st;
+  if (noalloc) {
+    const size_t need = M <= w8a8::kDecodeMaxM ? w8a8::decode_workspace_bytes(M, N, K) : 0;
+    W8A8_REQUIRE(need <= W8A8_NOALLOC_SCRATCH_BYTES,
+                 "shape %lld x %lld x %lld needs %zu bytes of scratch; the static buffer holds %d",
+                 (long long)M, (long long)N, (long long)K, need, W8A8_NOALLOC_SCRATCH_BYTES);
+    int dev = 0;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+    if ((st = scratch_for(dev, &workspace)) != W8A8_OK) return st;
+    workspace_bytes = W8A8_NOALLOC_SCRATCH_BYTES;
+  }
   w8a8::GemmArgs a{};
   a.A = xq;
   a.lda = ldx;
@@ -305,6 +357,26 @@ w8a8_status w8a8_scaled_mm_int8(const int8_t* xq, int64_t M, int64_t K, int64_t 
                            ? w8a8::launch_decode_mm(a, workspace, workspace_bytes, s)
                            : w8a8::launch_scaled_mm(a, s);
   return hip_status(e, "scaled_mm launch");
+}
+
+w8a8_status w8a8_scaled_mm_int8(const int8_t* xq, int64_t M, int64_t K, int64_t ldx, const int8_t* Wq,
+                                int64_t N, int64_t ldw, const float* s_x, int32_t s_x_per_token,
+                                const float* s_w, int32_t s_w_per_channel, const int32_t* zp,
+                                const int32_t* colsum, int32_t azp_mode, const uint16_t* bias, void* out,
+                                int32_t out_dtype, int64_t ldo, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  return scaled_mm_impl(xq, M, K, ldx, Wq, N, ldw, s_x, s_x_per_token, s_w, s_w_per_channel, zp, colsum,
+                        azp_mode, bias, out, out_dtype, ldo, workspace, workspace_bytes, false, stream);
+}
+
+w8a8_status w8a8_scaled_mm_int8_noalloc(const int8_t* xq, int64_t M, int64_t K, int64_t ldx,
+                                        const int8_t* Wq, int64_t N, int64_t ldw, const float* s_x,
+                                        int32_t s_x_per_token, const float* s_w, int32_t s_w_per_channel,
+                                        const int32_t* zp, const int32_t* colsum, int32_t azp_mode,
+                                        const uint16_t* bias, void* out, int32_t out_dtype, int64_t ldo,
+                                        void* stream) {
+  return scaled_mm_impl(xq, M, K, ldx, Wq, N, ldw, s_x, s_x_per_token, s_w, s_w_per_channel, zp, colsum,
+                        azp_mode, bias, out, out_dtype, ldo, nullptr, 0, true, stream);
 }
 
 w8a8_status w8a8_linear_dyn_sym(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const int8_t* Wq,

@@ -31,6 +31,7 @@ OUT_BF16, OUT_I32 = range(2)
 FLAG_NAN_CODE, FLAG_BAD_SCALE, FLAG_NONFINITE = 1, 2, 4
 MAX_K = 65536
 MAX_PARTITIONS = 16
+NOALLOC_SCRATCH_BYTES = 8 << 20
 
 
 class Scheme(ctypes.Structure):
@@ -53,6 +54,8 @@ _SIGS = {
     "w8a8_scaled_mm_workspace_size": (ctypes.c_size_t, [_i64, _i64, _i64]),
     "w8a8_scaled_mm_int8": (_i32, [_p, _i64, _i64, _i64, _p, _i64, _i64, _p, _i32, _p, _i32,
                                    _p, _p, _i32, _p, _p, _i32, _i64, _p, ctypes.c_size_t, _p]),
+    "w8a8_scaled_mm_int8_noalloc": (_i32, [_p, _i64, _i64, _i64, _p, _i64, _i64, _p, _i32, _p, _i32,
+                                           _p, _p, _i32, _p, _p, _i32, _i64, _p]),
     "w8a8_grouped_scaled_mm_int8": (_i32, [_p, _i64, _i64, _p, _p, _i64, _i64, _i64, _i64, _p,
                                            _p, _p, _p, _p, _i32, _i64, _p]),
     "w8a8_linear_dyn_sym": (_i32, [_p, _i64, _i64, _i64, _p, _i64, _i64, _p, _i32, _p, _p, _i64,
@@ -265,6 +268,27 @@ def scaled_mm_int8(xq, Wq, s_x, s_w, zp=None, colsum=None, azp_mode: int = AZP_N
                                     _ptr(bias), _ptr(out), out_dtype, out.stride(0) if M else N,
                                     _ptr(workspace), ws_bytes, _stream())
     _raise(st, "w8a8_scaled_mm_int8")
+    return out
+
+
+def scaled_mm_int8_noalloc(xq, Wq, s_x, s_w, zp=None, colsum=None, azp_mode: int = AZP_NONE, bias=None,
+                           out_dtype: int = OUT_BF16, out=None):
+    """scaled_mm_int8 through the entry point that allocates nothing: split-K
+    partials live in the library's static per-GPU scratch array (calls that
+    overlap on one GPU race). `out` is allocated here when not given; pass it
+    where nothing may be allocated."""
+    import torch
+    M, K = xq.shape
+    N = Wq.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16 if out_dtype == OUT_BF16 else torch.int32,
+                          device=xq.device)
+    st = load().w8a8_scaled_mm_int8_noalloc(_ptr(xq), M, K, xq.stride(0), _ptr(Wq), N, Wq.stride(0),
+                                            _ptr(s_x), int(s_x.numel() != 1 or M == 1), _ptr(s_w),
+                                            int(s_w.numel() != 1 or N == 1), _ptr(zp), _ptr(colsum),
+                                            azp_mode, _ptr(bias), _ptr(out), out_dtype,
+                                            out.stride(0) if M else N, _stream())
+    _raise(st, "w8a8_scaled_mm_int8_noalloc")
     return out
 
 

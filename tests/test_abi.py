@@ -16,7 +16,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = W.header_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -178,3 +178,27 @@ def test_prepare_rejects_before_device_work(L):
     assert L.w8a8_prepare_fp8_block_to_int8(FAKE, FAKE, 0, 64, 64, FAKE, FAKE, FAKE, None) == W.OK
     assert L.w8a8_prepare_colsum(FAKE, 16, 48, 40, None, FAKE, None) == W.ERR_INVALID_ARG
     assert L.w8a8_prepare_colsum(FAKE, 0, 48, 48, None, FAKE, None) == W.OK
+
+
+def test_noalloc_scratch_covers_every_workspace():
+    """No shape asks the no-allocation GEMM for more split-K scratch than its
+    static array holds: the workspace sizes (host arithmetic only) over the
+    decode range of M, N up to past the split limit and K up to the maximum."""
+    worst = 0
+    for M in range(1, 129):
+        for N in (16, 100, 1000, 4096, 6144, 8064, 8192, 8200, 16384):
+            for K in (128, 1024, 8192, 14336, 65536):
+                worst = max(worst, W.scaled_mm_workspace_size(M, N, K))
+    assert 0 < worst <= W.NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_rejects_before_device_work(L):
+    def mm(M=4, K=64, N=8, ldx=64, ldw=64, ldo=8, azp=0, out_dtype=0, xq=FAKE, w=FAKE, out=FAKE):
+        return L.w8a8_scaled_mm_int8_noalloc(xq, M, K, ldx, w, N, ldw, FAKE, 1, FAKE, 1, None, None, azp,
+                                             None, out, out_dtype, ldo, None)
+    assert mm(K=40, ldx=48, ldw=48) == W.ERR_INVALID_ARG    # K % 16
+    assert mm(xq=None) == W.ERR_INVALID_ARG
+    assert mm(ldo=4) == W.ERR_INVALID_ARG
+    assert mm(azp=W.AZP_PER_TOKEN) == W.ERR_INVALID_ARG     # zp / colsum missing
+    assert mm(out_dtype=5) == W.ERR_INVALID_ARG
+    assert mm(M=0) == W.OK
