@@ -39,7 +39,10 @@ brute force of every rounding decision on small rows, the half-step error
 bound, the argmax/argmin mapping, sign and power-of-two symmetries, the
 all-zero-row rule, a pure-Python integer GEMM, the dequantise-then-matmul
 identity, the OCP E4M3FN decoding against torch's float8_e4m3fn and hand
-values, and hand-computed worked examples under ``tests/golden/``.
+values, hand-computed worked examples under ``tests/golden/``, and for the MoE
+block: brute-force routing and sorting, closed forms and identities of the
+SiLU product and the combine, and the whole block against a float64
+dequantise-then-compute MoE layer.
 """
 
 from __future__ import annotations
@@ -64,6 +67,11 @@ __all__ = [
     "e4m3fn_table",
     "fp8_block_to_int8",
     "grouped_scaled_mm",
+    "moe_topk",
+    "moe_sort",
+    "silu_mul_bf16",
+    "moe_combine",
+    "moe_block",
     "linear_forward",
     "FLAG_NAN_CODE",
     "FLAG_BAD_SCALE",
@@ -427,3 +435,101 @@ def grouped_scaled_mm(xq, s_x, w, s_w, expert_offsets, row_ids=None, bias_bits=N
         out[r0:r1] = o
         cc[r0:r1] = c
     return out, cc
+
+
+# ------------------------------------------------------- MoE expert block --
+#
+# The int8 MoE method of [Kunlun] 版本 keeps the experts' w1 / w2 / w3, which
+# vLLM fuses (w1 and w3 into one w13) and runs with per-token dynamic
+# symmetric int8 activations and per-output-channel symmetric int8 weights;
+# [SGLang] 구조도 lists the same scheme (the w8a8_int8 MoE). The pages give
+# no formula for the routing, the activation between w13 and w2 or the
+# combine; the readings below are the plain ones:
+#  * routing: each token takes the k experts with the largest router logits
+#    (equal logits: the lower expert index first), weighted by the softmax of
+#    those k logits;
+#  * w13's rows are the gate (w1) rows followed by the up (w3) rows; the
+#    activation is silu(gate) * up, silu(g) = g / (1 + exp(-g)), taken in the
+#    bf16 dtype the GEMM returns and quantised per token for w2;
+#  * the token's output is the weighted sum of its k expert outputs.
+
+
+def moe_topk(logits, k):
+    """Top-k routing: for each token (row of the float32 logits [tokens, E])
+    the k experts with the largest logits, largest first, equal logits taken
+    in increasing expert order; weights = softmax of the selected logits
+    (the softmax over all experts restricted to the k and renormalised, which
+    is the same quantity), computed in float64.
+    Returns (ids int32 [tokens, k], weights float64 [tokens, k])."""
+    lg = np.asarray(logits, dtype=np.float32)
+    T, E = lg.shape
+    assert 1 <= k <= E
+    # a stable sort on the negated logits keeps equal logits in index order
+    ids = np.argsort(-lg.astype(np.float64), axis=1, kind="stable")[:, :k].astype(np.int32)
+    sel = np.take_along_axis(lg, ids, axis=1).astype(np.float64)
+    ex = np.exp(sel - sel[:, :1])
+    return ids, ex / ex.sum(axis=1, keepdims=True)
+
+
+def moe_sort(ids, E):
+    """Expert-sorted order of the routed (token, expert) pairs: sorted by
+    expert, then by token. Returns (row_ids int32 [T]: the token of each sorted
+    row; expert_offsets int32 [E+1]: where each expert's rows start; pos int32
+    [tokens, k]: the sorted row of the pair (t, ids[t, j]))."""
+    ids = np.asarray(ids, dtype=np.int64)
+    tokens, k = ids.shape
+    tok = np.repeat(np.arange(tokens), k)
+    exp = ids.reshape(-1)
+    order = np.lexsort((tok, exp))  # primary key expert, then token
+    row_ids = tok[order].astype(np.int32)
+    offsets = np.zeros(E + 1, np.int64)
+    offsets[1:] = np.cumsum(np.bincount(exp, minlength=E))
+    pos = np.empty(tokens * k, np.int64)
+    pos[order] = np.arange(tokens * k)
+    return row_ids, offsets.astype(np.int32), pos.reshape(tokens, k).astype(np.int32)
+
+
+def silu_mul_bf16(h_bits, inter):
+    """The activated product of the fused w13 output h (bf16 bits [T, 2*inter]):
+    gate = h[:, :inter], up = h[:, inter:], a = silu(gate) * up with
+    silu(g) = g / (1 + exp(-g)), formed in float64 from the bf16 values and
+    rounded once to bf16. Returns bf16 bits [T, inter]."""
+    h = bf16_bits_to_f32(h_bits).astype(np.float64)
+    g, u = h[:, :inter], h[:, inter:2 * inter]
+    with np.errstate(over="ignore"):
+        a = g / (1.0 + np.exp(-g)) * u
+    return f64_to_bf16_bits(a)
+
+
+def moe_combine(y_bits, pos, weights):
+    """out[t] = sum_j weights[t, j] * y[pos[t, j]] (y: the expert outputs in
+    sorted order, bf16 bits [T, N]), formed in float64 and rounded once to
+    bf16. Returns bf16 bits [tokens, N]."""
+    y = bf16_bits_to_f32(y_bits).astype(np.float64)
+    w = np.asarray(weights, dtype=np.float64)
+    pos = np.asarray(pos, dtype=np.int64)
+    acc = np.zeros((pos.shape[0], y.shape[1]), np.float64)
+    for j in range(pos.shape[1]):
+        acc += w[:, j:j + 1] * y[pos[:, j]]
+    return f64_to_bf16_bits(acc)
+
+
+def moe_block(x_bits, logits, k, w13, s13, w2, s2):
+    """The int8 MoE expert block, step by step: per-token symmetric
+    quantisation of x [tokens, H]; top-k routing; the grouped w13 GEMM
+    (w13 int8 [E, 2I, H], per-row scales s13 [E, 2I]) on each routed row;
+    silu(gate) * up in bf16; per-token symmetric quantisation of that; the
+    grouped w2 GEMM (w2 int8 [E, H, I], s2 [E, H]); the weighted combine.
+    Returns a dict of every intermediate and the output (bf16 bits)."""
+    E, two_i, H = w13.shape
+    inter = two_i // 2
+    xq, sx = quant_dyn_sym(x_bits)
+    ids, wts = moe_topk(logits, k)
+    row_ids, offsets, pos = moe_sort(ids, E)
+    h, _ = grouped_scaled_mm(xq, sx, w13, s13, offsets, row_ids=row_ids)
+    act = silu_mul_bf16(h, inter)
+    aq, sa = quant_dyn_sym(act)
+    y, _ = grouped_scaled_mm(aq, sa, w2, s2, offsets)
+    out = moe_combine(y, pos, wts)
+    return dict(xq=xq, sx=sx, ids=ids, weights=wts, row_ids=row_ids, offsets=offsets, pos=pos,
+                h=h, act=act, aq=aq, sa=sa, y=y, out=out)

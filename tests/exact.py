@@ -64,6 +64,22 @@ def nearest_f32(fr: Fraction) -> Fraction:
     return sign * n * quantum
 
 
+def nearest_bf16(fr: Fraction) -> Fraction:
+    """Correctly rounded bf16 value of an exact rational (ties to even): 8
+    significant bits, spacing 2**-133 below 2**-126. Overflow is not handled."""
+    if fr == 0:
+        return Fraction(0)
+    sign = -1 if fr < 0 else 1
+    a = abs(fr)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    elif Fraction(2) ** (e + 1) <= a:
+        e += 1
+    quantum = Fraction(2) ** max(e - 7, -133)
+    return sign * round_half_even(a / quantum) * quantum
+
+
 def clamp(v: int, lo: int, hi: int) -> int:
     return lo if v < lo else hi if v > hi else v
 
