@@ -433,10 +433,12 @@ def extra_sections(torch, np, W, synth, to_dev, timer, dev):
 
     # MoE: FP8 -> int8 conversion of the expert weights, then the two grouped GEMMs.
     m = synth.moe()
-    E = synth.MOE_E
-    T = m["row_ids"].shape[0]
-    rows = to_dev(m["row_ids"])
-    offs = to_dev(m["offsets"])
+    E, topk = synth.MOE_E, m["topk"]
+    tokens = m["x13"].shape[0]
+    T = tokens * topk
+    logits = to_dev(m["logits"])
+    # the routing and expert sort on the device (the block's own first step)
+    _, _, rows, offs, _ = W.moe_route(logits, topk)
     conv = {}
     qw = {}
     for name in ("w13", "w2"):
@@ -482,8 +484,55 @@ def extra_sections(torch, np, W, synth, to_dev, timer, dev):
     moe["quant_w2_input_32768x1536"] = {"us": round(qus, 1),
                                          "GBs": round(quant_bytes(T, 1536) / (qus * 1e-6) / 1e9, 1)}
     out["moe_grouped"] = moe
+    del xq2, sx2, x2
+    out["moe_block"] = moe_block_section(torch, W, timer, dev, x13, logits, topk, qw)
     torch.cuda.synchronize()
     return out
+
+
+def moe_block_section(torch, W, timer, dev, x, logits, topk, qw):
+    """The whole int8 MoE expert block on the MoE workload (4096 tokens, top-8
+    of 64 experts, hidden 3072, intermediate 1536, the converted expert
+    weights): one w8a8_moe_block_int8 call, and each of its steps alone."""
+    (w13, s13), (w2, s2) = qw["w13"], qw["w2"]
+    tokens, H = x.shape
+    E = logits.shape[1]
+    I = w2.shape[2]
+    T = tokens * topk
+    ws = torch.empty(W.moe_block_workspace_size(tokens, E, topk, H, I), dtype=torch.uint8, device=dev)
+    o = torch.empty((tokens, H), dtype=torch.bfloat16, device=dev)
+    R = 5
+    g = capture(torch, lambda: [W.moe_block_int8(x, logits, topk, w13, s13, w2, s2, out=o, workspace=ws)
+                                for _ in range(R)])
+    us = timer.graph_us(g, R)
+    del g
+    ops = 2.0 * T * (2 * I) * H + 2.0 * T * H * I
+    res = {"block_us": round(us, 1), "TOPS": round(ops / (us * 1e-6) / 1e12, 1),
+           "mfma_frac": round(ops / (us * 1e-6) / 1e12 / INT8_PEAK_TOPS, 4)}
+    # the steps around the grouped GEMMs, each as a graph of back-to-back launches
+    rws = torch.empty(max(16, int(W.load().w8a8_moe_route_workspace_size(tokens, E))), dtype=torch.uint8,
+                      device=dev)
+    routed = W.moe_route(logits, topk, workspace=rws)
+    g = capture(torch, lambda: [W.moe_route(logits, topk, workspace=rws, out=routed) for _ in range(R)])
+    res["route_us"] = round(timer.graph_us(g, R), 2)
+    h = torch.randn((T, 2 * I), device=dev).to(torch.bfloat16)
+    aq = torch.empty((T, I), dtype=torch.int8, device=dev)
+    sa = torch.empty(T, dtype=torch.float32, device=dev)
+    g = capture(torch, lambda: [W.silu_mul_quant(h, I, aq=aq, s_a=sa) for _ in range(R)])
+    sus = timer.graph_us(g, R)
+    sb = T * 2 * I * 2 + T * I + 4 * T
+    res["silu_mul_quant_us"] = round(sus, 1)
+    res["silu_mul_quant_GBs"] = round(sb / (sus * 1e-6) / 1e9, 1)
+    del h, aq
+    y = torch.randn((T, H), device=dev).to(torch.bfloat16)
+    _, wts, _, _, pos = routed
+    g = capture(torch, lambda: [W.moe_combine(y, pos, wts, out=o) for _ in range(R)])
+    cus = timer.graph_us(g, R)
+    cb = T * H * 2 + tokens * H * 2 + T * 8
+    res["combine_us"] = round(cus, 1)
+    res["combine_GBs"] = round(cb / (cus * 1e-6) / 1e9, 1)
+    del g, y, ws
+    return res
 
 
 def cpu_baseline(np, synth, shapes, min_seconds):

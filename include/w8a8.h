@@ -304,6 +304,78 @@ w8a8_status w8a8_grouped_scaled_mm_int8(const int8_t* xq, int64_t ldx, int64_t M
                                         const uint16_t* bias, void* out, int32_t out_dtype,
                                         int64_t ldo, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * The int8 MoE expert block around the grouped GEMM: the int8 MoE method of
+ * [Kunlun] 版本 (experts w1 / w2 / w3, with w1 and w3 fused into one w13;
+ * per-token dynamic symmetric int8 activations, per-output-channel symmetric
+ * int8 weights) and the w8a8 int8 MoE scheme of [SGLang] 구조도. The pages
+ * give no formula for the routing, the activation or the combine; these calls
+ * take the plain readings stated with each. */
+
+/* Bytes of workspace w8a8_moe_route needs (0 for an invalid shape). */
+size_t w8a8_moe_route_workspace_size(int64_t tokens, int64_t E);
+
+/* Top-k routing and the expert sort. For each token (row of the float router
+ * logits [tokens, E], row stride ldl) the topk experts with the largest
+ * logits, largest first, equal logits taken in increasing expert order:
+ * topk_ids int32 [tokens, topk]; topk_w float [tokens, topk] = the softmax of
+ * the selected logits. The routed (token, expert) pairs sorted by expert,
+ * then token: row_ids int32 [tokens*topk] (the token of each sorted row),
+ * expert_offsets int32 [E+1] (where each expert's rows start; the grouped
+ * GEMM's input), pos int32 [tokens, topk] (the sorted row of each pair; the
+ * combine's input). The result is fully determined (no atomics decide an
+ * order). workspace: 16-byte aligned, w8a8_moe_route_workspace_size bytes,
+ * no state kept. 1 <= E <= 512, 1 <= topk <= min(E, 16); NaN logits are
+ * outside the contract. */
+w8a8_status w8a8_moe_route(const float* logits, int64_t ldl, int64_t tokens, int64_t E,
+                           int32_t topk, int32_t* topk_ids, float* topk_w, int32_t* row_ids,
+                           int32_t* expert_offsets, int32_t* pos, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* The activated product of a fused w13 output and its per-token symmetric
+ * quantisation, the w2 GEMM's input: h bf16 [T, 2*I] (ldh) holds the gate
+ * (w1) columns [0, I) and the up (w3) columns [I, 2*I);
+ *   a = bf16(silu(gate) * up),  silu(g) = g / (1 + exp(-g))   (binary32)
+ *   s_a[t] = max|a_t| / 127,  aq = clamp(rne(a / s_a[t]), -127, 127)
+ * with the rule and exact rounding of w8a8_quantize_act (W8A8_QUANT_DYN_SYM)
+ * on the bf16 values a. aq int8 [T, I] (ldq), s_a float [T]; act (nullable)
+ * receives a itself, bf16 [T, I] (ld_act). I % 16 == 0, I <= 16384; h, aq,
+ * act 16-byte aligned, ldh % 8 == 0, ldq % 16 == 0, ld_act % 8 == 0. */
+w8a8_status w8a8_silu_mul_quant(const uint16_t* h, int64_t T, int64_t I, int64_t ldh, int8_t* aq,
+                                int64_t ldq, float* s_a, uint16_t* act, int64_t ld_act,
+                                void* stream);
+
+/* The weighted combine of a token's expert outputs:
+ *   out[t, :] = bf16( sum_j topk_w[t, j] * y[pos[t, j], :] )
+ * (binary32 fused multiply-adds in the order j = 0 .. topk-1). y bf16 [.., N]
+ * (ldy) in sorted order, pos / topk_w [tokens, topk] as w8a8_moe_route
+ * writes them, out bf16 [tokens, N] (ldo). pos values must lie inside y.
+ * 1 <= topk <= 16, N % 8 == 0; y and out 16-byte aligned, ldy, ldo
+ * multiples of 8. */
+w8a8_status w8a8_moe_combine(const uint16_t* y, int64_t ldy, const int32_t* pos,
+                             const float* topk_w, int64_t tokens, int32_t topk, int64_t N,
+                             uint16_t* out, int64_t ldo, void* stream);
+
+/* Bytes of workspace w8a8_moe_block_int8 needs (0 for an invalid shape). */
+size_t w8a8_moe_block_workspace_size(int64_t tokens, int64_t E, int32_t topk, int64_t H,
+                                     int64_t I);
+
+/* The whole int8 MoE expert block for bf16 tokens x [tokens, H] (ldx):
+ * per-token symmetric quantisation of x; w8a8_moe_route on the logits
+ * [tokens, E] (ldl); the grouped GEMM of each routed row with its expert's
+ * w13 (int8 [E, 2*I, H], per-row scales s13 float [E, 2*I]) into bf16;
+ * w8a8_silu_mul_quant; the grouped GEMM with w2 (int8 [E, H, I], s2 float
+ * [E, H]) into bf16; w8a8_moe_combine into out bf16 [tokens, H] (ldo). The
+ * results are those of the separate calls in that order. workspace:
+ * 16-byte aligned, w8a8_moe_block_workspace_size bytes, holding every
+ * intermediate (no state kept). H % 16 == 0, H <= W8A8_MAX_K, I % 16 == 0,
+ * I <= 16384, E <= 512, topk <= min(E, 16). */
+w8a8_status w8a8_moe_block_int8(const uint16_t* x, int64_t ldx, const float* logits, int64_t ldl,
+                                int64_t tokens, int64_t E, int32_t topk, int64_t H, int64_t I,
+                                const int8_t* w13, const float* s13, const int8_t* w2,
+                                const float* s2, uint16_t* out, int64_t ldo, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 /* Name of the kernel template instance that w8a8_scaled_mm_int8 launches
  * for an M x N x K problem (static storage; "" for an empty or invalid
  * shape). Profilers list kernels by these names; no device is touched. */

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libw8a8.so")
 OBJDIR = os.path.join(HERE, "_build")
 
-SOURCES = ["api.cpp", "quant.hip", "prepare.hip", "gemm.hip", "gemv.hip"]
+SOURCES = ["api.cpp", "quant.hip", "prepare.hip", "gemm.hip", "gemv.hip", "moe.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -478,6 +478,217 @@ w8a8_status w8a8_grouped_scaled_mm_int8(const int8_t* xq, int64_t ldx, int64_t M
   return hip_status(w8a8::launch_grouped_mm(a, static_cast<hipStream_t>(stream)), "grouped_mm launch");
 }
 
+}  // extern "C"
+
+// ------------------------------------------------------------ MoE block
+
+namespace {
+
+constexpr int kMoeMaxExperts = 512;
+constexpr int kMoeMaxTopk = 16;
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+size_t route_ws_bytes(int64_t tokens, int64_t E) {
+  return align256((size_t)w8a8::moe_route_chunks(tokens) * (size_t)E * sizeof(uint64_t));
+}
+
+w8a8_status check_moe_shape(int64_t tokens, int64_t E, int32_t topk) {
+  w8a8_status st;
+  if ((st = check_dim(tokens, "tokens")) != W8A8_OK) return st;
+  W8A8_REQUIRE(E >= 1 && E <= kMoeMaxExperts, "E=%lld outside [1, %d]", (long long)E, kMoeMaxExperts);
+  W8A8_REQUIRE(topk >= 1 && topk <= kMoeMaxTopk && topk <= E, "topk=%d outside [1, min(E, %d)]", topk,
+               kMoeMaxTopk);
+  W8A8_REQUIRE(tokens * topk < kMaxDim, "tokens*topk=%lld routed rows exceed 2^26", (long long)(tokens * topk));
+  return W8A8_OK;
+}
+
+// Where each intermediate of w8a8_moe_block_int8 sits in its workspace
+// (256-byte aligned pieces; the w2 output reuses the w13 output's bytes,
+// which are dead once the activated product is quantised).
+struct MoeLayout {
+  size_t xq, sx, ids, wts, row_ids, offsets, pos, masks, h, aq, sa, y, total;
+};
+
+MoeLayout moe_layout(int64_t tokens, int64_t E, int32_t topk, int64_t H, int64_t I) {
+  MoeLayout L{};
+  const size_t T = (size_t)tokens * (size_t)topk;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align256(bytes);
+    return at;
+  };
+  L.xq = take((size_t)tokens * H);
+  L.sx = take((size_t)tokens * 4);
+  L.ids = take(T * 4);
+  L.wts = take(T * 4);
+  L.row_ids = take(T * 4);
+  L.offsets = take((size_t)(E + 1) * 4);
+  L.pos = take(T * 4);
+  L.masks = take(route_ws_bytes(tokens, E));
+  L.aq = take(T * (size_t)I);
+  L.sa = take(T * 4);
+  const size_t h_bytes = T * (size_t)(2 * I) * 2, y_bytes = T * (size_t)H * 2;
+  L.h = take(h_bytes > y_bytes ? h_bytes : y_bytes);
+  L.y = L.h;
+  L.total = o;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t w8a8_moe_route_workspace_size(int64_t tokens, int64_t E) {
+  if (tokens <= 0 || tokens >= kMaxDim || E <= 0 || E > kMoeMaxExperts) return 0;
+  return route_ws_bytes(tokens, E);
+}
+
+w8a8_status w8a8_moe_route(const float* logits, int64_t ldl, int64_t tokens, int64_t E, int32_t topk,
+                           int32_t* topk_ids, float* topk_w, int32_t* row_ids, int32_t* expert_offsets,
+                           int32_t* pos, void* workspace, size_t workspace_bytes, void* stream) {
+  w8a8_status st;
+  if ((st = check_moe_shape(tokens, E, topk)) != W8A8_OK) return st;
+  if (tokens == 0) return ok();
+  W8A8_REQUIRE(logits && topk_ids && topk_w && row_ids && expert_offsets && pos,
+               "logits, topk_ids, topk_w, row_ids, expert_offsets and pos must not be NULL");
+  W8A8_REQUIRE(ldl >= E, "ldl=%lld must be >= E", (long long)ldl);
+  W8A8_REQUIRE(workspace && aligned16(workspace) && workspace_bytes >= route_ws_bytes(tokens, E),
+               "routing needs a 16-byte aligned workspace of %zu bytes", route_ws_bytes(tokens, E));
+  if ((st = check_current_device()) != W8A8_OK) return st;
+  return hip_status(w8a8::launch_moe_route(logits, ldl, tokens, (int)E, topk, topk_ids, topk_w, row_ids,
+                                           expert_offsets, pos, static_cast<uint64_t*>(workspace),
+                                           static_cast<hipStream_t>(stream)),
+                    "moe_route launch");
+}
+
+w8a8_status w8a8_silu_mul_quant(const uint16_t* h, int64_t T, int64_t I, int64_t ldh, int8_t* aq, int64_t ldq,
+                                float* s_a, uint16_t* act, int64_t ld_act, void* stream) {
+  w8a8_status st;
+  if ((st = check_dim(T, "T")) != W8A8_OK) return st;
+  W8A8_REQUIRE(I >= 1 && I <= 16384 && I % 16 == 0, "I=%lld must be a multiple of 16 in [16, 16384]",
+               (long long)I);
+  if (T == 0) return ok();
+  W8A8_REQUIRE(h && aq && s_a, "h, aq and s_a must not be NULL");
+  W8A8_REQUIRE(aligned16(h) && aligned16(aq) && (act == nullptr || aligned16(act)),
+               "h, aq and act must be 16-byte aligned");
+  W8A8_REQUIRE(ldh >= 2 * I && ldh % 8 == 0, "ldh=%lld must be >= 2*I and a multiple of 8", (long long)ldh);
+  W8A8_REQUIRE(ldq >= I && ldq % 16 == 0, "ldq=%lld must be >= I and a multiple of 16", (long long)ldq);
+  if (act) W8A8_REQUIRE(ld_act >= I && ld_act % 8 == 0, "ld_act=%lld must be >= I and a multiple of 8",
+                        (long long)ld_act);
+  if ((st = check_current_device()) != W8A8_OK) return st;
+  return hip_status(w8a8::launch_silu_mul_quant(h, T, I, ldh, aq, ldq, s_a, act, ld_act,
+                                                static_cast<hipStream_t>(stream)),
+                    "silu_mul_quant launch");
+}
+
+w8a8_status w8a8_moe_combine(const uint16_t* y, int64_t ldy, const int32_t* pos, const float* topk_w,
+                             int64_t tokens, int32_t topk, int64_t N, uint16_t* out, int64_t ldo, void* stream) {
+  w8a8_status st;
+  if ((st = check_dim(tokens, "tokens")) != W8A8_OK) return st;
+  if ((st = check_dim(N, "N")) != W8A8_OK) return st;
+  W8A8_REQUIRE(topk >= 1 && topk <= kMoeMaxTopk, "topk=%d outside [1, %d]", topk, kMoeMaxTopk);
+  W8A8_REQUIRE(N % 8 == 0, "N=%lld must be a multiple of 8", (long long)N);
+  if (tokens == 0 || N == 0) return ok();
+  W8A8_REQUIRE(y && pos && topk_w && out, "y, pos, topk_w and out must not be NULL");
+  W8A8_REQUIRE(aligned16(y) && aligned16(out), "y and out must be 16-byte aligned");
+  W8A8_REQUIRE(ldy >= N && ldy % 8 == 0 && ldo >= N && ldo % 8 == 0,
+               "ldy and ldo must be >= N and multiples of 8");
+  if ((st = check_current_device()) != W8A8_OK) return st;
+  return hip_status(w8a8::launch_moe_combine(y, ldy, pos, topk_w, tokens, topk, N, out, ldo,
+                                             static_cast<hipStream_t>(stream)),
+                    "moe_combine launch");
+}
+
+size_t w8a8_moe_block_workspace_size(int64_t tokens, int64_t E, int32_t topk, int64_t H, int64_t I) {
+  if (tokens <= 0 || tokens >= kMaxDim || E <= 0 || E > kMoeMaxExperts || topk <= 0 || H <= 0 || I <= 0)
+    return 0;
+  return moe_layout(tokens, E, topk, H, I).total;
+}
+
+w8a8_status w8a8_moe_block_int8(const uint16_t* x, int64_t ldx, const float* logits, int64_t ldl,
+                                int64_t tokens, int64_t E, int32_t topk, int64_t H, int64_t I,
+                                const int8_t* w13, const float* s13, const int8_t* w2, const float* s2,
+                                uint16_t* out, int64_t ldo, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  w8a8_status st;
+  if ((st = check_moe_shape(tokens, E, topk)) != W8A8_OK) return st;
+  if ((st = check_k(H)) != W8A8_OK) return st;
+  W8A8_REQUIRE(I >= 16 && I <= 16384 && I % 16 == 0, "I=%lld must be a multiple of 16 in [16, 16384]",
+               (long long)I);
+  if (tokens == 0) return ok();
+  W8A8_REQUIRE(x && logits && w13 && s13 && w2 && s2 && out, "no array may be NULL");
+  W8A8_REQUIRE(aligned16(x) && aligned16(w13) && aligned16(w2) && aligned16(out),
+               "x, w13, w2 and out must be 16-byte aligned");
+  W8A8_REQUIRE(ldx >= H && ldx % 8 == 0, "ldx=%lld must be >= H and a multiple of 8", (long long)ldx);
+  W8A8_REQUIRE(ldl >= E, "ldl=%lld must be >= E", (long long)ldl);
+  W8A8_REQUIRE(ldo >= H && ldo % 8 == 0, "ldo=%lld must be >= H and a multiple of 8", (long long)ldo);
+  const int64_t T = tokens * topk;
+  if ((st = check_tiles(T, E, 2 * I)) != W8A8_OK) return st;
+  if ((st = check_tiles(T, E, H)) != W8A8_OK) return st;
+  const MoeLayout L = moe_layout(tokens, E, topk, H, I);
+  W8A8_REQUIRE(workspace && aligned16(workspace) && workspace_bytes >= L.total,
+               "the block needs a 16-byte aligned workspace of %zu bytes", L.total);
+  if ((st = check_current_device()) != W8A8_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  int8_t* xq = reinterpret_cast<int8_t*>(ws + L.xq);
+  float* sx = reinterpret_cast<float*>(ws + L.sx);
+  int32_t* ids = reinterpret_cast<int32_t*>(ws + L.ids);
+  float* wts = reinterpret_cast<float*>(ws + L.wts);
+  int32_t* row_ids = reinterpret_cast<int32_t*>(ws + L.row_ids);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+  int32_t* pos = reinterpret_cast<int32_t*>(ws + L.pos);
+  uint64_t* masks = reinterpret_cast<uint64_t*>(ws + L.masks);
+  uint16_t* h = reinterpret_cast<uint16_t*>(ws + L.h);
+  int8_t* aq = reinterpret_cast<int8_t*>(ws + L.aq);
+  float* sa = reinterpret_cast<float*>(ws + L.sa);
+  uint16_t* y = reinterpret_cast<uint16_t*>(ws + L.y);
+
+  hipError_t e = w8a8::launch_quantize_act(x, tokens, H, ldx, W8A8_QUANT_DYN_SYM, nullptr, nullptr, xq, H, sx,
+                                           nullptr, s);
+  if (e != hipSuccess) return hip_status(e, "quantize_act launch");
+  e = w8a8::launch_moe_route(logits, ldl, tokens, (int)E, topk, ids, wts, row_ids, offsets, pos, masks, s);
+  if (e != hipSuccess) return hip_status(e, "moe_route launch");
+  w8a8::GemmArgs g{};
+  g.A = xq;
+  g.lda = H;
+  g.B = w13;
+  g.ldb = H;
+  g.M = T;
+  g.N = 2 * I;
+  g.K = H;
+  g.s_x = sx;
+  g.sx_per_token = 1;
+  g.s_w = s13;
+  g.sw_per_channel = 1;
+  g.azp_mode = W8A8_AZP_NONE;
+  g.out = h;
+  g.ldo = 2 * I;
+  g.row_ids = row_ids;
+  g.expert_offsets = offsets;
+  g.E = E;
+  g.M_src = tokens;
+  if ((e = w8a8::launch_grouped_mm(g, s)) != hipSuccess) return hip_status(e, "grouped w13 launch");
+  e = w8a8::launch_silu_mul_quant(h, T, I, 2 * I, aq, I, sa, nullptr, 0, s);
+  if (e != hipSuccess) return hip_status(e, "silu_mul_quant launch");
+  g.A = aq;
+  g.lda = I;
+  g.B = w2;
+  g.ldb = I;
+  g.N = H;
+  g.K = I;
+  g.s_x = sa;
+  g.s_w = s2;
+  g.out = y;
+  g.ldo = H;
+  g.row_ids = nullptr;
+  g.M_src = T;
+  if ((e = w8a8::launch_grouped_mm(g, s)) != hipSuccess) return hip_status(e, "grouped w2 launch");
+  return hip_status(w8a8::launch_moe_combine(y, H, pos, wts, tokens, topk, H, out, ldo, s), "moe_combine launch");
+}
+
 const char* w8a8_scaled_mm_kernel_name(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K <= 0) return "";
   return (M <= w8a8::kDecodeMaxM) ? w8a8::decode_kernel_name(M, N, K, w8a8::decode_workspace_bytes(M, N, K)) : w8a8::scaled_mm_kernel_name(M, N, K);

@@ -77,4 +77,17 @@ const char* fused_linear_kernel_name(int64_t M, int64_t N, int64_t K);
 hipError_t launch_grouped_mm(const GemmArgs& a, hipStream_t stream);
 const char* grouped_mm_kernel_name(int64_t K);
 
+// MoE expert block steps (moe.hip). Routing needs moe_route_chunks(tokens) * E
+// 64-bit masks of scratch; E <= 512, k <= min(E, 64).
+int64_t moe_route_chunks(int64_t tokens);
+hipError_t launch_moe_route(const float* logits, int64_t ldl, int64_t tokens, int E, int k, int32_t* ids,
+                            float* wts, int32_t* row_ids, int32_t* offsets, int32_t* pos, uint64_t* masks,
+                            hipStream_t stream);
+// I % 8 == 0, I <= 16384; act (bf16 [T, I], ld_act) nullable.
+hipError_t launch_silu_mul_quant(const uint16_t* h, int64_t T, int64_t I, int64_t ldh, int8_t* aq, int64_t ldq,
+                                 float* s_a, uint16_t* act, int64_t ld_act, hipStream_t stream);
+// N % 8 == 0, k <= 16.
+hipError_t launch_moe_combine(const uint16_t* y, int64_t ldy, const int32_t* pos, const float* wts,
+                              int64_t tokens, int k, int64_t N, uint16_t* out, int64_t ldo, hipStream_t stream);
+
 }  // namespace w8a8

@@ -60,6 +60,13 @@ _SIGS = {
                                            _p, _p, _p, _p, _i32, _i64, _p]),
     "w8a8_linear_dyn_sym": (_i32, [_p, _i64, _i64, _i64, _p, _i64, _i64, _p, _i32, _p, _p, _i64,
                                    _p, _i64, _p, _p, ctypes.c_size_t, _p]),
+    "w8a8_moe_route_workspace_size": (ctypes.c_size_t, [_i64, _i64]),
+    "w8a8_moe_route": (_i32, [_p, _i64, _i64, _i64, _i32, _p, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]),
+    "w8a8_silu_mul_quant": (_i32, [_p, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p]),
+    "w8a8_moe_combine": (_i32, [_p, _i64, _p, _p, _i64, _i32, _i64, _p, _i64, _p]),
+    "w8a8_moe_block_workspace_size": (ctypes.c_size_t, [_i64, _i64, _i32, _i64, _i64]),
+    "w8a8_moe_block_int8": (_i32, [_p, _i64, _p, _i64, _i64, _i64, _i32, _i64, _i64, _p, _p, _p, _p,
+                                   _p, _i64, _p, ctypes.c_size_t, _p]),
     "w8a8_scaled_mm_kernel_name": (ctypes.c_char_p, [_i64, _i64, _i64]),
     "w8a8_linear_dyn_sym_kernel_name": (ctypes.c_char_p, [_i64, _i64, _i64]),
     "w8a8_status_string": (ctypes.c_char_p, [_i32]),
@@ -345,4 +352,87 @@ def grouped_scaled_mm_int8(xq, expert_offsets, Wq, s_x, s_w, row_ids=None, bias=
                                             _ptr(s_w), _ptr(bias), _ptr(out), out_dtype,
                                             out.stride(0) if T else N, _stream())
     _raise(st, "w8a8_grouped_scaled_mm_int8")
+    return out
+
+
+def moe_route(logits, topk: int, workspace=None, out=None):
+    """Top-k routing and the expert sort of float router logits [tokens, E].
+    Returns (topk_ids int32 [tokens, k], topk_w float [tokens, k], row_ids
+    int32 [tokens*k], expert_offsets int32 [E+1], pos int32 [tokens, k]);
+    `out` may pass those five tensors in."""
+    import torch
+    tokens, E = logits.shape
+    dev = logits.device
+    if out is None:
+        out = (torch.empty((tokens, topk), dtype=torch.int32, device=dev),
+               torch.empty((tokens, topk), dtype=torch.float32, device=dev),
+               torch.empty(tokens * topk, dtype=torch.int32, device=dev),
+               torch.empty(E + 1, dtype=torch.int32, device=dev),
+               torch.empty((tokens, topk), dtype=torch.int32, device=dev))
+    ids, w, rows, off, pos = out
+    if workspace is None:
+        workspace = torch.empty(max(16, int(load().w8a8_moe_route_workspace_size(tokens, E))),
+                                dtype=torch.uint8, device=dev)
+    st = load().w8a8_moe_route(_ptr(logits), logits.stride(0) if tokens else E, tokens, E, topk, _ptr(ids),
+                               _ptr(w), _ptr(rows), _ptr(off), _ptr(pos), _ptr(workspace),
+                               workspace.numel(), _stream())
+    _raise(st, "w8a8_moe_route")
+    return ids, w, rows, off, pos
+
+
+def silu_mul_quant(h, inter: int, aq=None, s_a=None, act=None, want_act=False):
+    """h bf16 [T, 2*inter] (gate, then up). Returns (aq int8 [T, inter], s_a
+    float [T], act bf16 [T, inter] or None)."""
+    import torch
+    T = h.shape[0]
+    dev = h.device
+    if aq is None:
+        aq = torch.empty((T, inter), dtype=torch.int8, device=dev)
+    if s_a is None:
+        s_a = torch.empty(T, dtype=torch.float32, device=dev)
+    if act is None and want_act:
+        act = torch.empty((T, inter), dtype=torch.bfloat16, device=dev)
+    st = load().w8a8_silu_mul_quant(_ptr(h), T, inter, h.stride(0) if T else 2 * inter, _ptr(aq),
+                                    aq.stride(0) if T else inter, _ptr(s_a), _ptr(act),
+                                    act.stride(0) if act is not None and T else inter, _stream())
+    _raise(st, "w8a8_silu_mul_quant")
+    return aq, s_a, act
+
+
+def moe_combine(y, pos, topk_w, out=None):
+    """out[t] = sum_j topk_w[t, j] * y[pos[t, j]]: y bf16 [T, N] (sorted rows),
+    pos int32 / topk_w float [tokens, k]. Returns bf16 [tokens, N]."""
+    import torch
+    tokens, k = pos.shape
+    N = y.shape[1]
+    if out is None:
+        out = torch.empty((tokens, N), dtype=torch.bfloat16, device=y.device)
+    st = load().w8a8_moe_combine(_ptr(y), y.stride(0) if y.shape[0] else N, _ptr(pos), _ptr(topk_w), tokens, k,
+                                 N, _ptr(out), out.stride(0) if tokens else N, _stream())
+    _raise(st, "w8a8_moe_combine")
+    return out
+
+
+def moe_block_workspace_size(tokens: int, E: int, topk: int, H: int, inter: int) -> int:
+    return int(load().w8a8_moe_block_workspace_size(tokens, E, topk, H, inter))
+
+
+def moe_block_int8(x, logits, topk: int, w13, s13, w2, s2, out=None, workspace=None):
+    """The int8 MoE expert block: x bf16 [tokens, H], logits float [tokens, E],
+    w13 int8 [E, 2I, H] with s13 float [E, 2I], w2 int8 [E, H, I] with s2
+    float [E, H]. Returns bf16 [tokens, H]."""
+    import torch
+    tokens, H = x.shape
+    E = logits.shape[1]
+    inter = w2.shape[2]
+    if out is None:
+        out = torch.empty((tokens, H), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(16, moe_block_workspace_size(tokens, E, topk, H, inter)),
+                                dtype=torch.uint8, device=x.device)
+    st = load().w8a8_moe_block_int8(_ptr(x), x.stride(0) if tokens else H, _ptr(logits),
+                                    logits.stride(0) if tokens else E, tokens, E, topk, H, inter, _ptr(w13),
+                                    _ptr(s13), _ptr(w2), _ptr(s2), _ptr(out), out.stride(0) if tokens else H,
+                                    _ptr(workspace), workspace.numel(), _stream())
+    _raise(st, "w8a8_moe_block_int8")
     return out

@@ -1,7 +1,7 @@
 """Seeded synthetic inputs for the W8A8 INT8 linear layer.
 
 This module only *draws* inputs: activations, int8 weights, scales, FP8 block
-weights and MoE routings. It holds none of the layer's arithmetic
+weights and MoE router logits. It holds none of the layer's arithmetic
 (quantisation, GEMM, epilogue, weight preparation), so the tests, the benchmark
 and the CPU checker can all feed the same bytes to both sides.
 
@@ -16,7 +16,7 @@ same data. Workloads (shapes from the Llama-3-8B linears that the
               round(0.005 K) outlier channels x30; bias ~ N(0, 0.02).
 3. prefill    M in {2048, 8192}, same (K,N); x ~ N(0.3, 1).
 4. static     M=512, K=4096, N=4096+1024+1024 with three per-tensor scales.
-5. moe        64 experts, top-8 of router logits N(0,1) for 4096 tokens,
+5. moe        64 experts, router logits N(0,1) for 4096 tokens (top-8),
               hidden 3072, w13 (K=3072,N=3072) and w2 (K=1536,N=3072) as
               OCP FP8 E4M3FN N(0, 0.02) with 128x128 block scales.
 
@@ -139,24 +139,10 @@ def fp8_block_weight(rng, E, N, K, std=0.02, block=128):
     return codes, scales
 
 
-def moe_routing(rng, tokens, E, topk):
-    """Top-k of N(0,1) router logits per token (ties to the lower expert id).
-
-    Returns (row_ids int32 [tokens*topk], expert_offsets int32 [E+1]): the
-    routed (token, expert) pairs sorted by (expert, token), row_ids holding
-    the token of each sorted row and expert_offsets the prefix sum of the
-    per-expert counts.
-    """
-    logits = rng.standard_normal((tokens, E), dtype=np.float32)
-    order = np.argsort(-logits, axis=1, kind="stable")[:, :topk]
-    tok = np.repeat(np.arange(tokens), topk)
-    exp = order.reshape(-1)
-    perm = np.lexsort((tok, exp))
-    row_ids = tok[perm].astype(np.int32)
-    counts = np.bincount(exp, minlength=E)
-    offsets = np.zeros(E + 1, np.int32)
-    offsets[1:] = np.cumsum(counts)
-    return row_ids, offsets
+def router_logits(rng, tokens, E):
+    """Router logits [tokens, E] ~ N(0, 1), float32 (the routing itself is a
+    step of the MoE block, not drawn here)."""
+    return rng.standard_normal((tokens, E), dtype=np.float32)
 
 
 def moe(tokens=MOE_TOKENS, E=MOE_E, topk=MOE_TOPK, hidden=MOE_HIDDEN, inter=MOE_INTER,
@@ -165,9 +151,9 @@ def moe(tokens=MOE_TOKENS, E=MOE_E, topk=MOE_TOPK, hidden=MOE_HIDDEN, inter=MOE_
     K = inter, N = hidden. The w2 input is an N(0,1) stand-in for the
     activated gate*up product, already in expert-sorted order."""
     rng = rng_for(5, tokens, E, topk, hidden, inter)
-    row_ids, offsets = moe_routing(rng, tokens, E, topk)
+    logits = router_logits(rng, tokens, E)
     T = tokens * topk
-    d = dict(row_ids=row_ids, offsets=offsets,
+    d = dict(logits=logits, topk=topk,
              x13=activations(rng, tokens, hidden),
              x2=activations(rng_for(5, tokens, E, topk, hidden, inter, 2), T, inter))
     if with_weights:

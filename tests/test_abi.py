@@ -16,7 +16,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = W.header_functions()
-    assert len(names) == 16, names
+    assert len(names) == 22, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -202,3 +202,54 @@ def test_noalloc_rejects_before_device_work(L):
     assert mm(azp=W.AZP_PER_TOKEN) == W.ERR_INVALID_ARG     # zp / colsum missing
     assert mm(out_dtype=5) == W.ERR_INVALID_ARG
     assert mm(M=0) == W.OK
+
+
+def test_moe_calls_reject_before_device_work(L):
+    """The MoE block's calls: sizes, limits and missing buffers are refused on
+    the host; empty problems are no-ops."""
+    def route(tokens=8, E=64, k=8, ldl=64, ws=FAKE, nbytes=1 << 20, logits=FAKE):
+        return L.w8a8_moe_route(logits, ldl, tokens, E, k, FAKE, FAKE, FAKE, FAKE, FAKE, ws, nbytes, None)
+    assert route(E=0) == W.ERR_INVALID_ARG
+    assert route(E=513) == W.ERR_INVALID_ARG
+    assert route(k=0) == W.ERR_INVALID_ARG
+    assert route(k=17) == W.ERR_INVALID_ARG
+    assert route(E=4, k=5, ldl=4) == W.ERR_INVALID_ARG   # more experts asked for than exist
+    assert route(ldl=32) == W.ERR_INVALID_ARG
+    assert route(ws=None) == W.ERR_INVALID_ARG
+    assert route(nbytes=8) == W.ERR_INVALID_ARG
+    assert route(logits=None) == W.ERR_INVALID_ARG
+    assert route(tokens=0) == W.OK
+    assert L.w8a8_moe_route_workspace_size(4096, 64) == 64 * 64 * 8
+    assert L.w8a8_moe_route_workspace_size(0, 64) == 0
+
+    def smq(T=4, I=64, ldh=128, ldq=64, h=FAKE, act=None, ld_act=0):
+        return L.w8a8_silu_mul_quant(h, T, I, ldh, FAKE, ldq, FAKE, act, ld_act, None)
+    assert smq(I=40) == W.ERR_INVALID_ARG
+    assert smq(I=16400, ldh=32800, ldq=16400) == W.ERR_INVALID_ARG
+    assert smq(ldh=120) == W.ERR_INVALID_ARG
+    assert smq(ldq=72) == W.ERR_INVALID_ARG
+    assert smq(h=FAKE + 8) == W.ERR_INVALID_ARG
+    assert smq(act=FAKE, ld_act=60) == W.ERR_INVALID_ARG
+    assert smq(T=0) == W.OK
+
+    def comb(tokens=4, k=8, N=64, ldy=64, ldo=64, y=FAKE):
+        return L.w8a8_moe_combine(y, ldy, FAKE, FAKE, tokens, k, N, FAKE, ldo, None)
+    assert comb(k=17) == W.ERR_INVALID_ARG
+    assert comb(N=60, ldy=60, ldo=60) == W.ERR_INVALID_ARG
+    assert comb(ldo=32) == W.ERR_INVALID_ARG
+    assert comb(y=None) == W.ERR_INVALID_ARG
+    assert comb(tokens=0) == W.OK
+
+    def block(tokens=8, E=8, k=2, H=64, I=32, ws=FAKE, nbytes=1 << 30):
+        return L.w8a8_moe_block_int8(FAKE, H, FAKE, E, tokens, E, k, H, I, FAKE, FAKE, FAKE, FAKE, FAKE, H,
+                                     ws, nbytes, None)
+    assert block(H=40) == W.ERR_INVALID_ARG
+    assert block(I=24) == W.ERR_INVALID_ARG
+    assert block(k=9) == W.ERR_INVALID_ARG
+    assert block(nbytes=1024) == W.ERR_INVALID_ARG
+    assert block(ws=None) == W.ERR_INVALID_ARG
+    assert block(tokens=0) == W.OK
+    need = L.w8a8_moe_block_workspace_size(4096, 64, 8, 3072, 1536)
+    T = 4096 * 8
+    # codes, scales, routing, the int8 w2 input and one bf16 [T, 3072] buffer shared by h and y
+    assert need >= 4096 * 3072 + T * 1536 + T * 3072 * 2 and need < 300 << 20

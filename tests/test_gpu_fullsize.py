@@ -145,7 +145,7 @@ def test_moe_grouped_full(moe_inputs, name):
     expert's first and last row among them) compared."""
     m = moe_inputs
     E = synth.MOE_E
-    off, rid = m["offsets"], m["row_ids"]
+    rid, off, _ = O.moe_sort(O.moe_topk(m["logits"], m["topk"])[0], E)
     T = int(off[-1])
     if name == "w13":
         K, N, x, gather = synth.MOE_HIDDEN, 2 * synth.MOE_INTER, m["x13"], True

@@ -71,7 +71,7 @@ def test_grouped(counts, K, N, M_src):
 def test_grouped_moe_routing_small():
     """The MoE workload's routing on a reduced size: top-8 of 64 experts for 256 tokens."""
     rng = synth.rng_for(921)
-    rows, off = synth.moe_routing(rng, 256, 64, 8)
+    rows, off, _ = O.moe_sort(O.moe_topk(synth.router_logits(rng, 256, 64), 8)[0], 64)
     K, N = 384, 256
     d = dict(off=off, T=len(rows), rows=rows,
              xq=rng.integers(-127, 128, (256, K), dtype=np.int8),

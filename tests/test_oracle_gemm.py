@@ -158,13 +158,3 @@ def test_grouped_against_per_row_brute_force():
     xs = xq[row_ids]
     out2, c2 = O.grouped_scaled_mm(xs, sx[row_ids], w, sw, off, bias_bits=b)
     assert np.array_equal(out2, out) and np.array_equal(c2, c)
-
-
-def test_moe_routing_generator_is_a_valid_grouping():
-    row_ids, off = synth.moe_routing(np.random.default_rng(0), 64, 8, 2)
-    assert off[0] == 0 and off[-1] == 128 and np.all(np.diff(off) >= 0)
-    # each token appears exactly top-k times, in distinct experts
-    assert np.array_equal(np.bincount(row_ids, minlength=64), np.full(64, 2))
-    for e in range(8):
-        seg = row_ids[off[e]:off[e + 1]]
-        assert np.all(np.diff(seg) > 0)
