@@ -67,6 +67,16 @@ __all__ = [
     "e4m3fn_table",
     "fp8_block_to_int8",
     "grouped_scaled_mm",
+    "e4m3fn_encode",
+    "quant_fp8",
+    "scaled_mm_fp8",
+    "FP8_MAX",
+    "FP8_ACT_TOKEN",
+    "FP8_ACT_TENSOR",
+    "FP8_ACT_GROUP128",
+    "FP8_W_TENSOR",
+    "FP8_W_CHANNEL",
+    "FP8_W_BLOCK128",
     "moe_topk",
     "moe_sort",
     "silu_mul_bf16",
@@ -533,3 +543,109 @@ def moe_block(x_bits, logits, k, w13, s13, w2, s2):
     out = moe_combine(y, pos, wts)
     return dict(xq=xq, sx=sx, ids=ids, weights=wts, row_ids=row_ids, offsets=offsets, pos=pos,
                 h=h, act=act, aq=aq, sa=sa, y=y, out=out)
+
+
+# ------------------------------------------------------------ W8A8 FP8 --
+#
+# The W8A8 FP8 scheme of [SGLang] 핵심 코드 분석 §1-§2: E4M3 weights and
+# activations; a weight scale per channel ([N, 1]), per tensor (one per
+# fused partition), or per 128 x 128 block ([N/128, K/128]); the block path
+# (w8a8_block_fp8_linear) quantises the activation per token in groups of
+# 128 along K, the others per token (the per-token / per-channel path) or
+# with a static per-tensor input scale. Readings: the activation scale is the
+# group's absmax over the largest E4M3 value (448), the FP8 counterpart of
+# the int8 absmax/127 rule; an all-zero row (or group) gives scale 1; codes
+# are the quotient x / s rounded to nearest E4M3 (ties to even), saturated at
+# +-448; the product is exact and the scales are applied per K block before
+# the block sums are added.
+
+FP8_MAX = 448.0
+FP8_ACT_TOKEN, FP8_ACT_TENSOR, FP8_ACT_GROUP128 = 0, 1, 2
+FP8_W_TENSOR, FP8_W_CHANNEL, FP8_W_BLOCK128 = 0, 1, 2
+
+
+def e4m3fn_encode(v):
+    """Nearest OCP E4M3FN code of each float32 value (ties to the even code,
+    whose last mantissa bit is 0), |v| <= 448 (larger values are outside the
+    encoding's range and must be clamped first). The sign bit is kept, so -0
+    and negative values that round to zero give 0x80. Found by searching the
+    sorted non-negative values of e4m3fn_table()."""
+    v = np.asarray(v, dtype=np.float32)
+    assert not np.any(np.isnan(v)) and np.all(np.abs(v) <= FP8_MAX)
+    mags = e4m3fn_table()[:127].astype(np.float64)  # codes 0 .. 126, increasing
+    a = np.abs(v).astype(np.float64)
+    hi = np.clip(np.searchsorted(mags, a, side="left"), 0, 126)  # first magnitude >= a
+    lo = np.clip(hi - 1, 0, 126)
+    d_lo, d_hi = a - mags[lo], mags[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return np.where(np.signbit(v), code | np.uint8(0x80), code).astype(np.uint8)
+
+
+def quant_fp8(x_bits, mode, s_in=None, group=128):
+    """E4M3 quantisation of bf16 activations [M, K] ([SGLang] §1-§2).
+    FP8_ACT_TOKEN:   s[t] = max_k |x_tk| / 448                 (scales [M])
+    FP8_ACT_TENSOR:  s = s_in                                  (given)
+    FP8_ACT_GROUP128: s[g, t] = max over k in group g |x_tk| / 448, groups of
+                     128 along K (the last may be shorter)     (scales [G, M])
+    An all-zero row (group) gives s = 1. q = E4M3(clamp(fl(x / s), -448, 448)).
+    Returns (codes uint8 [M, K], scales float32 or None)."""
+    x = bf16_bits_to_f32(x_bits)
+    M, K = x.shape
+    if mode == FP8_ACT_TENSOR:
+        s_full = np.full((M, K), _F(s_in), _F)
+        scales = None
+    elif mode == FP8_ACT_TOKEN:
+        a = np.max(np.abs(x), axis=1) if K else np.zeros(M, _F)
+        scales = np.where(a == 0, _F(1), a / _F(FP8_MAX)).astype(_F)
+        s_full = np.repeat(scales[:, None], K, axis=1)
+    elif mode == FP8_ACT_GROUP128:
+        G = -(-K // group)
+        scales = np.empty((G, M), _F)
+        s_full = np.empty((M, K), _F)
+        for g in range(G):
+            blk = x[:, g * group:(g + 1) * group]
+            a = np.max(np.abs(blk), axis=1)
+            scales[g] = np.where(a == 0, _F(1), a / _F(FP8_MAX)).astype(_F)
+            s_full[:, g * group:(g + 1) * group] = scales[g][:, None]
+    else:
+        raise ValueError(f"unknown FP8 activation mode {mode}")
+    with np.errstate(over="ignore"):
+        t = (x / s_full).astype(_F)
+    t = np.clip(t, _F(-FP8_MAX), _F(FP8_MAX))
+    return e4m3fn_encode(t), scales
+
+
+def scaled_mm_fp8(xq, wq, s_x, s_w, act_mode, w_mode, bias_bits=None, block=128):
+    """The W8A8 FP8 GEMM ([SGLang] §2): out[t, n] = sum_k dec(xq[t, k]) *
+    dec(wq[n, k]) with the scales applied, plus bias, rounded once to bf16.
+    Per-tensor / per-channel weights: y = acc * s_x[t] (or s_x) * s_w[n] (or
+    s_w). 128 x 128 blocks: y = sum_g acc_g * s_x[g, t] * s_w[n // 128, g],
+    acc_g the sum over the K group g (activation scales group-major [G, M]).
+    The products of E4M3 values are exact in float64 and so are the sums
+    (at most 2^51 apart within a 128-wide group). Returns (bf16 bits [M, N],
+    y float64 [M, N])."""
+    dec = e4m3fn_table().astype(np.float64)
+    X = dec[np.asarray(xq, np.uint8)]
+    Wt = dec[np.asarray(wq, np.uint8)]
+    M, K = X.shape
+    N = Wt.shape[0]
+    if w_mode == FP8_W_BLOCK128:
+        assert act_mode == FP8_ACT_GROUP128
+        sx = np.asarray(s_x, np.float32).astype(np.float64)
+        sw = np.asarray(s_w, np.float32).astype(np.float64)
+        y = np.zeros((M, N), np.float64)
+        nblk = np.arange(N) // block
+        for g in range(-(-K // block)):
+            acc = X[:, g * block:(g + 1) * block] @ Wt[:, g * block:(g + 1) * block].T
+            y += acc * sx[g][:, None] * sw[nblk, g][None, :]
+    else:
+        assert act_mode in (FP8_ACT_TOKEN, FP8_ACT_TENSOR)
+        sx = np.asarray(s_x, np.float32).astype(np.float64).reshape(-1)
+        sw = np.asarray(s_w, np.float32).astype(np.float64).reshape(-1)
+        sx = sx[:, None] if act_mode == FP8_ACT_TOKEN else sx[0]    # [M] per token, or one scale
+        sw = sw[None, :] if w_mode == FP8_W_CHANNEL else sw[0]      # [N] per channel, or one scale
+        y = (X @ Wt.T) * sx * sw
+    if bias_bits is not None:
+        y = y + bf16_bits_to_f32(bias_bits).astype(np.float64)[None, :]
+    return f64_to_bf16_bits(y), y
