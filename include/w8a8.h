@@ -78,7 +78,22 @@ enum {
 /* Output element type of the GEMMs. */
 enum {
   W8A8_OUT_BF16 = 0, /* bf16(c * s_x * s_w + bias), round to nearest even            */
-  W8A8_OUT_I32 = 1   /* the corrected integer c itself (exact; for checking)        */
+  W8A8_OUT_I32 = 1,  /* the corrected integer c itself (exact; for checking)        */
+  W8A8_OUT_F32 = 2   /* w8a8_scaled_mm_fp8 only: the binary32 value before rounding */
+};
+
+/* W8A8 FP8 activation quantisation (w8a8_quantize_act_fp8). */
+enum {
+  W8A8_FP8_ACT_TOKEN = 0,    /* per token, s = absmax / 448                        */
+  W8A8_FP8_ACT_TENSOR = 1,   /* one given scale                                    */
+  W8A8_FP8_ACT_GROUP128 = 2  /* per token in groups of 128 along K                 */
+};
+
+/* W8A8 FP8 weight scales (w8a8_scaled_mm_fp8). */
+enum {
+  W8A8_FP8_W_TENSOR = 0,   /* one scale                                              */
+  W8A8_FP8_W_CHANNEL = 1,  /* one per output channel [N]                             */
+  W8A8_FP8_W_BLOCK128 = 2  /* one per 128 x 128 block [ceil(N/128), ceil(K/128)]     */
 };
 
 /* err_flag bits. */
@@ -303,6 +318,49 @@ w8a8_status w8a8_grouped_scaled_mm_int8(const int8_t* xq, int64_t ldx, int64_t M
                                         const float* s_x, const float* s_w,
                                         const uint16_t* bias, void* out, int32_t out_dtype,
                                         int64_t ldo, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * The W8A8 FP8 scheme of [SGLang] 핵심 코드 분석 §1-§2: E4M3 (OCP E4M3FN)
+ * weights and activations; a weight scale per tensor, per output channel or
+ * per 128 x 128 block; per-token (or static per-tensor) activation scales,
+ * per-token groups of 128 along K on the block path. */
+
+/* E4M3 quantisation of bf16 activations x [M,K] (ldx) to codes xq uint8
+ * [M,K] (ldq):
+ *   TOKEN:    s_x[t] = max|x_t| / 448                          s_x float [M]
+ *   TENSOR:   s = *s_in (device scalar)                        s_x unused
+ *   GROUP128: s_x[g*M + t] = max over k in [128g, 128g+128) of |x_tk| / 448
+ *             (group-major, G = ceil(K/128) groups)            s_x float [G*M]
+ * An all-zero row (group) gives scale 1. xq = E4M3(clamp(x / s, -448, 448)):
+ * the IEEE binary32 quotient rounded to the nearest E4M3 value, ties to even;
+ * the sign of a zero is kept. Requires K % 16 == 0, K <= W8A8_MAX_K, x and
+ * xq 16-byte aligned, ldx % 8 == 0, ldq % 16 == 0. */
+w8a8_status w8a8_quantize_act_fp8(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                  int32_t mode, const float* s_in, uint8_t* xq, int64_t ldq,
+                                  float* s_x, void* stream);
+
+/* The W8A8 FP8 GEMM ([SGLang] 핵심 코드 분석 §2):
+ *   acc[t,n] = sum_k dec(xq[t,k]) * dec(Wq[n,k])       (binary32 MFMA sums)
+ *   TENSOR / CHANNEL weight scales, TOKEN / TENSOR activation scales:
+ *     y = acc * s_x[t or 0] * s_w[n or 0] + bias[n]
+ *   BLOCK128 weight scales s_w [ceil(N/128), G] with GROUP128 activation
+ *   scales s_x [G, M] (as w8a8_quantize_act_fp8 writes them for this M):
+ *     y = sum_g acc_g[t,n] * s_x[g*M + t] * s_w[(n/128)*G + g] + bias[n]
+ *     (acc_g: the sum over k in group g)
+ *   out[t,n] = bf16(y) (W8A8_OUT_BF16) or y (W8A8_OUT_F32).
+ * xq, Wq E4M3 codes [M,K] / [N,K] (ldx, ldw); bias bf16 [N] or NULL; out
+ * [M,N] (ldo). Other mode pairs return W8A8_ERR_NOT_IMPLEMENTED. Requires
+ * K % 16 == 0, 1 <= K <= W8A8_MAX_K, xq/Wq/out 16-byte aligned, ldx % 16 ==
+ * 0, ldw % 16 == 0. NaN codes (0x7F, 0xFF) are outside the contract. */
+w8a8_status w8a8_scaled_mm_fp8(const uint8_t* xq, int64_t M, int64_t K, int64_t ldx,
+                               const uint8_t* Wq, int64_t N, int64_t ldw, const float* s_x,
+                               int32_t act_mode, const float* s_w, int32_t w_mode,
+                               const uint16_t* bias, void* out, int32_t out_dtype, int64_t ldo,
+                               void* stream);
+
+/* Name of the kernel instance w8a8_scaled_mm_fp8 launches for an M x N x K
+ * problem with the given weight-scale mode (static storage; "" if invalid). */
+const char* w8a8_scaled_mm_fp8_kernel_name(int64_t M, int64_t N, int64_t K, int32_t w_mode);
 
 /* ---------------------------------------------------------------------------
  * The int8 MoE expert block around the grouped GEMM: the int8 MoE method of

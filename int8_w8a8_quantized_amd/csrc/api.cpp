@@ -478,6 +478,75 @@ w8a8_status w8a8_grouped_scaled_mm_int8(const int8_t* xq, int64_t ldx, int64_t M
   return hip_status(w8a8::launch_grouped_mm(a, static_cast<hipStream_t>(stream)), "grouped_mm launch");
 }
 
+w8a8_status w8a8_quantize_act_fp8(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int32_t mode,
+                                  const float* s_in, uint8_t* xq, int64_t ldq, float* s_x, void* stream) {
+  w8a8_status st;
+  if ((st = check_dim(M, "M")) != W8A8_OK) return st;
+  if ((st = check_k(K)) != W8A8_OK) return st;
+  W8A8_REQUIRE(mode >= W8A8_FP8_ACT_TOKEN && mode <= W8A8_FP8_ACT_GROUP128, "unknown FP8 mode %d", mode);
+  if (M == 0) return ok();
+  W8A8_REQUIRE(x && xq, "x and xq must not be NULL");
+  W8A8_REQUIRE(aligned16(x) && aligned16(xq), "x and xq must be 16-byte aligned");
+  W8A8_REQUIRE(ldx >= K && ldx % 8 == 0, "ldx=%lld must be >= K and a multiple of 8", (long long)ldx);
+  W8A8_REQUIRE(ldq >= K && ldq % 16 == 0, "ldq=%lld must be >= K and a multiple of 16", (long long)ldq);
+  if (mode == W8A8_FP8_ACT_TENSOR) W8A8_REQUIRE(s_in != nullptr, "s_in must not be NULL in TENSOR mode");
+  else W8A8_REQUIRE(s_x != nullptr, "s_x must not be NULL in a dynamic mode");
+  if ((st = check_current_device()) != W8A8_OK) return st;
+  return hip_status(w8a8::launch_quantize_act_fp8(x, M, K, ldx, mode, s_in, xq, ldq, s_x,
+                                                  static_cast<hipStream_t>(stream)),
+                    "quantize_act_fp8 launch");
+}
+
+w8a8_status w8a8_scaled_mm_fp8(const uint8_t* xq, int64_t M, int64_t K, int64_t ldx, const uint8_t* Wq, int64_t N,
+                               int64_t ldw, const float* s_x, int32_t act_mode, const float* s_w, int32_t w_mode,
+                               const uint16_t* bias, void* out, int32_t out_dtype, int64_t ldo, void* stream) {
+  w8a8_status st;
+  if ((st = check_dim(M, "M")) != W8A8_OK) return st;
+  if ((st = check_dim(N, "N")) != W8A8_OK) return st;
+  if ((st = check_k(K)) != W8A8_OK) return st;
+  W8A8_REQUIRE(act_mode >= W8A8_FP8_ACT_TOKEN && act_mode <= W8A8_FP8_ACT_GROUP128, "unknown act_mode %d",
+               act_mode);
+  W8A8_REQUIRE(w_mode >= W8A8_FP8_W_TENSOR && w_mode <= W8A8_FP8_W_BLOCK128, "unknown w_mode %d", w_mode);
+  const bool block = w_mode == W8A8_FP8_W_BLOCK128;
+  if (block != (act_mode == W8A8_FP8_ACT_GROUP128))
+    return fail(W8A8_ERR_NOT_IMPLEMENTED,
+                "FP8 scales: 128x128 weight blocks go with per-token groups of 128 activations, "
+                "tensor/channel weights with token/tensor activations (got w_mode=%d, act_mode=%d)",
+                w_mode, act_mode);
+  W8A8_REQUIRE(out_dtype == W8A8_OUT_BF16 || out_dtype == W8A8_OUT_F32, "out_dtype must be BF16 or F32");
+  if (M == 0 || N == 0) return ok();
+  W8A8_REQUIRE(xq && Wq && out && s_x && s_w, "xq, Wq, out, s_x and s_w must not be NULL");
+  W8A8_REQUIRE(aligned16(xq) && aligned16(Wq) && aligned16(out), "xq, Wq and out must be 16-byte aligned");
+  W8A8_REQUIRE(ldx >= K && ldx % 16 == 0, "ldx=%lld must be >= K and a multiple of 16", (long long)ldx);
+  W8A8_REQUIRE(ldw >= K && ldw % 16 == 0, "ldw=%lld must be >= K and a multiple of 16", (long long)ldw);
+  W8A8_REQUIRE(ldo >= N, "ldo=%lld must be >= N", (long long)ldo);
+  if ((st = check_tiles(M, 0, N)) != W8A8_OK) return st;
+  if ((st = check_current_device()) != W8A8_OK) return st;
+  w8a8::GemmArgs a{};
+  a.A = reinterpret_cast<const int8_t*>(xq);
+  a.lda = ldx;
+  a.B = reinterpret_cast<const int8_t*>(Wq);
+  a.ldb = ldw;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.s_x = s_x;
+  a.sx_per_token = act_mode == W8A8_FP8_ACT_TOKEN;
+  a.s_w = s_w;
+  a.sw_per_channel = w_mode == W8A8_FP8_W_CHANNEL;
+  a.azp_mode = W8A8_AZP_NONE;
+  a.bias = bias;
+  a.out = out;
+  a.out_i32 = out_dtype == W8A8_OUT_F32;
+  a.ldo = ldo;
+  return hip_status(w8a8::launch_scaled_mm_fp8(a, block, static_cast<hipStream_t>(stream)), "scaled_mm_fp8 launch");
+}
+
+const char* w8a8_scaled_mm_fp8_kernel_name(int64_t M, int64_t N, int64_t K, int32_t w_mode) {
+  if (M <= 0 || N <= 0 || K <= 0 || w_mode < W8A8_FP8_W_TENSOR || w_mode > W8A8_FP8_W_BLOCK128) return "";
+  return w8a8::scaled_mm_fp8_kernel_name(M, N, K, w_mode == W8A8_FP8_W_BLOCK128);
+}
+
 }  // extern "C"
 
 // ------------------------------------------------------------ MoE block

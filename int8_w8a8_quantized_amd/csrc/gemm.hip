@@ -257,9 +257,12 @@ __device__ __forceinline__ EpiFetch epilogue_fetch(const GemmArgs& a, const Tile
 // stores).
 enum { kStoreScalar = 0, kStoreVecRows = 1, kStoreVec = 2 };
 
-template <int BM, int BN, bool MASKED, bool OUT_I32, int AZP, int ST>
+// FACC: the accumulators hold binary32 bit patterns (the FP8 product), and
+// OUT_I32 then means a binary32 output of the scaled value (no AZP).
+template <int BM, int BN, bool MASKED, bool OUT_I32, int AZP, int ST, bool FACC = false>
 __device__ __forceinline__ void epilogue_store_tile(const GemmArgs& a, const TileLoc& t, int8_t* smem,
                                                     i32x16 (&acc)[BM / 64][BN / 64]) {
+  static_assert(!FACC || AZP == 0, "no zero-point correction on float accumulators");
   constexpr int TM = BM / 2, TN = BN / 2, FM = TM / 32, FN = TN / 32;
   constexpr int CSTRIDE = TN + 8;  // int32 words; rows 4 apart land 32 banks apart
   constexpr int LPR = TN / 8;      // lanes per row
@@ -293,7 +296,7 @@ __device__ __forceinline__ void epilogue_store_tile(const GemmArgs& a, const Til
       const int4 v = *reinterpret_cast<const int4*>(p + c0 + cB);
       d[0] = u.x; d[1] = u.y; d[2] = u.z; d[3] = u.w; d[4] = v.x; d[5] = v.y; d[6] = v.z; d[7] = v.w;
     };
-    if (!OUT_I32) get4f(col_sw, sw8), get4f(col_bias, bias8);
+    if (!OUT_I32 || FACC) get4f(col_sw, sw8), get4f(col_bias, bias8);
     if (AZP == 1 || AZP == 3) get4i(col_sum, sum8);
     if (AZP == 2 || AZP == 3) get4i(col_adj, adj8);
   }
@@ -329,6 +332,11 @@ __device__ __forceinline__ void epilogue_store_tile(const GemmArgs& a, const Til
       }
       OutT* o = o_lane + (int64_t)dr * a.ldo;
       const bool row_ok = ST == kStoreVec || t.row_begin + lrow0 + dr < t.row_end;
+      if (OUT_I32 && FACC) {  // the scaled binary32 value, as its bit pattern
+        const float sx = __int_as_float(rp.y);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) c[k] = __float_as_int(__builtin_fmaf(__int_as_float(c[k]) * sx, sw8[k], bias8[k]));
+      }
       if (OUT_I32) {
         if (ST != kStoreScalar) {
           if (row_ok) {
@@ -345,8 +353,10 @@ __device__ __forceinline__ void epilogue_store_tile(const GemmArgs& a, const Til
         uint32_t h[4];
 #pragma unroll
         for (int k = 0; k < 8; k += 2) {
-          const float y0 = __builtin_fmaf((float)c[k] * sx, sw8[k], bias8[k]);
-          const float y1 = __builtin_fmaf((float)c[k + 1] * sx, sw8[k + 1], bias8[k + 1]);
+          const float a0 = FACC ? __int_as_float(c[k]) : (float)c[k];
+          const float a1 = FACC ? __int_as_float(c[k + 1]) : (float)c[k + 1];
+          const float y0 = __builtin_fmaf(a0 * sx, sw8[k], bias8[k]);
+          const float y1 = __builtin_fmaf(a1 * sx, sw8[k + 1], bias8[k + 1]);
           h[k / 2] = pack_bf16x2(y0, y1);
         }
         if (ST != kStoreScalar) {
@@ -365,10 +375,13 @@ __device__ __forceinline__ void epilogue_store_tile(const GemmArgs& a, const Til
   }
 }
 
-template <int BM, int BN, bool GROUPED, int ST>
+template <int BM, int BN, bool GROUPED, int ST, bool FACC>
 __device__ __forceinline__ void epilogue_dispatch(const GemmArgs& a, const TileLoc& t, int8_t* smem,
                                                   i32x16 (&acc)[BM / 64][BN / 64]) {
-  if (a.out_i32) {
+  if (FACC) {
+    if (a.out_i32) epilogue_store_tile<BM, BN, GROUPED, true, 0, ST, true>(a, t, smem, acc);
+    else epilogue_store_tile<BM, BN, GROUPED, false, 0, ST, true>(a, t, smem, acc);
+  } else if (a.out_i32) {
     if (a.azp_mode == 1) epilogue_store_tile<BM, BN, GROUPED, true, 1, ST>(a, t, smem, acc);
     else if (a.azp_mode == 2) epilogue_store_tile<BM, BN, GROUPED, true, 2, ST>(a, t, smem, acc);
     else epilogue_store_tile<BM, BN, GROUPED, true, 0, ST>(a, t, smem, acc);
@@ -379,7 +392,7 @@ __device__ __forceinline__ void epilogue_dispatch(const GemmArgs& a, const TileL
   }
 }
 
-template <int BM, int BN, bool GROUPED>
+template <int BM, int BN, bool GROUPED, bool FACC = false>
 __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const TileLoc& t, const EpiFetch& f,
                                               int8_t* smem, i32x16 (&acc)[BM / 64][BN / 64]) {
   constexpr int TN = BN / 2;
@@ -406,12 +419,18 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const TileLoc& 
   const bool vec = t.n_begin + (wn + 1) * TN <= a.N && a.ldo % 4 == 0;
   const bool rows = t.row_begin + BM <= t.row_end;
   if (!vec) {
-    if (a.out_i32) epilogue_store_tile<BM, BN, GROUPED, true, 3, kStoreScalar>(a, t, smem, acc);
-    else epilogue_store_tile<BM, BN, GROUPED, false, 3, kStoreScalar>(a, t, smem, acc);
+    if (FACC) {
+      if (a.out_i32) epilogue_store_tile<BM, BN, GROUPED, true, 0, kStoreScalar, true>(a, t, smem, acc);
+      else epilogue_store_tile<BM, BN, GROUPED, false, 0, kStoreScalar, true>(a, t, smem, acc);
+    } else if (a.out_i32) {
+      epilogue_store_tile<BM, BN, GROUPED, true, 3, kStoreScalar>(a, t, smem, acc);
+    } else {
+      epilogue_store_tile<BM, BN, GROUPED, false, 3, kStoreScalar>(a, t, smem, acc);
+    }
   } else if (rows) {
-    epilogue_dispatch<BM, BN, GROUPED, kStoreVec>(a, t, smem, acc);
+    epilogue_dispatch<BM, BN, GROUPED, kStoreVec, FACC>(a, t, smem, acc);
   } else {
-    epilogue_dispatch<BM, BN, GROUPED, kStoreVecRows>(a, t, smem, acc);
+    epilogue_dispatch<BM, BN, GROUPED, kStoreVecRows, FACC>(a, t, smem, acc);
   }
 }
 
@@ -438,8 +457,12 @@ __device__ __forceinline__ int swz(int r) {
   return CH == 4 ? (((r >> 1) ^ (r >> 3)) & 3) : ((r ^ ((r >> 3) & 3)) & 7);
 }
 
-template <int BM, int BN, int BK, int NH, bool GROUPED>
-__global__ __launch_bounds__(256) void gemm_i8_dma_kernel(GemmArgs a, int tiles_m, int tiles_n) {
+// The ring kernel's body, for int8 operands (v_mfma_i32_32x32x32_i8, exact
+// int32 sums) or, with FP8, for E4M3 operands (v_mfma_scale_f32_32x32x64_f8f6f4
+// with unit block scales: 64 k per instruction from two 16-byte fragment
+// reads per lane, binary32 sums kept as bit patterns in the same registers).
+template <int BM, int BN, int BK, int NH, bool GROUPED, bool FP8>
+__device__ __forceinline__ void gemm_dma_body(const GemmArgs& a, int tiles_m, int tiles_n) {
   constexpr int TM = BM / 2, TN = BN / 2, FM = TM / 32, FN = TN / 32;
   // The ring is made of NH half-stages: half-stage 2s + p holds K step s of
   // the A rows [p*TM, p*TM + TM) and the B rows [p*TN, p*TN + TN) -- the
@@ -449,7 +472,8 @@ __global__ __launch_bounds__(256) void gemm_i8_dma_kernel(GemmArgs a, int tiles_
   constexpr int RPI = 64 / CH;                // tile rows per 1-KiB load instruction
   constexpr int AI = TM / RPI / 4, BI = TN / RPI / 4;  // load instructions per wave per half-stage
   constexpr int PER_HALF = AI + BI;
-  constexpr int KS = BK / 32;                 // MFMA k slices per K step
+  constexpr int KS = BK / (FP8 ? 64 : 32);    // MFMA k slices per K step
+  constexpr int RPF = FP8 ? 2 : 1;            // 16-byte LDS reads per fragment
   static_assert(CH == 4 || CH == 8, "BK is 64 or 128");
   static_assert(TM % (4 * RPI) == 0 && TN % (4 * RPI) == 0, "tile / load mismatch");
   static_assert(NH >= 5 && (NH - 3) * PER_HALF <= 63, "ring / vmcnt range");
@@ -518,15 +542,27 @@ __global__ __launch_bounds__(256) void gemm_i8_dma_kernel(GemmArgs a, int tiles_
   // this wave's tile row (A) and tile column (B); rows 32 apart share swz().
   const int fr = lane & 31;
   const int fsw = swz<CH>(fr);
-  i32x4 fa[2][FM], fb[2][FN];
+  using Frag = typename std::conditional<FP8, i32x8, i32x4>::type;
+  Frag fa[2][FM], fb[2][FN];
+  // int8: the lane's 16 bytes of the 32-deep slice; FP8: its 32 bytes of the
+  // 64-deep slice (two chunks), the same k positions in A and in B
+  auto frag_at = [&](const int8_t* p, int ks) __attribute__((always_inline)) -> Frag {
+    if constexpr (FP8) {
+      const int c0 = 4 * ks + 2 * (lane >> 5);
+      const i32x4 lo = *reinterpret_cast<const i32x4*>(p + ((c0 ^ fsw) * 16));
+      const i32x4 hi = *reinterpret_cast<const i32x4*>(p + (((c0 + 1) ^ fsw) * 16));
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    } else {
+      return *reinterpret_cast<const i32x4*>(p + (((2 * ks + (lane >> 5)) ^ fsw) * 16));
+    }
+  };
   auto read_one = [&](int s, int ks, int slot, int f) __attribute__((always_inline)) {
-    const int off = ((2 * ks + (lane >> 5)) ^ fsw) * 16;
     if (f < FM) {
       const int8_t* sa = smem + ((2 * s + wm) % NH) * HSTAGE + fr * BK;
-      fa[slot][f] = *reinterpret_cast<const i32x4*>(sa + f * 32 * BK + off);
+      fa[slot][f] = frag_at(sa + f * 32 * BK, ks);
     } else {
       const int8_t* sb = smem + ((2 * s + wn) % NH) * HSTAGE + TM * BK + fr * BK;
-      fb[slot][f - FM] = *reinterpret_cast<const i32x4*>(sb + (f - FM) * 32 * BK + off);
+      fb[slot][f - FM] = frag_at(sb + (f - FM) * 32 * BK, ks);
     }
   };
 
@@ -542,7 +578,10 @@ __global__ __launch_bounds__(256) void gemm_i8_dma_kernel(GemmArgs a, int tiles_
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x32(fa[slot][i], fb[slot][j], acc[i][j]);
+      for (int j = 0; j < FN; ++j) {
+        if constexpr (FP8) acc[i][j] = mfma32x32x64_fp8(fa[slot][i], fb[slot][j], acc[i][j]);
+        else acc[i][j] = mfma32x32x32(fa[slot][i], fb[slot][j], acc[i][j]);
+      }
   };
   static_assert(KS % 2 == 0, "the next step's first slice reuses fragment slot 0");
   constexpr int NR = FM + FN, NM = FM * FN;
@@ -595,7 +634,7 @@ __global__ __launch_bounds__(256) void gemm_i8_dma_kernel(GemmArgs a, int tiles_
       for (int q = 0; q < NM; ++q) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         if (q < NR) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, RPF, 0);
           const int r = s * NR + q;
           if (r % RA == RA - 1 && r / RA < PER_HALF) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
         }
@@ -626,7 +665,7 @@ __global__ __launch_bounds__(256) void gemm_i8_dma_kernel(GemmArgs a, int tiles_
     for (int q = 0; q < NM; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if (q < NR) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, RPF, 0);
         if (q < PER_HALF) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
       } else if (q < PER_HALF) {
         __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
@@ -634,7 +673,19 @@ __global__ __launch_bounds__(256) void gemm_i8_dma_kernel(GemmArgs a, int tiles_
     }
   }
   __syncthreads();  // waits for every load, including the reloads past the last step
-  epilogue_tile<BM, BN, GROUPED>(a, t, ef, smem, acc);
+  epilogue_tile<BM, BN, GROUPED, FP8>(a, t, ef, smem, acc);
+}
+
+template <int BM, int BN, int BK, int NH, bool GROUPED>
+__global__ __launch_bounds__(256) void gemm_i8_dma_kernel(GemmArgs a, int tiles_m, int tiles_n) {
+  gemm_dma_body<BM, BN, BK, NH, GROUPED, false>(a, tiles_m, tiles_n);
+}
+
+// The W8A8 FP8 product with a per-tensor / per-channel weight scale and a
+// per-token / per-tensor activation scale, applied in the epilogue.
+template <int BM, int BN, int NH>
+__global__ __launch_bounds__(256) void gemm_fp8_dma_kernel(GemmArgs a, int tiles_m, int tiles_n) {
+  gemm_dma_body<BM, BN, 128, NH, false, true>(a, tiles_m, tiles_n);
 }
 
 // ------------------------------------------------------------- general kernel
@@ -755,6 +806,169 @@ __global__ __launch_bounds__(256) void gemm_i8_kernel(GemmArgs a, int tiles_m, i
   epilogue_tile<BM, BN, GROUPED>(a, t, ef, smem, acc);
 }
 
+// ------------------------------------------------------------- FP8 kernel
+// The W8A8 FP8 product for the 128 x 128 block scales of "[SGLang] W4A8,
+// W8A8, W4A4: 혼합 정밀도 양자화 스킴" (핵심 코드 분석 §1-§2, the block path),
+// and for per-tensor / per-channel scales when K is not a multiple of 128.
+// Tiles are staged through registers into two LDS buffers (XOR-swizzled as
+// in the ring kernel), one 128-deep K step (one scale block) per buffer, zero
+// codes past K. With BLOCK, each K step's sums go to a fresh set of
+// accumulators, which are then scaled by s_x[g, t] * s_w[n / 128, g] and
+// added into the running ones (the block scales are applied per K block, so
+// they cannot wait for the epilogue); the epilogue then adds only the bias.
+// Activation scales are group-major [G, M], weight scales [ceil(N/128), G].
+template <int BM, int BN, bool BLOCK>
+__global__ __launch_bounds__(256) void gemm_fp8_kernel(GemmArgs a, int tiles_m, int tiles_n) {
+  constexpr int NT = 256, BK = 128, CH = BK / 16;
+  constexpr int STAGE = (BM + BN) * BK;
+  constexpr int SXB = BLOCK ? BM * 4 : 0;  // the step's activation scales after the tiles
+  constexpr int TM = BM / 2, TN = BN / 2, FM = TM / 32, FN = TN / 32;
+  constexpr int A_PER_T = BM * CH / NT, B_PER_T = BN * CH / NT;
+  static_assert(BM * CH % NT == 0 && BN * CH % NT == 0, "tile / thread mismatch");
+  static_assert(!BLOCK || (BN == 128 && BM <= NT), "a block-scaled tile spans one 128-column weight block");
+  static_assert(epilogue_lds_bytes<BM, BN>() <= 2 * (STAGE + SXB), "epilogue does not fit the LDS");
+
+  __shared__ __attribute__((aligned(1024))) int8_t smem[2 * (STAGE + SXB)];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const TileLoc t = locate_tile<BM, BN, false>(a, tiles_m, tiles_n);
+  const float* sw = a.s_w;
+  EpiFetch ef = epilogue_fetch<BM, BN, false>(a, t, sw, a.bias);
+  if (BLOCK) {  // the scales are applied in the main loop
+    ef.row_sx = 1.0f;
+    ef.col_sw = 1.0f;
+  }
+
+  // per-thread chunks: chunk c = tid + i * NT of the A (B) tile is row c / CH,
+  // logical chunk c % CH, stored at chunk position (c % CH) ^ swz(row)
+  const int8_t* a_src[A_PER_T];
+  int a_lds[A_PER_T], a_kc[A_PER_T];
+  bool a_ok[A_PER_T];
+#pragma unroll
+  for (int i = 0; i < A_PER_T; ++i) {
+    const int c = tid + i * NT, r = c / CH, kc = c % CH;
+    const int64_t gr = t.row_begin + r;
+    a_ok[i] = gr < t.row_end;
+    a_src[i] = a.A + (a_ok[i] ? gr : 0) * a.lda + kc * 16;
+    a_kc[i] = kc * 16;
+    a_lds[i] = r * BK + ((kc ^ swz<CH>(r)) * 16);
+  }
+  const int8_t* b_src[B_PER_T];
+  int b_lds[B_PER_T], b_kc[B_PER_T];
+  bool b_ok[B_PER_T];
+#pragma unroll
+  for (int i = 0; i < B_PER_T; ++i) {
+    const int c = tid + i * NT, r = c / CH, kc = c % CH;
+    const int64_t n = t.n_begin + r;
+    b_ok[i] = n < a.N;
+    b_src[i] = a.B + (b_ok[i] ? n : 0) * a.ldb + kc * 16;
+    b_kc[i] = kc * 16;
+    b_lds[i] = BM * BK + r * BK + ((kc ^ swz<CH>(r)) * 16);
+  }
+  const int64_t G = (a.K + BK - 1) / BK;
+  const int64_t sx_row = min(t.row_begin + (tid < BM ? tid : 0), a.M - 1);
+  const int64_t nb = t.n_begin / 128;
+
+  u32x4 ra[A_PER_T], rb[B_PER_T];
+  float rs = 0.0f;
+  auto load_tile = [&](int64_t g) __attribute__((always_inline)) {
+    const int64_t k0 = g * BK;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < A_PER_T; ++i) {
+      const bool ok = a_ok[i] && k0 + a_kc[i] < a.K;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(a_src[i] + (ok ? k0 : 0));
+      ra[i] = ok ? v : z;
+    }
+#pragma unroll
+    for (int i = 0; i < B_PER_T; ++i) {
+      const bool ok = b_ok[i] && k0 + b_kc[i] < a.K;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(b_src[i] + (ok ? k0 : 0));
+      rb[i] = ok ? v : z;
+    }
+    if (BLOCK) rs = a.s_x[g * a.M + sx_row];
+  };
+  auto store_tile = [&](int buf) __attribute__((always_inline)) {
+    int8_t* base = smem + buf * (STAGE + SXB);
+#pragma unroll
+    for (int i = 0; i < A_PER_T; ++i) *reinterpret_cast<u32x4*>(base + a_lds[i]) = ra[i];
+#pragma unroll
+    for (int i = 0; i < B_PER_T; ++i) *reinterpret_cast<u32x4*>(base + b_lds[i]) = rb[i];
+    if (BLOCK && tid < BM) reinterpret_cast<float*>(base + STAGE)[tid] = rs;
+  };
+
+  i32x16 acc[FM][FN], part[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+
+  const int fr = lane & 31, fsw = swz<CH>(fr);
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  for (int64_t g = 0; g < G; ++g) {
+    const bool more = g + 1 < G;
+    if (more) load_tile(g + 1);
+    const int8_t* base = smem + (g & 1) * (STAGE + SXB);
+#pragma unroll
+    for (int ks = 0; ks < BK / 64; ++ks) {
+      const int c0 = 4 * ks + 2 * (lane >> 5);
+      i32x8 af[FM], bf[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int8_t* p = base + (wm * TM + 32 * i + fr) * BK;
+        const i32x4 lo = *reinterpret_cast<const i32x4*>(p + ((c0 ^ fsw) * 16));
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(p + (((c0 + 1) ^ fsw) * 16));
+        af[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int8_t* p = base + BM * BK + (wn * TN + 32 * j + fr) * BK;
+        const i32x4 lo = *reinterpret_cast<const i32x4*>(p + ((c0 ^ fsw) * 16));
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(p + (((c0 + 1) ^ fsw) * 16));
+        bf[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          if (BLOCK) {
+            i32x16 z = {};
+            part[i][j] = mfma32x32x64_fp8(af[i], bf[j], ks == 0 ? z : part[i][j]);
+          } else {
+            acc[i][j] = mfma32x32x64_fp8(af[i], bf[j], acc[i][j]);
+          }
+        }
+    }
+    if (BLOCK) {
+      // acc += part * s_x[g, row] * s_w[nb, g]; the lane's rows of fragment i
+      // are 32 i + 8 q + 4 (lane / 32) + (0..3), q = register / 4
+      const float swg = sw[nb * G + g];
+      const float* sx = reinterpret_cast<const float*>(base + STAGE) + wm * TM + 4 * (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 s4 = *reinterpret_cast<const float4*>(sx + 32 * i + 8 * q);
+          const float sc[4] = {s4.x * swg, s4.y * swg, s4.z * swg, s4.w * swg};
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              acc[i][j][4 * q + r] = __float_as_int(__builtin_fmaf(__int_as_float(part[i][j][4 * q + r]), sc[r],
+                                                                   __int_as_float(acc[i][j][4 * q + r])));
+        }
+    }
+    if (more) store_tile((g + 1) & 1);
+    __syncthreads();
+  }
+  epilogue_tile<BM, BN, false, true>(a, t, ef, smem, acc);
+}
+
 namespace {
 
 struct TileCfg {
@@ -861,6 +1075,50 @@ hipError_t launch_scaled_mm(const GemmArgs& a, hipStream_t stream) {
 const char* scaled_mm_kernel_name(int64_t M, int64_t N, int64_t K) {
   const TileCfg t = pick_tile(M, N, K);
   return kernel_name(t.bm, t.bn, false, K);
+}
+
+// W8A8 FP8: per-tensor / per-channel weight scales run the ring kernel when K
+// is a multiple of 128 (the int8 tile menu), the register-staged FP8 kernel
+// otherwise; 128 x 128 block scales run the register-staged kernel with the
+// per-block scaling on 128 x 128 tiles.
+hipError_t launch_scaled_mm_fp8(const GemmArgs& a, bool block, hipStream_t stream) {
+  const dim3 block_dim(256);
+  if (block || a.K % 128 != 0) {
+    const int tm = (int)((a.M + 127) / 128), tn = (int)((a.N + 127) / 128);
+    if (block)
+      hipLaunchKernelGGL((gemm_fp8_kernel<128, 128, true>), dim3((unsigned)(tm * tn)), block_dim, 0, stream, a, tm,
+                         tn);
+    else
+      hipLaunchKernelGGL((gemm_fp8_kernel<128, 128, false>), dim3((unsigned)(tm * tn)), block_dim, 0, stream, a, tm,
+                         tn);
+    return hipGetLastError();
+  }
+  const TileCfg t = pick_tile(a.M, a.N, a.K);
+  const int tm = (int)((a.M + t.bm - 1) / t.bm), tn = (int)((a.N + t.bn - 1) / t.bn);
+  const dim3 grid((unsigned)(tm * tn));
+  if (t.bm == 256 && t.bn == 256)
+    hipLaunchKernelGGL((gemm_fp8_dma_kernel<256, 256, ring_halves<256, 256, 128>()>), grid, block_dim, 0, stream, a, tm,
+                       tn);
+  else if (t.bm == 256 && t.bn == 192)
+    hipLaunchKernelGGL((gemm_fp8_dma_kernel<256, 192, ring_halves<256, 192, 128>()>), grid, block_dim, 0, stream, a, tm,
+                       tn);
+  else if (t.bm == 256)
+    hipLaunchKernelGGL((gemm_fp8_dma_kernel<256, 128, ring_halves<256, 128, 128>()>), grid, block_dim, 0, stream, a, tm,
+                       tn);
+  else
+    hipLaunchKernelGGL((gemm_fp8_dma_kernel<128, 128, ring_halves<128, 128, 128>()>), grid, block_dim, 0, stream, a, tm,
+                       tn);
+  return hipGetLastError();
+}
+
+const char* scaled_mm_fp8_kernel_name(int64_t M, int64_t N, int64_t K, bool block) {
+  if (block) return "gemm_fp8_kernel<128, 128, true>";
+  if (K % 128 != 0) return "gemm_fp8_kernel<128, 128, false>";
+  const TileCfg t = pick_tile(M, N, K);
+  if (t.bm == 256 && t.bn == 256) return "gemm_fp8_dma_kernel<256, 256, 5>";
+  if (t.bm == 256 && t.bn == 192) return "gemm_fp8_dma_kernel<256, 192, 5>";
+  if (t.bm == 256) return "gemm_fp8_dma_kernel<256, 128, 6>";
+  return "gemm_fp8_dma_kernel<128, 128, 10>";
 }
 
 hipError_t launch_grouped_mm(const GemmArgs& a, hipStream_t stream) {

@@ -29,6 +29,18 @@ __device__ __forceinline__ i32x16 mfma32x32x32(i32x4 a, i32x4 b, i32x16 c) {
   return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
 }
 
+// v_mfma_scale_f32_32x32x64_f8f6f4 on E4M3 operands with unit (E8M0 127)
+// block scales: D[32x32] += A[32x64] * B[64x32] in binary32. Lane l supplies
+// row (A) / column (B) l % 32 and 32 consecutive k values of k-group l / 32
+// (any order consistent between A and B gives the same products); the
+// accumulators have the 32x32x32 int8 layout and are kept as bit patterns.
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ i32x16 mfma32x32x64_fp8(i32x8 a, i32x8 b, i32x16 c) {
+  return __builtin_bit_cast(i32x16, __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                         a, b, __builtin_bit_cast(f32x16, c), 0, 0, 0, 127, 0, 127));
+}
+
 __device__ __forceinline__ i32x4 as_i32x4(uint4 v) {
   i32x4 r;
   r.x = (int)v.x;

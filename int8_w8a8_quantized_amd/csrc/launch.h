@@ -77,6 +77,14 @@ const char* fused_linear_kernel_name(int64_t M, int64_t N, int64_t K);
 hipError_t launch_grouped_mm(const GemmArgs& a, hipStream_t stream);
 const char* grouped_mm_kernel_name(int64_t K);
 
+// W8A8 FP8 (quant.hip, gemm.hip). mode: 0 per token, 1 per tensor (*s_in),
+// 2 per token in groups of 128 along K (scales group-major [G, M]).
+hipError_t launch_quantize_act_fp8(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int mode,
+                                   const float* s_in, uint8_t* xq, int64_t ldq, float* s_x, hipStream_t stream);
+// a.A / a.B hold E4M3 codes; out_i32 means a binary32 output; no zero points.
+hipError_t launch_scaled_mm_fp8(const GemmArgs& a, bool block, hipStream_t stream);
+const char* scaled_mm_fp8_kernel_name(int64_t M, int64_t N, int64_t K, bool block);
+
 // MoE expert block steps (moe.hip). Routing needs moe_route_chunks(tokens) * E
 // 64-bit masks of scratch; E <= 512, k <= min(E, 64).
 int64_t moe_route_chunks(int64_t tokens);

@@ -147,6 +147,151 @@ static hipError_t launch_mode(const uint16_t* x, int64_t M, int64_t K, int64_t l
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------- FP8 activations
+// E4M3 quantisation of the W8A8 FP8 scheme ("[SGLang] W4A8, W8A8, W4A4: 혼합
+// 정밀도 양자화 스킴", 핵심 코드 분석 §1-§2): per token (s = absmax / 448),
+// with a given per-tensor scale, or per token in groups of 128 along K (the
+// block path's activation; scales stored group-major [G, M]). Each code is
+// the true quotient x / s (one IEEE division), saturated at +-448 and
+// rounded to the nearest E4M3 value, ties to even.
+enum { kFp8Token = 0, kFp8Tensor = 1, kFp8Group = 2 };
+
+// E4M3FN code of t, |t| <= 448 (not NaN). Below 2^-6 the values are the
+// multiples of 2^-9 (codes 0..8, 8 being 2^-6 itself); above, the binary32
+// mantissa is rounded to 3 bits (ties to even, a carry moves the exponent)
+// and the exponent rebiased from 127 to 7. The sign bit is kept.
+__device__ __forceinline__ uint32_t e4m3_code(float t) {
+  const uint32_t u = __float_as_uint(t);
+  const float a = fabsf(t);
+  uint32_t mag;
+  if (a < 0x1p-6f) {
+    mag = (uint32_t)rne(a * 512.0f);
+  } else {
+    uint32_t v = __float_as_uint(a);
+    v += 0x7FFFFu + ((v >> 20) & 1u);
+    mag = (((v >> 23) - 120u) << 3) | ((v >> 20) & 7u);
+  }
+  return ((u >> 24) & 0x80u) | mag;
+}
+
+// 8 bf16 values -> 8 E4M3 codes, x / s saturated at +-448.
+__device__ __forceinline__ uint2 fp8_codes8(uint4 v, float s) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t c[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    c[2 * i] = e4m3_code(fminf(fmaxf(bf16_lo(w[i]) / s, -448.0f), 448.0f));
+    c[2 * i + 1] = e4m3_code(fminf(fmaxf(bf16_hi(w[i]) / s, -448.0f), 448.0f));
+  }
+  return make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24), c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
+}
+
+// Largest magnitude over the 16 lanes of a DPP row (a group of 128 values
+// spread 8 per lane), every lane of the row receiving it.
+__device__ __forceinline__ float row16_max(float v) {
+  auto op = [](float a, float b) { return __builtin_elementwise_maximum(a, b); };
+  v = op(v, dpp_move<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = op(v, dpp_move<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = op(v, dpp_move<0x141>(v));  // row_half_mirror
+  v = op(v, dpp_move<0x140>(v));  // row_mirror
+  return v;
+}
+
+// TPR threads own one row (TPR a multiple of 64, or 64 with 4 rows per
+// workgroup); chunk j of 8 values is held by thread j % TPR in pass j / TPR,
+// so the 16 chunks of a 128-group sit in one DPP row of 16 lanes.
+template <int MODE, int TPR, int CH>
+__global__ __launch_bounds__(TPR < 256 ? 256 : TPR) void quant_fp8_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx, const float* __restrict__ s_in,
+    uint8_t* __restrict__ xq, int64_t ldq, float* __restrict__ s_x) {
+  constexpr int BLOCK = TPR < 256 ? 256 : TPR;
+  constexpr int RPB = BLOCK / TPR, WPR = TPR / 64;
+  const int sub = threadIdx.x % TPR;
+  const int64_t t = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+  const bool row_ok = t < M;
+  if (WPR == 1 && !row_ok) return;
+  const int64_t nchunk = K >> 3;
+  const uint16_t* row = x + (row_ok ? t : 0) * ldx;
+  uint4 v[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int64_t j = (int64_t)c * TPR + sub;
+    v[c] = (row_ok && j < nchunk) ? ld16(row + j * 8) : make_uint4(0, 0, 0, 0);
+  }
+  float s_row = 1.0f;
+  if (MODE == kFp8Token) {
+    float a = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) absmax8(v[c], a);
+    a = wave_extreme<true>(a);
+    if (WPR > 1) {
+      __shared__ float red[RPB][WPR > 1 ? WPR : 1];
+      const int rb = threadIdx.x / TPR;
+      if ((threadIdx.x & 63) == 0) red[rb][sub >> 6] = a;
+      __syncthreads();
+      a = red[rb][0];
+#pragma unroll
+      for (int i = 1; i < WPR; ++i) a = max_ieee(a, red[rb][i]);
+    }
+    if (!row_ok) return;
+    s_row = a == 0.0f ? 1.0f : a / 448.0f;
+    if (sub == 0) s_x[t] = s_row;
+  } else if (MODE == kFp8Tensor) {
+    if (!row_ok) return;
+    s_row = *s_in;
+  }
+  if (!row_ok) return;
+  uint8_t* orow = xq + t * ldq;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int64_t j = (int64_t)c * TPR + sub;
+    float s = s_row;
+    if (MODE == kFp8Group) {
+      float a = 0.0f;
+      absmax8(v[c], a);
+      a = row16_max(a);  // chunks past K read as zeros
+      s = a == 0.0f ? 1.0f : a / 448.0f;
+      if ((sub & 15) == 0 && j < nchunk) s_x[(j >> 4) * M + t] = s;
+    }
+    if (j < nchunk) *reinterpret_cast<uint2*>(orow + j * 8) = fp8_codes8(v[c], s);
+  }
+}
+
+hipError_t launch_quantize_act_fp8(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int mode,
+                                   const float* s_in, uint8_t* xq, int64_t ldq, float* s_x, hipStream_t stream) {
+  const int64_t nchunk = K / 8;
+  int tpr;
+  if (M <= 256)
+    tpr = nchunk <= 64 ? 64 : (nchunk <= 256 ? 256 : 1024);
+  else
+    tpr = nchunk <= 128 ? 64 : (nchunk <= 2048 ? 256 : 1024);
+  const int ch = (int)((nchunk + tpr - 1) / tpr);  // <= 8 since K <= 65536
+#define W8A8_F8(MODEV, TPRV, CHV)                                                                         \
+  hipLaunchKernelGGL((quant_fp8_kernel<MODEV, TPRV, CHV>),                                                \
+                     dim3((unsigned)(TPRV < 256 ? (M + 3) / 4 : M)), dim3(TPRV < 256 ? 256 : TPRV), 0, stream, \
+                     x, M, K, ldx, s_in, xq, ldq, s_x)
+#define W8A8_F8_CH(MODEV, TPRV)                     \
+  do {                                              \
+    if (ch <= 1) W8A8_F8(MODEV, TPRV, 1);           \
+    else if (ch <= 2) W8A8_F8(MODEV, TPRV, 2);      \
+    else if (ch <= 4) W8A8_F8(MODEV, TPRV, 4);      \
+    else W8A8_F8(MODEV, TPRV, 8);                   \
+  } while (0)
+#define W8A8_F8_TPR(MODEV)                                                    \
+  do {                                                                        \
+    if (tpr == 64) W8A8_F8_CH(MODEV, 64);                                     \
+    else if (tpr == 256) W8A8_F8_CH(MODEV, 256);                              \
+    else W8A8_F8_CH(MODEV, 1024);                                             \
+  } while (0)
+  if (mode == kFp8Token) W8A8_F8_TPR(kFp8Token);
+  else if (mode == kFp8Tensor) W8A8_F8_TPR(kFp8Tensor);
+  else W8A8_F8_TPR(kFp8Group);
+#undef W8A8_F8_TPR
+#undef W8A8_F8_CH
+#undef W8A8_F8
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int mode,
                                const float* s_in, const int32_t* zp_in, int8_t* xq, int64_t ldq,
                                float* s_x, int32_t* zp, hipStream_t stream) {

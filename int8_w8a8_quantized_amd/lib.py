@@ -27,7 +27,9 @@ OK, ERR_INVALID_ARG, ERR_NOT_IMPLEMENTED, ERR_UNSUPPORTED_DEVICE, ERR_HIP = rang
 STRATEGY_TENSOR, STRATEGY_CHANNEL, STRATEGY_TOKEN, STRATEGY_BLOCK, STRATEGY_GROUP = range(5)
 QUANT_DYN_SYM, QUANT_DYN_ASYM, QUANT_STATIC_SYM, QUANT_STATIC_ASYM = range(4)
 AZP_NONE, AZP_PER_TOKEN, AZP_STATIC = range(3)
-OUT_BF16, OUT_I32 = range(2)
+OUT_BF16, OUT_I32, OUT_F32 = range(3)
+FP8_ACT_TOKEN, FP8_ACT_TENSOR, FP8_ACT_GROUP128 = range(3)
+FP8_W_TENSOR, FP8_W_CHANNEL, FP8_W_BLOCK128 = range(3)
 FLAG_NAN_CODE, FLAG_BAD_SCALE, FLAG_NONFINITE = 1, 2, 4
 MAX_K = 65536
 MAX_PARTITIONS = 16
@@ -60,6 +62,10 @@ _SIGS = {
                                            _p, _p, _p, _p, _i32, _i64, _p]),
     "w8a8_linear_dyn_sym": (_i32, [_p, _i64, _i64, _i64, _p, _i64, _i64, _p, _i32, _p, _p, _i64,
                                    _p, _i64, _p, _p, ctypes.c_size_t, _p]),
+    "w8a8_quantize_act_fp8": (_i32, [_p, _i64, _i64, _i64, _i32, _p, _p, _i64, _p, _p]),
+    "w8a8_scaled_mm_fp8": (_i32, [_p, _i64, _i64, _i64, _p, _i64, _i64, _p, _i32, _p, _i32, _p, _p, _i32,
+                                  _i64, _p]),
+    "w8a8_scaled_mm_fp8_kernel_name": (ctypes.c_char_p, [_i64, _i64, _i64, _i32]),
     "w8a8_moe_route_workspace_size": (ctypes.c_size_t, [_i64, _i64]),
     "w8a8_moe_route": (_i32, [_p, _i64, _i64, _i64, _i32, _p, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]),
     "w8a8_silu_mul_quant": (_i32, [_p, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p]),
@@ -436,3 +442,40 @@ def moe_block_int8(x, logits, topk: int, w13, s13, w2, s2, out=None, workspace=N
                                     _ptr(workspace), workspace.numel(), _stream())
     _raise(st, "w8a8_moe_block_int8")
     return out
+
+
+def quantize_act_fp8(x, mode: int = FP8_ACT_TOKEN, s_in=None, xq=None, s_x=None):
+    """E4M3 codes of bf16 x [M, K] (as uint8). Returns (xq uint8 [M, K],
+    s_x: float [M] (TOKEN), float [G, M] (GROUP128) or None (TENSOR))."""
+    import torch
+    M, K = x.shape
+    dev = x.device
+    if xq is None:
+        xq = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    if s_x is None and mode != FP8_ACT_TENSOR:
+        s_x = torch.empty(M if mode == FP8_ACT_TOKEN else (-(-K // 128), M), dtype=torch.float32, device=dev)
+    st = load().w8a8_quantize_act_fp8(_ptr(x), M, K, x.stride(0) if M else K, mode, _ptr(s_in), _ptr(xq),
+                                      xq.stride(0) if M else K, _ptr(s_x) if mode != FP8_ACT_TENSOR else None,
+                                      _stream())
+    _raise(st, "w8a8_quantize_act_fp8")
+    return xq, (s_x if mode != FP8_ACT_TENSOR else None)
+
+
+def scaled_mm_fp8(xq, Wq, s_x, s_w, act_mode: int, w_mode: int, bias=None, out_dtype: int = OUT_BF16, out=None):
+    """The W8A8 FP8 GEMM on E4M3 codes (uint8): xq [M, K], Wq [N, K]; scales as
+    w8a8_scaled_mm_fp8 documents. Returns bf16 (or float32) [M, N]."""
+    import torch
+    M, K = xq.shape
+    N = Wq.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16 if out_dtype == OUT_BF16 else torch.float32,
+                          device=xq.device)
+    st = load().w8a8_scaled_mm_fp8(_ptr(xq), M, K, xq.stride(0) if M else K, _ptr(Wq), N,
+                                   Wq.stride(0) if N else K, _ptr(s_x), act_mode, _ptr(s_w), w_mode, _ptr(bias),
+                                   _ptr(out), out_dtype, out.stride(0) if M else N, _stream())
+    _raise(st, "w8a8_scaled_mm_fp8")
+    return out
+
+
+def scaled_mm_fp8_kernel_name(M: int, N: int, K: int, w_mode: int) -> str:
+    return load().w8a8_scaled_mm_fp8_kernel_name(M, N, K, w_mode).decode()

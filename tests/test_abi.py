@@ -16,7 +16,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = W.header_functions()
-    assert len(names) == 22, names
+    assert len(names) == 25, names
     for n in names:
         assert hasattr(L, n), n
 
