@@ -41,6 +41,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA, TOPS
+FP8_PEAK_TFLOPS = 5000.0     # MI355X dense fp8 MFMA, TFLOP/s
 ROTATE_BYTES = 1 << 30       # weight bytes cycled between reuses of one copy, per shape
 GRAPH_STEPS = 16             # distinct step graphs (weight-rotation period)
 
@@ -159,6 +160,11 @@ class Timer:
         return 1e3 * e0.elapsed_time(e1) / (reps * launches)
 
 
+def progress(msg):
+    """One line on stderr per finished section (the JSON line stays alone on stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def capture(torch, fn):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
@@ -269,6 +275,7 @@ def main():
     ms_per_step = 1e3 * elapsed / args.steps
     value = step_bytes / (elapsed / args.steps) / 1e9
 
+    progress(f"decode step: {value:.1f} GB/s")
     # ---------------------------------------- per-kernel launch durations
     # One graph per shape of back-to-back launches over that shape's weight
     # copies; HIP events on the launch stream around its replays.
@@ -319,6 +326,7 @@ def main():
                    "GBs": round(v["bytes"] / (v["us"] * 1e-6) / 1e9, 1)} for k, v in per_kernel.items()}
     del graphs
 
+    progress("decode per-kernel durations done")
     # ------------------------------------------------------------ prefill TOPS
     prefill = None
     if not args.no_prefill:
@@ -351,7 +359,11 @@ def main():
         torch.cuda.synchronize()
 
     extra = None if args.no_extra else extra_sections(torch, np, W, synth, to_dev, timer, dev)
+    if extra is not None:
+        extra["fp8_prefill"] = fp8_section(torch, W, synth, to_dev, timer, dev)
+        progress("fp8 section done")
 
+    progress("prefill and extra sections done")
     # ------------------------------------------------------------- CPU oracle
     cpu = None
     if not args.no_cpu:
@@ -455,6 +467,7 @@ def extra_sections(torch, np, W, synth, to_dev, timer, dev):
         qw[name] = (Wq, s)
         del codes, S
     out["fp8_block_to_int8"] = conv
+    progress("fp8 conversion done")
 
     x13 = to_dev(m["x13"])
     x2 = to_dev(m["x2"])
@@ -484,10 +497,49 @@ def extra_sections(torch, np, W, synth, to_dev, timer, dev):
     moe["quant_w2_input_32768x1536"] = {"us": round(qus, 1),
                                          "GBs": round(quant_bytes(T, 1536) / (qus * 1e-6) / 1e9, 1)}
     out["moe_grouped"] = moe
+    progress("grouped GEMMs done")
     del xq2, sx2, x2
     out["moe_block"] = moe_block_section(torch, W, timer, dev, x13, logits, topk, qw)
     torch.cuda.synchronize()
     return out
+
+
+def fp8_section(torch, W, synth, to_dev, timer, dev):
+    """The W8A8 FP8 GEMM on the prefill shapes: E4M3 activations quantised on
+    the device (per token, or per token in groups of 128), E4M3 weights of
+    N(0, 1) values scaled to the format's range, per-channel or 128 x 128
+    block scales; TFLOP/s against the fp8 peak, plus the quantiser's time."""
+    res = {}
+    for M in synth.PREFILL_M:
+        for (K, N) in synth.DECODE_KN:
+            d = synth.prefill(M, K, N)
+            x = to_dev(d["x"])
+            g = torch.Generator(device=dev)
+            g.manual_seed(M * 7 + K * 3 + N)
+            w8 = (torch.randn((N, K), device=dev, generator=g) * 100).clamp(-448, 448).to(
+                torch.float8_e4m3fn).view(torch.uint8)
+            sw_ch = torch.rand(N, device=dev, generator=g) * 1e-4 + 1e-5
+            G, NB = -(-K // 128), -(-N // 128)
+            sw_blk = torch.rand((NB, G), device=dev, generator=g) * 1e-4 + 1e-5
+            out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            row = {}
+            for name, act, wm, sw in (("channel", W.FP8_ACT_TOKEN, W.FP8_W_CHANNEL, sw_ch),
+                                      ("block128", W.FP8_ACT_GROUP128, W.FP8_W_BLOCK128, sw_blk)):
+                xq, sx = W.quantize_act_fp8(x, act)
+                R = 5
+                gq = capture(torch, lambda: [W.quantize_act_fp8(x, act, xq=xq, s_x=sx) for _ in range(R)])
+                qus = timer.graph_us(gq, R)
+                gg = capture(torch, lambda: [W.scaled_mm_fp8(xq, w8, sx, sw, act, wm, out=out) for _ in range(R)])
+                us = timer.graph_us(gg, R)
+                del gq, gg
+                tf = 2.0 * M * N * K / (us * 1e-6) / 1e12
+                row[name] = {"kernel": W.scaled_mm_fp8_kernel_name(M, N, K, wm), "gemm_us": round(us, 1),
+                             "TFLOPS": round(tf, 1), "frac": round(tf / FP8_PEAK_TFLOPS, 4),
+                             "quant_us": round(qus, 1)}
+            res[f"{M}x{K}x{N}"] = row
+            del x, w8, out
+    torch.cuda.synchronize()
+    return res
 
 
 def moe_block_section(torch, W, timer, dev, x, logits, topk, qw):

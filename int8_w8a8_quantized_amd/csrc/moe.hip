@@ -7,10 +7,9 @@
 // W8A8, W4A4: 혼합 정밀도 양자화 스킴" (구조도).
 //
 // Routing (moe_topk_kernel): one wave per token, lane l holding the logits of
-// experts l, l + 64, ... Each of the k rounds takes the wave maximum of a
-// 64-bit key (the logit mapped to an order-preserving integer above the
-// complement of the expert index, so equal logits go to the lower index)
-// and retires the winner. The weights are the softmax of the k selected
+// experts l, l + 64, ... Each expert is ranked by counting the experts that
+// beat it (a larger logit, or an equal one and a lower index); the k ranked
+// first are the selection, in rank order. The weights are the softmax of the k selected
 // logits. Tokens are taken 64 at a time per workgroup (a chunk); for each
 // expert the workgroup publishes a 64-bit mask of the chunk's tokens routed
 // to it.
@@ -32,7 +31,7 @@
 
 namespace w8a8 {
 
-constexpr int kRouteChunk = 64;  // tokens per routing workgroup: one 64-bit mask per expert
+constexpr int kRouteChunk = 32;  // tokens per routing workgroup (at most 64: one 64-bit mask per expert)
 
 // Order-preserving map of a float onto unsigned integers (larger float ->
 // larger integer; -0 and +0 apart, which does not matter for a maximum).
@@ -41,95 +40,131 @@ __device__ __forceinline__ uint32_t float_key(float v) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const uint64_t w = __shfl_xor(v, o, kWave);
-    v = w > v ? w : v;
-  }
-  return v;
-}
 
+constexpr int kRouteWaves = 16;  // waves per routing workgroup: 2 tokens each
+
+// Each wave ranks its tokens' experts: 64-bit keys (the logit mapped to an
+// order-preserving integer above the complement of the expert index, so a
+// larger key is a larger logit or an equal one with a lower index) go to
+// the wave's LDS row, and every lane counts, for each of its experts, the
+// larger keys, reading the row as broadcast 16-byte loads. The experts
+// ranked below k are the selection, in rank order; no chain of cross-lane
+// reductions is involved.
 template <int EPL>
-__global__ __launch_bounds__(256) void moe_topk_kernel(const float* __restrict__ logits, int64_t ldl,
-                                                       int64_t tokens, int E, int k,
-                                                       int32_t* __restrict__ ids, float* __restrict__ wts,
-                                                       uint64_t* __restrict__ masks) {
-  __shared__ unsigned long long mask[64 * EPL];
+__global__ __launch_bounds__(64 * kRouteWaves) void moe_topk_kernel(const float* __restrict__ logits, int64_t ldl,
+                                                                     int64_t tokens, int E, int k,
+                                                                     int32_t* __restrict__ ids,
+                                                                     float* __restrict__ wts,
+                                                                     uint64_t* __restrict__ masks) {
+  constexpr int EP = 64 * EPL;
+  __shared__ unsigned long long mask[EP];
+  __shared__ __attribute__((aligned(16))) uint64_t kbuf[kRouteWaves][EP];
+  __shared__ float topv[kRouteWaves];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t c = blockIdx.x;
-  for (int e = threadIdx.x; e < E; e += 256) mask[e] = 0ull;
+  for (int e = threadIdx.x; e < E; e += 64 * kRouteWaves) mask[e] = 0ull;
   __syncthreads();
-  for (int lt = wave; lt < kRouteChunk; lt += 4) {
+  // the wave's tokens lt = wave, wave + 16, ...: every logit load is issued
+  // before the first token is ranked
+  constexpr int TPW = kRouteChunk / kRouteWaves;
+  float lv[TPW][EPL];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int64_t t = c * kRouteChunk + wave + kRouteWaves * i;
+#pragma unroll
+    for (int q = 0; q < EPL; ++q) {
+      const int e = lane + 64 * q;
+      lv[i][q] = (t < tokens && e < E) ? logits[t * ldl + e] : 0.0f;
+    }
+  }
+  uint64_t* kw = kbuf[wave];
+  const int E2 = (E + 1) & ~1;
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int lt = wave + kRouteWaves * i;
     const int64_t t = c * kRouteChunk + lt;
     if (t >= tokens) break;
-    const float* row = logits + t * ldl;
-    // keys of this lane's experts: 0 for none (a real logit's key is > 0)
     uint64_t key[EPL];
 #pragma unroll
     for (int q = 0; q < EPL; ++q) {
       const int e = lane + 64 * q;
-      key[q] = e < E ? ((uint64_t)float_key(row[e]) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e) : 0ull;
+      key[q] = ((uint64_t)float_key(lv[i][q]) << 32) | (uint32_t)~(uint32_t)e;
+      if (e < E2) kw[e] = e < E ? key[q] : 0ull;  // the padding key loses to every expert
     }
-    int my_e = 0;
-    float my_v = 0.0f, top = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      uint64_t best = 0ull;
+    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's own LDS writes, in order
+    int rank[EPL];
 #pragma unroll
-      for (int q = 0; q < EPL; ++q) best = key[q] > best ? key[q] : best;
-      best = wave_max_u64(best);
-      // k <= E leaves a live key in every round; the clamp keeps the read in
-      // the row regardless
-      const int e = min(max((int)(0xFFFFFFFFu - (uint32_t)best), 0), E - 1);
-      const float v = row[e];  // the winner's logit (a cache hit)
+    for (int q = 0; q < EPL; ++q) rank[q] = 0;
+    for (int e0 = 0; e0 < E2; e0 += 2) {
+      const ulonglong2 o = *reinterpret_cast<const ulonglong2*>(kw + e0);
 #pragma unroll
-      for (int q = 0; q < EPL; ++q)
-        if (lane + 64 * q == e) key[q] = 0ull;
-      if (lane == j) {
-        my_e = e;
-        my_v = v;
+      for (int q = 0; q < EPL; ++q) rank[q] += (o.x > key[q] ? 1 : 0) + (o.y > key[q] ? 1 : 0);
+    }
+    // the winner's logit, then the softmax over the k selected
+#pragma unroll
+    for (int q = 0; q < EPL; ++q)
+      if (lane + 64 * q < E && rank[q] == 0) topv[wave] = lv[i][q];
+    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const float top = topv[wave];
+    float ex[EPL], part = 0.0f;
+#pragma unroll
+    for (int q = 0; q < EPL; ++q) {
+      const bool sel = lane + 64 * q < E && rank[q] < k;
+      ex[q] = sel ? expf(lv[i][q] - top) : 0.0f;
+      part += ex[q];
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o, kWave);
+#pragma unroll
+    for (int q = 0; q < EPL; ++q) {
+      const int e = lane + 64 * q;
+      if (e < E && rank[q] < k) {
+        ids[t * k + rank[q]] = e;
+        wts[t * k + rank[q]] = ex[q] / part;
+        atomicOr(&mask[e], 1ull << lt);
       }
-      if (j == 0) top = v;
-    }
-    // softmax of the k selected logits, the largest one subtracted first
-    const float ex = lane < k ? expf(my_v - top) : 0.0f;
-    float sum = ex;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, kWave);
-    if (lane < k) {
-      ids[t * k + lane] = my_e;
-      wts[t * k + lane] = ex / sum;
-      atomicOr(&mask[my_e], 1ull << lt);
     }
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += 256) masks[c * E + e] = mask[e];
+  for (int e = threadIdx.x; e < E; e += 64 * kRouteWaves) masks[c * E + e] = mask[e];
 }
 
 template <int EPL>
-__global__ __launch_bounds__(256) void moe_scatter_kernel(const int32_t* __restrict__ ids,
-                                                          const uint64_t* __restrict__ masks, int64_t tokens,
-                                                          int E, int k, int64_t nchunks,
-                                                          int32_t* __restrict__ row_ids,
-                                                          int32_t* __restrict__ offsets,
-                                                          int32_t* __restrict__ pos) {
+__global__ __launch_bounds__(1024) void moe_scatter_kernel(const int32_t* __restrict__ ids,
+                                                           const uint64_t* __restrict__ masks, int64_t tokens,
+                                                           int E, int k, int64_t nchunks,
+                                                           int32_t* __restrict__ row_ids,
+                                                           int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ pos) {
+  constexpr int NT = 1024, U = 4;
   __shared__ int total[64 * EPL], before[64 * EPL], start[64 * EPL + 1];
   __shared__ unsigned long long own[64 * EPL];
   const int64_t c = blockIdx.x;
-  for (int e = threadIdx.x; e < E; e += 256) {
+  for (int e = threadIdx.x; e < E; e += NT) {
     total[e] = 0;
     before[e] = 0;
     own[e] = masks[c * E + e];
   }
   __syncthreads();
-  // routed tokens per expert over all chunks, and over the chunks before this one
+  // routed tokens per expert over all chunks, and over the chunks before this
+  // one: U mask loads in flight per thread, then their popcounts
   const int64_t cells = nchunks * E;
-  for (int64_t i = threadIdx.x; i < cells; i += 256) {
-    const int e = (int)(i % E);
-    const int n = __popcll(masks[i]);
-    if (n) {
-      atomicAdd(&total[e], n);
-      if (i / E < c) atomicAdd(&before[e], n);
+  for (int64_t i0 = threadIdx.x; i0 < cells; i0 += (int64_t)NT * U) {
+    uint64_t m[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = i0 + (int64_t)u * NT;
+      m[u] = i < cells ? masks[i] : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = i0 + (int64_t)u * NT;
+      const int n = __popcll(m[u]);
+      if (n) {
+        const int e = (int)(i % E);
+        atomicAdd(&total[e], n);
+        if (i / E < c) atomicAdd(&before[e], n);
+      }
     }
   }
   __syncthreads();
@@ -153,9 +188,9 @@ __global__ __launch_bounds__(256) void moe_scatter_kernel(const int32_t* __restr
   }
   __syncthreads();
   if (c == 0)
-    for (int e = threadIdx.x; e <= E; e += 256) offsets[e] = start[e];
+    for (int e = threadIdx.x; e <= E; e += NT) offsets[e] = start[e];
   // every routed pair of this chunk
-  for (int p = threadIdx.x; p < kRouteChunk * k; p += 256) {
+  for (int p = threadIdx.x; p < kRouteChunk * k; p += NT) {
     const int lt = p / k;
     const int64_t t = c * kRouteChunk + lt;
     if (t >= tokens) break;
@@ -168,11 +203,22 @@ __global__ __launch_bounds__(256) void moe_scatter_kernel(const int32_t* __restr
 }
 
 // silu(g) = g / (1 + exp(-g)) in binary32, written as g e' / (1 + e) with
-// e = exp(-|g|) and e' = 1 (g >= 0) or e (g < 0), so no exponential overflows
-// and very negative gates keep their small (possibly subnormal) product.
+// e = exp(-|g|) and e' = 1 (g >= 0) or e (g < 0), so no exponential overflows.
+// e = 2^(a log2 e) for a = -|g|: the product is split into its rounded value
+// t (log2 e in two parts) and the exact remainder r, e = 2^t (1 + r ln 2) from
+// the hardware exp2 (v_exp_f32), and the quotient uses the hardware reciprocal
+// (v_rcp_f32): a few units in the last place of binary32 in all, against the
+// 2^16 units between neighbouring bf16 values the result is rounded to.
 __device__ __forceinline__ float silu(float g) {
-  const float e = expf(-fabsf(g));
-  return (g >= 0.0f ? g : g * e) / (1.0f + e);
+  constexpr float kLog2eHi = 1.44269502162933349609375f;  // binary32 log2(e)
+  constexpr float kLog2eLo = 1.92596298909109e-8f;        // log2(e) - kLog2eHi
+  constexpr float kLn2 = 0.693147180559945309f;
+  const float a = -fabsf(g);
+  const float t = a * kLog2eHi;
+  const float r = fmaf(a, kLog2eHi, -t) + a * kLog2eLo;
+  const float p = __builtin_amdgcn_exp2f(t);
+  const float e = fmaf(p, r * kLn2, p);
+  return (g >= 0.0f ? g : g * e) * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
 // silu(g) * u, rounded to bf16 (both halves of the result word).
@@ -285,14 +331,14 @@ hipError_t launch_moe_route(const float* logits, int64_t ldl, int64_t tokens, in
                             float* wts, int32_t* row_ids, int32_t* offsets, int32_t* pos, uint64_t* masks,
                             hipStream_t stream) {
   const int64_t nch = moe_route_chunks(tokens);
-  const dim3 grid((unsigned)nch), block(256);
+  const dim3 grid((unsigned)nch), block(64 * kRouteWaves), block_s(1024);
 #define W8A8_ROUTE(EPLV)                                                                                      \
   do {                                                                                                      \
     hipLaunchKernelGGL((moe_topk_kernel<EPLV>), grid, block, 0, stream, logits, ldl, tokens, E, k, ids, wts,  \
                        masks);                                                                              \
     hipError_t e = hipGetLastError();                                                                       \
     if (e != hipSuccess) return e;                                                                          \
-    hipLaunchKernelGGL((moe_scatter_kernel<EPLV>), grid, block, 0, stream, ids, masks, tokens, E, k, nch,   \
+    hipLaunchKernelGGL((moe_scatter_kernel<EPLV>), grid, block_s, 0, stream, ids, masks, tokens, E, k, nch, \
                        row_ids, offsets, pos);                                                              \
     return hipGetLastError();                                                                               \
   } while (0)

@@ -219,7 +219,7 @@ def test_moe_calls_reject_before_device_work(L):
     assert route(nbytes=8) == W.ERR_INVALID_ARG
     assert route(logits=None) == W.ERR_INVALID_ARG
     assert route(tokens=0) == W.OK
-    assert L.w8a8_moe_route_workspace_size(4096, 64) == 64 * 64 * 8
+    assert L.w8a8_moe_route_workspace_size(4096, 64) == 128 * 64 * 8  # one 64-bit mask per expert and 32 tokens
     assert L.w8a8_moe_route_workspace_size(0, 64) == 0
 
     def smq(T=4, I=64, ldh=128, ldq=64, h=FAKE, act=None, ld_act=0):
