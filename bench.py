@@ -146,18 +146,32 @@ class Timer:
     def __init__(self, torch, stream):
         self.torch, self.stream = torch, stream
 
-    def graph_us(self, graph, launches, reps=3):
-        """Average microseconds per launch of a graph holding `launches` launches."""
+    def graph_us(self, graph, launches, reps=5, warm_ms=20.0):
+        """Microseconds per launch of a graph holding `launches` launches, in
+        steady state: the graph is first replayed until at least warm_ms of
+        GPU time has passed (the first replays after a capture, or after other
+        work, run at a lower clock), then `reps` replays are timed back to
+        back, each between its own pair of events, and the median is taken."""
         torch = self.torch
-        graph.replay()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(self.stream)
-        for _ in range(reps):
+        done = 0.0
+        while True:
+            w0 = torch.cuda.Event(enable_timing=True)
+            w1 = torch.cuda.Event(enable_timing=True)
+            w0.record(self.stream)
             graph.replay()
-        e1.record(self.stream)
-        e1.synchronize()
-        return 1e3 * e0.elapsed_time(e1) / (reps * launches)
+            w1.record(self.stream)
+            w1.synchronize()
+            done += w0.elapsed_time(w1)
+            if done >= warm_ms:
+                break
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record(self.stream)
+        for i in range(reps):
+            graph.replay()
+            ev[i + 1].record(self.stream)
+        ev[-1].synchronize()
+        per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))
+        return 1e3 * per[reps // 2] / launches
 
 
 def progress(msg):
