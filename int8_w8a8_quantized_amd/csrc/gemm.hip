@@ -969,6 +969,146 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(GemmArgs a, int tiles_m, 
   epilogue_tile<BM, BN, false, true>(a, t, ef, smem, acc);
 }
 
+// The 128 x 128 block-scaled FP8 product with its tiles in a ring of S
+// direct-to-LDS stages (K a multiple of 128): stage g holds K step g (one
+// scale block) of the tile's 128 A rows and 128 B rows (XOR-swizzled 16-byte
+// chunks, as in the ring kernel), the step's 128 activation scales and its
+// weight-block scale; every wave issues the same 9 loads per stage (4 of A,
+// 4 of B, one of 32 activation scales plus a copy of the weight scale), so
+// its own vmcnt tells it when its part of a stage has landed, and no other
+// global load sits behind them in the loop. S - 1 stages
+// are in flight; stage g + S - 1 goes into the slot step g - 1 used, after
+// the barrier that opens step g. Each step's two 64-deep slices go to fresh
+// accumulators, which are scaled by s_x[g, row] * s_w[n / 128, g] and added
+// into the running ones.
+template <int S>
+__global__ __launch_bounds__(256) void gemm_fp8_block_dma_kernel(GemmArgs a, int tiles_m, int tiles_n) {
+  constexpr int BM = 128, BN = 128, BK = 128, CH = BK / 16;
+  constexpr int TM = BM / 2, TN = BN / 2, FM = TM / 32, FN = TN / 32;
+  constexpr int AB = (BM + BN) * BK;       // tile bytes of a stage
+  constexpr int STG = AB + 1024;           // + 4 x 256 B of scales (wave w: s_x rows 32w.., then s_w)
+  constexpr int PER_STAGE = 9;             // loads per wave per stage
+  static_assert(S >= 3 && (S - 2) * PER_STAGE <= 63, "ring / vmcnt range");
+  static_assert(epilogue_lds_bytes<BM, BN>() <= S * STG, "epilogue does not fit the LDS");
+  __shared__ __attribute__((aligned(1024))) int8_t smem[S * STG];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const TileLoc t = locate_tile<BM, BN, false>(a, tiles_m, tiles_n);
+  EpiFetch ef = epilogue_fetch<BM, BN, false>(a, t, a.s_w, a.bias);
+  ef.row_sx = 1.0f;  // the scales are applied in the main loop
+  ef.col_sw = 1.0f;
+  const int G = (int)(a.K / BK);
+  const int64_t nb = t.n_begin / 128;
+
+  // DMA sources: instruction q of this wave fills tile rows (wave * 4 + q) * 8
+  // .. + 7 of A (of B); lane l writes row + l / 8, physical chunk l % 8, which
+  // holds logical chunk (l % 8) ^ swz(row). Rows past the matrix load its last
+  // row (never stored).
+  const int lrow = lane >> 3, pch = lane & 7;
+  const int8_t* a_src[4];
+  const int8_t* b_src[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = (wave * 4 + q) * 8 + lrow;
+    a_src[q] = a.A + min(t.row_begin + r, a.M - 1) * a.lda + ((pch ^ swz<CH>(r)) * 16);
+    b_src[q] = a.B + min(t.n_begin + r, a.N - 1) * a.ldb + ((pch ^ swz<CH>(r)) * 16);
+  }
+  // scales: lanes 0 .. 31 of wave w load s_x of rows 32 w .. 32 w + 31,
+  // lane 32 the weight block's scale (group-major s_x, stride M; s_w stride 1)
+  const bool sc_lane = lane <= 32;
+  const float* sc_src = lane < 32 ? a.s_x + min(t.row_begin + wave * 32 + lane, a.M - 1) : a.s_w + nb * G;
+  const int64_t sc_step = lane < 32 ? a.M : 1;
+
+  // the loads of stage h into slot h % S (past the last step: a reload of it)
+  auto issue = [&](int h) __attribute__((always_inline)) {
+    int8_t* dst = smem + (h % S) * STG;
+    const int g = min(h, G - 1);
+    const int64_t k0 = (int64_t)g * BK;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      __builtin_amdgcn_global_load_lds((global_void_ptr)(a_src[q] + k0), (lds_void_ptr)(dst + (wave * 4 + q) * 1024),
+                                       16, 0, 0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      __builtin_amdgcn_global_load_lds((global_void_ptr)(b_src[q] + k0),
+                                       (lds_void_ptr)(dst + BM * BK + (wave * 4 + q) * 1024), 16, 0, 0);
+    if (sc_lane)
+      __builtin_amdgcn_global_load_lds((global_void_ptr)(sc_src + g * sc_step), (lds_void_ptr)(dst + AB + wave * 256),
+                                       4, 0, 0);
+  };
+
+  i32x16 acc[FM][FN], part[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+
+  const int fr = lane & 31, fsw = swz<CH>(fr);
+#pragma unroll
+  for (int h = 0; h < S - 1; ++h) issue(h);
+  for (int g = 0; g < G; ++g) {
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<(S - 2) * PER_STAGE>();  // this wave's part of stage g has landed
+    __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    issue(g + S - 1);  // into the slot of step g - 1, which every wave has finished reading
+    const int8_t* base = smem + (g % S) * STG;
+#pragma unroll
+    for (int ks = 0; ks < BK / 64; ++ks) {
+      const int c0 = 4 * ks + 2 * (lane >> 5);
+      i32x8 af[FM], bf[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int8_t* p = base + (wm * TM + 32 * i + fr) * BK;
+        const i32x4 lo = *reinterpret_cast<const i32x4*>(p + ((c0 ^ fsw) * 16));
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(p + (((c0 + 1) ^ fsw) * 16));
+        af[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int8_t* p = base + BM * BK + (wn * TN + 32 * j + fr) * BK;
+        const i32x4 lo = *reinterpret_cast<const i32x4*>(p + ((c0 ^ fsw) * 16));
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(p + (((c0 + 1) ^ fsw) * 16));
+        bf[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          i32x16 z = {};
+          part[i][j] = mfma32x32x64_fp8(af[i], bf[j], ks == 0 ? z : part[i][j]);
+        }
+    }
+    // acc += part * s_x[g, row] * s_w[nb, g]; the lane's rows of fragment i
+    // are 32 i + 8 q + 4 (lane / 32) + (0..3), q = register / 4
+    // (read as integers, like the tiles: typed float reads of the stage make
+    // the compiler wait for every load in flight)
+    const int* scl = reinterpret_cast<const int*>(base + AB);
+    const float swg = __int_as_float(scl[wave * 64 + 32]);
+    const int* sx = scl + wm * 128 + 4 * (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const i32x4 s4 = *reinterpret_cast<const i32x4*>(sx + 64 * i + 8 * q);  // rows 32 (2 wm + i) + ..
+        const float sc[4] = {__int_as_float(s4[0]) * swg, __int_as_float(s4[1]) * swg, __int_as_float(s4[2]) * swg,
+                             __int_as_float(s4[3]) * swg};
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            acc[i][j][4 * q + r] = __float_as_int(__builtin_fmaf(__int_as_float(part[i][j][4 * q + r]), sc[r],
+                                                                 __int_as_float(acc[i][j][4 * q + r])));
+      }
+  }
+  wait_vmcnt<0>();
+  __syncthreads();  // every load has landed, including the reloads past the last step
+  epilogue_tile<BM, BN, false, true>(a, t, ef, smem, acc);
+}
+
 namespace {
 
 struct TileCfg {
@@ -1077,6 +1217,8 @@ const char* scaled_mm_kernel_name(int64_t M, int64_t N, int64_t K) {
   return kernel_name(t.bm, t.bn, false, K);
 }
 
+constexpr int kFp8BlockStages = 4;  // stages of the block-scaled FP8 ring (4 x 33 KiB of LDS)
+
 // W8A8 FP8: per-tensor / per-channel weight scales run the ring kernel when K
 // is a multiple of 128 (the int8 tile menu), the register-staged FP8 kernel
 // otherwise; 128 x 128 block scales run the register-staged kernel with the
@@ -1085,7 +1227,10 @@ hipError_t launch_scaled_mm_fp8(const GemmArgs& a, bool block, hipStream_t strea
   const dim3 block_dim(256);
   if (block || a.K % 128 != 0) {
     const int tm = (int)((a.M + 127) / 128), tn = (int)((a.N + 127) / 128);
-    if (block)
+    if (block && a.K % 128 == 0)
+      hipLaunchKernelGGL((gemm_fp8_block_dma_kernel<kFp8BlockStages>), dim3((unsigned)(tm * tn)), block_dim, 0, stream,
+                         a, tm, tn);
+    else if (block)
       hipLaunchKernelGGL((gemm_fp8_kernel<128, 128, true>), dim3((unsigned)(tm * tn)), block_dim, 0, stream, a, tm,
                          tn);
     else
@@ -1112,7 +1257,7 @@ hipError_t launch_scaled_mm_fp8(const GemmArgs& a, bool block, hipStream_t strea
 }
 
 const char* scaled_mm_fp8_kernel_name(int64_t M, int64_t N, int64_t K, bool block) {
-  if (block) return "gemm_fp8_kernel<128, 128, true>";
+  if (block) return K % 128 == 0 ? "gemm_fp8_block_dma_kernel<4>" : "gemm_fp8_kernel<128, 128, true>";
   if (K % 128 != 0) return "gemm_fp8_kernel<128, 128, false>";
   const TileCfg t = pick_tile(M, N, K);
   if (t.bm == 256 && t.bn == 256) return "gemm_fp8_dma_kernel<256, 256, 5>";
