@@ -44,6 +44,7 @@ INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA, TOPS
 FP8_PEAK_TFLOPS = 5000.0     # MI355X dense fp8 MFMA, TFLOP/s
 ROTATE_BYTES = 1 << 30       # weight bytes cycled between reuses of one copy, per shape
 GRAPH_STEPS = 16             # distinct step graphs (weight-rotation period)
+SECTIONS = ("decode", "prefill", "static", "moe", "fp8")
 
 
 def gemm_bytes(M, K, N, bias=False, asym=False):
@@ -132,12 +133,24 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-prefill", action="store_true", help="skip the prefill TOPS section")
     p.add_argument("--no-extra", action="store_true", help="skip the static / MoE / FP8 sections")
+    p.add_argument("--sections", default=",".join(SECTIONS),
+                   help="comma-separated subset of %s (a run without decode reports no value; "
+                        "for profiling one part)" % ",".join(SECTIONS))
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="minimum CPU time of the oracle sample")
     p.add_argument("--calib-copy", action="store_true",
                    help="first copy 256 MiB device-to-device once (the known-size reference for "
                         "rocprofv3 FETCH_SIZE / WRITE_SIZE)")
-    return p.parse_args()
+    args = p.parse_args()
+    args.sections = {x.strip() for x in args.sections.split(",") if x.strip()}
+    unknown = args.sections - set(SECTIONS)
+    if unknown:
+        p.error(f"unknown sections {sorted(unknown)}")
+    if args.no_prefill:
+        args.sections.discard("prefill")
+    if args.no_extra:
+        args.sections -= {"static", "moe", "fp8"}
+    return args
 
 
 class Timer:
@@ -186,41 +199,9 @@ def capture(torch, fn):
     return g
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(across GPUs the layer would shard by output columns)", file=sys.stderr)
-        return 2
-
-    import numpy as np
-    import torch
-
-    from int8_w8a8_quantized_amd import lib as W
-    from int8_w8a8_quantized_amd import synth
-
-    W.init(0)
-    dev = "cuda:0"
-
-    def to_dev(a):
-        a = np.ascontiguousarray(a)
-        if a.dtype == np.uint16:
-            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
-        return torch.from_numpy(a).to(dev)
-
-    if args.calib_copy:
-        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-
-    # Graph capture runs on a side stream; all timing happens on this one.
-    stream = torch.cuda.Stream()
-    torch.cuda.set_stream(stream)
-    timer = Timer(torch, stream)
-
-    # ---------------------------------------------------------------- inputs
+def decode_section(args, torch, W, synth, to_dev, timer, dev):
+    """The headline decode step (16 linears, each the quantiser and the scaled
+    GEMM), timed as whole-step graph replays, then each shape on its own."""
     shapes = [(M, K, N) for M in synth.DECODE_M for (K, N) in synth.DECODE_KN]
     pools = {}
     for (K, N) in synth.DECODE_KN:
@@ -341,9 +322,50 @@ def main():
     del graphs
 
     progress("decode per-kernel durations done")
+    return dict(value=value, ms_per_step=ms_per_step, step_bytes=step_bytes, roofline=roofline,
+                kernels=kernels, per_shape=per_shape, shapes=shapes)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(across GPUs the layer would shard by output columns)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from int8_w8a8_quantized_amd import lib as W
+    from int8_w8a8_quantized_amd import synth
+
+    W.init(0)
+    dev = "cuda:0"
+
+    def to_dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    if args.calib_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # Graph capture runs on a side stream; all timing happens on this one.
+    stream = torch.cuda.Stream()
+    torch.cuda.set_stream(stream)
+    timer = Timer(torch, stream)
+
+    # ---------------------------------------------------------------- decode
+    shapes = [(M, K, N) for M in synth.DECODE_M for (K, N) in synth.DECODE_KN]
+    dec = decode_section(args, torch, W, synth, to_dev, timer, dev) if "decode" in args.sections else None
     # ------------------------------------------------------------ prefill TOPS
     prefill = None
-    if not args.no_prefill:
+    if "prefill" in args.sections:
         prefill = {}
         for M in synth.PREFILL_M:
             for (K, N) in synth.DECODE_KN:
@@ -370,12 +392,15 @@ def main():
                                            "quant_GBs": round(quant_bytes(M, K, True) / (qus * 1e-6) / 1e9, 1)}
                 prefill[f"{M}x{K}x{N}"]["plain_int32"] = vendor_int32(torch, W, timer, xq, w, s_x, s_w, R)
                 del x, w, xq, out
+                progress(f"prefill {M}x{K}x{N} done")
         torch.cuda.synchronize()
 
-    extra = None if args.no_extra else extra_sections(torch, np, W, synth, to_dev, timer, dev)
-    if extra is not None:
-        extra["fp8_prefill"] = fp8_section(torch, W, synth, to_dev, timer, dev)
-        progress("fp8 section done")
+    extra = None
+    if args.sections & {"static", "moe", "fp8"}:
+        extra = extra_sections(torch, np, W, synth, to_dev, timer, dev, args.sections)
+        if "fp8" in args.sections:
+            extra["fp8_prefill"] = fp8_section(torch, W, synth, to_dev, timer, dev)
+            progress("fp8 section done")
 
     progress("prefill and extra sections done")
     # ------------------------------------------------------------- CPU oracle
@@ -383,14 +408,16 @@ def main():
     if not args.no_cpu:
         cpu = cpu_baseline(np, synth, shapes, args.cpu_seconds)
 
+    dec = dec or dict(value=None, ms_per_step=None, step_bytes=None, roofline=None, kernels=None,
+                      per_shape=None)
     line = {
         "metric": "INT8 scaled-GEMM TOPS (prefill) and GB/s (decode), % of MI355X roofline",
-        "value": round(value, 1),
+        "value": None if dec["value"] is None else round(dec["value"], 1),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": None if dec["ms_per_step"] is None else round(dec["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -399,12 +426,12 @@ def main():
         "config": {"workload": "decode: M in {1,8,32,64} x (K,N) in {(4096,6144),(4096,4096),"
                                "(4096,28672),(14336,4096)}; dynamic per-token symmetric quant + "
                                "scaled int8 GEMM with bf16 bias",
-                   "shapes": len(shapes), "step_bytes": step_bytes, "timing": "HIP graph replay",
+                   "shapes": len(shapes), "step_bytes": dec["step_bytes"], "timing": "HIP graph replay",
                    "parallelism": "single GPU"},
-        "roofline": roofline,
+        "roofline": dec["roofline"],
         "cpu_baseline": cpu,
-        "kernels": kernels,
-        "decode_shapes": per_shape,
+        "kernels": dec["kernels"],
+        "decode_shapes": dec["per_shape"],
         "prefill": prefill,
         "extra": extra,
     }
@@ -412,9 +439,18 @@ def main():
     return 0
 
 
-def extra_sections(torch, np, W, synth, to_dev, timer, dev):
+def extra_sections(torch, np, W, synth, to_dev, timer, dev, sections):
     """The static per-tensor scheme, the MoE grouped GEMM and the FP8 weight
     conversion, each timed as a graph of back-to-back launches."""
+    out = {}
+    if "static" in sections:
+        out.update(static_section(torch, np, W, synth, to_dev, timer, dev))
+    if "moe" in sections:
+        out.update(moe_section(torch, np, W, synth, to_dev, timer, dev))
+    return out
+
+
+def static_section(torch, np, W, synth, to_dev, timer, dev):
     out = {}
 
     # Static per-tensor scheme: fused QKV, M=512, K=4096, N=6144.
@@ -456,8 +492,14 @@ def extra_sections(torch, np, W, synth, to_dev, timer, dev):
         "hbm_frac": round(gb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "quant_us": round(qus, 2),
         "per_channel_scales": {"expand_us": round(eus, 2), "gemm_us": round(us_ch, 2)}}
     del x, w, w0, xq, o, one
+    progress("static fused QKV done")
+    return out
 
-    # MoE: FP8 -> int8 conversion of the expert weights, then the two grouped GEMMs.
+
+def moe_section(torch, np, W, synth, to_dev, timer, dev):
+    """MoE: FP8 -> int8 conversion of the expert weights, the two grouped
+    GEMMs, then the whole expert block."""
+    out = {}
     m = synth.moe()
     E, topk = synth.MOE_E, m["topk"]
     tokens = m["x13"].shape[0]
@@ -551,6 +593,7 @@ def fp8_section(torch, W, synth, to_dev, timer, dev):
                              "TFLOPS": round(tf, 1), "frac": round(tf / FP8_PEAK_TFLOPS, 4),
                              "quant_us": round(qus, 1)}
             res[f"{M}x{K}x{N}"] = row
+            progress(f"fp8 {M}x{K}x{N} done")
             del x, w8, out
     torch.cuda.synchronize()
     return res
