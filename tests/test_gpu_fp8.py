@@ -202,10 +202,10 @@ FP8_CASES = [
     (37, 128, 100, W.FP8_W_CHANNEL, "gemm_fp8_dma_kernel<128, 128, 10>"),
     (130, 208, 260, W.FP8_W_CHANNEL, "gemm_fp8_kernel<128, 128, false>"),
     (5, 16, 3, W.FP8_W_TENSOR, "gemm_fp8_kernel<128, 128, false>"),
-    (300, 1152, 520, W.FP8_W_BLOCK128, "gemm_fp8_block_dma_kernel<4>"),
-    (1, 128, 128, W.FP8_W_BLOCK128, "gemm_fp8_block_dma_kernel<4>"),
-    (129, 256, 129, W.FP8_W_BLOCK128, "gemm_fp8_block_dma_kernel<4>"),
-    (257, 4096, 384, W.FP8_W_BLOCK128, "gemm_fp8_block_dma_kernel<4>"),
+    (300, 1152, 520, W.FP8_W_BLOCK128, "gemm_fp8_block_dma_kernel<2>"),
+    (1, 128, 128, W.FP8_W_BLOCK128, "gemm_fp8_block_dma_kernel<2>"),
+    (129, 256, 129, W.FP8_W_BLOCK128, "gemm_fp8_block_dma_kernel<2>"),
+    (257, 4096, 384, W.FP8_W_BLOCK128, "gemm_fp8_block_dma_kernel<2>"),
     (130, 272, 260, W.FP8_W_BLOCK128, "gemm_fp8_kernel<128, 128, true>"),
     (7, 400, 130, W.FP8_W_BLOCK128, "gemm_fp8_kernel<128, 128, true>"),
 ]
