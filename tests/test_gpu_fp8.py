@@ -3,10 +3,10 @@
 * w8a8_quantize_act_fp8: E4M3 codes and scales bit-exact (per token, per
   tensor, per token in groups of 128).
 * w8a8_scaled_mm_fp8: every kernel variant (the ring kernel's four tiles, the
-  block-scaled ring kernel, the register-staged kernel with and without
-  128 x 128 block scales), against
-  the exact sums. The FP8 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4) does not
-  sum an instruction's 64 products exactly in binary32: it aligns them to the
+  block-scaled ring kernel with 128- and 256-row tiles, the register-staged
+  kernel with and without 128 x 128 block scales), against the exact sums.
+  The FP8 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4) does not sum an
+  instruction's 64 products exactly in binary32: it aligns them to the
   largest and truncates (measured with power-of-two operands, a product 2^14
   or more below the largest is dropped, toward zero); the accumulator input
   is added in binary32. Measured on random full-range E4M3 codes its loss is
@@ -202,10 +202,12 @@ FP8_CASES = [
     (37, 128, 100, W.FP8_W_CHANNEL, "gemm_fp8_dma_kernel<128, 128, 10>"),
     (130, 208, 260, W.FP8_W_CHANNEL, "gemm_fp8_kernel<128, 128, false>"),
     (5, 16, 3, W.FP8_W_TENSOR, "gemm_fp8_kernel<128, 128, false>"),
-    (300, 1152, 520, W.FP8_W_BLOCK128, "gemm_fp8_block_dma_kernel<2>"),
-    (1, 128, 128, W.FP8_W_BLOCK128, "gemm_fp8_block_dma_kernel<2>"),
-    (129, 256, 129, W.FP8_W_BLOCK128, "gemm_fp8_block_dma_kernel<2>"),
-    (257, 4096, 384, W.FP8_W_BLOCK128, "gemm_fp8_block_dma_kernel<2>"),
+    (300, 1152, 520, W.FP8_W_BLOCK128, "gemm_fp8_block_dma_kernel<2, 128>"),
+    (1, 128, 128, W.FP8_W_BLOCK128, "gemm_fp8_block_dma_kernel<2, 128>"),
+    (129, 256, 129, W.FP8_W_BLOCK128, "gemm_fp8_block_dma_kernel<2, 128>"),
+    (257, 4096, 384, W.FP8_W_BLOCK128, "gemm_fp8_block_dma_kernel<2, 128>"),
+    (2000, 384, 3100, W.FP8_W_BLOCK128, "gemm_fp8_block_dma_kernel<2, 256>"),
+    (1800, 256, 3968, W.FP8_W_BLOCK128, "gemm_fp8_block_dma_kernel<2, 256>"),
     (130, 272, 260, W.FP8_W_BLOCK128, "gemm_fp8_kernel<128, 128, true>"),
     (7, 400, 130, W.FP8_W_BLOCK128, "gemm_fp8_kernel<128, 128, true>"),
 ]
