@@ -39,10 +39,12 @@ brute force of every rounding decision on small rows, the half-step error
 bound, the argmax/argmin mapping, sign and power-of-two symmetries, the
 all-zero-row rule, a pure-Python integer GEMM, the dequantise-then-matmul
 identity, the OCP E4M3FN decoding against torch's float8_e4m3fn and hand
-values, hand-computed worked examples under ``tests/golden/``, and for the MoE
+values, hand-computed worked examples under ``tests/golden/``, for the MoE
 block: brute-force routing and sorting, closed forms and identities of the
 SiLU product and the combine, and the whole block against a float64
-dequantise-then-compute MoE layer.
+dequantise-then-compute MoE layer; for the RMS normalisation: torch's
+float64 rms_norm, closed forms, power-of-two symmetries and the residual add
+against exact rational sums.
 """
 
 from __future__ import annotations
@@ -80,6 +82,8 @@ __all__ = [
     "moe_topk",
     "moe_sort",
     "silu_mul_bf16",
+    "rmsnorm_bf16",
+    "rmsnorm_quant",
     "moe_combine",
     "moe_block",
     "linear_forward",
@@ -509,6 +513,37 @@ def silu_mul_bf16(h_bits, inter):
     with np.errstate(over="ignore"):
         a = g / (1.0 + np.exp(-g)) * u
     return f64_to_bf16_bits(a)
+
+
+def rmsnorm_bf16(x_bits, gamma_bits, eps, residual_bits=None):
+    """RMS normalisation of bf16 rows [M, K] with a bf16 weight gamma [K],
+    the op whose output the per-token quantiser takes in a decoder layer
+    (the quantiser runs right before the GEMM, [SGLang] 핵심 코드 분석 §3):
+        h = x                     (no residual), or
+        h = bf16(x + residual)    (the residual add, rounded once),
+        y = bf16(h * gamma / sqrt(mean_k(h**2) + eps)),
+    each value formed in float64 and rounded once to bf16. The float64 sum of
+    two bf16 values is exact while their exponents are within 44 of each
+    other; h**2 is exact, and the mean and the quotient carry float64
+    rounding only. Returns (h_bits, y_bits); h is the new residual."""
+    x = bf16_bits_to_f32(x_bits).astype(np.float64)
+    if residual_bits is not None:
+        h_bits = f64_to_bf16_bits(x + bf16_bits_to_f32(residual_bits).astype(np.float64))
+    else:
+        h_bits = np.asarray(x_bits, dtype=np.uint16).copy()
+    h = bf16_bits_to_f32(h_bits).astype(np.float64)
+    g = bf16_bits_to_f32(gamma_bits).astype(np.float64)
+    ms = np.mean(h * h, axis=1, keepdims=True) if h.shape[1] else np.zeros((h.shape[0], 1))
+    y = h / np.sqrt(ms + float(np.float32(eps))) * g[None, :]
+    return h_bits, f64_to_bf16_bits(y)
+
+
+def rmsnorm_quant(x_bits, gamma_bits, eps, residual_bits=None):
+    """RMS normalisation followed by dynamic per-token symmetric quantisation
+    of its bf16 output (quant_dyn_sym). Returns (h_bits, y_bits, q, s)."""
+    h_bits, y_bits = rmsnorm_bf16(x_bits, gamma_bits, eps, residual_bits)
+    q, s = quant_dyn_sym(y_bits)
+    return h_bits, y_bits, q, s
 
 
 def moe_combine(y_bits, pos, weights):
