@@ -44,7 +44,7 @@ INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA, TOPS
 FP8_PEAK_TFLOPS = 5000.0     # MI355X dense fp8 MFMA, TFLOP/s
 ROTATE_BYTES = 1 << 30       # weight bytes cycled between reuses of one copy, per shape
 GRAPH_STEPS = 16             # distinct step graphs (weight-rotation period)
-SECTIONS = ("decode", "prefill", "static", "moe", "fp8")
+SECTIONS = ("decode", "prefill", "static", "moe", "fp8", "rmsnorm")
 
 
 def gemm_bytes(M, K, N, bias=False, asym=False):
@@ -86,6 +86,11 @@ def quant_bytes(M, K, asym=False):
 
 def grouped_bytes(E, T, K, N, rows_read):
     return E * N * K + rows_read * K + 4 * T + 4 * E * N + 2 * T * N + 4 * (E + 1)
+
+
+def rmsnorm_quant_bytes(M, K, residual):
+    """x in, codes and scales out, gamma once; the residual read and written."""
+    return 3 * M * K + 4 * M + 2 * K + (4 * M * K if residual else 0)
 
 
 def fp8_convert_bytes(E, N, K):
@@ -396,11 +401,14 @@ def main():
         torch.cuda.synchronize()
 
     extra = None
-    if args.sections & {"static", "moe", "fp8"}:
+    if args.sections & {"static", "moe", "fp8", "rmsnorm"}:
         extra = extra_sections(torch, np, W, synth, to_dev, timer, dev, args.sections)
         if "fp8" in args.sections:
             extra["fp8_prefill"] = fp8_section(torch, W, synth, to_dev, timer, dev)
             progress("fp8 section done")
+        if "rmsnorm" in args.sections:
+            extra["rmsnorm_quant"] = rmsnorm_section(torch, W, synth, to_dev, timer, dev)
+            progress("rmsnorm section done")
 
     progress("prefill and extra sections done")
     # ------------------------------------------------------------- CPU oracle
@@ -595,6 +603,36 @@ def fp8_section(torch, W, synth, to_dev, timer, dev):
             res[f"{M}x{K}x{N}"] = row
             progress(f"fp8 {M}x{K}x{N} done")
             del x, w8, out
+    torch.cuda.synchronize()
+    return res
+
+
+def rmsnorm_section(torch, W, synth, to_dev, timer, dev):
+    """The quantiser fused into the RMS normalisation before it (with the
+    residual add) on the hidden rows (K = 4096) of the decode and prefill
+    batches; against the plain quantiser on the same rows (the launch the
+    fusion removes from a layer that normalises anyway) and the read + write
+    HBM roof."""
+    res = {}
+    R = 16
+    for M in synth.DECODE_M + synth.PREFILL_M:
+        for K in (4096,):
+            d = synth.decode(M, K, 16)
+            x = to_dev(d["x"])
+            g = torch.ones(K, dtype=torch.bfloat16, device=dev)
+            r = x.clone()
+            xq = torch.empty((M, K), dtype=torch.int8, device=dev)
+            sx = torch.empty(M, dtype=torch.float32, device=dev)
+            gf = capture(torch, lambda: [W.rmsnorm_quant(x, g, 1e-6, residual=r, xq=xq, s_x=sx) for _ in range(R)])
+            us = timer.graph_us(gf, R)
+            gq = capture(torch, lambda: [W.quantize_act(x, W.QUANT_DYN_SYM, xq=xq, s_x=sx) for _ in range(R)])
+            qus = timer.graph_us(gq, R)
+            del gf, gq
+            b = rmsnorm_quant_bytes(M, K, True)
+            res[f"{M}x{K}"] = {"us": round(us, 2), "GBs": round(b / (us * 1e-6) / 1e9, 1),
+                               "hbm_frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                               "quant_only_us": round(qus, 2)}
+            del x, r, xq
     torch.cuda.synchronize()
     return res
 

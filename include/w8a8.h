@@ -295,6 +295,25 @@ w8a8_status w8a8_linear_dyn_sym(const uint16_t* x, int64_t M, int64_t K, int64_t
                                 int64_t ldo, int8_t* xq, int64_t ldq, float* s_x, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
+/* The per-token quantiser fused into the op before it in a decoder layer
+ * (the quantiser runs right before the GEMM: "[SGLang] W4A8, W8A8, W4A4:
+ * 혼합 정밀도 양자화 스킴", 핵심 코드 분석 §3): RMS normalisation of bf16 rows,
+ * after an optional residual add, then W8A8_QUANT_DYN_SYM on its bf16 output:
+ *   h = residual ? bf16(x + residual) : x     (residual <- h, in place)
+ *   y = bf16(h * gamma / sqrt(mean_k(h^2) + eps))
+ *   s_x[t] = max|y_t| / 127,  xq = clamp(rne(y / s_x[t]), -127, 127)
+ * (each bf16 value the correctly rounded one; the mean square, root and
+ * products in binary64; the codes and the scale with the rule and exact
+ * rounding of w8a8_quantize_act). x, residual (nullable) and y (nullable:
+ * receives the normalised rows) bf16 [M, K] with strides ldx, ldr, ldy
+ * (multiples of 8); gamma bf16 [K]; xq int8 [M, K] (ldq % 16 == 0), s_x
+ * float [M]. K % 16 == 0; eps finite and > 0; x, residual, y, gamma and xq
+ * 16-byte aligned. residual and y may be x itself. */
+w8a8_status w8a8_rmsnorm_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                               const uint16_t* gamma, float eps, uint16_t* residual, int64_t ldr,
+                               uint16_t* y, int64_t ldy, int8_t* xq, int64_t ldq, float* s_x,
+                               void* stream);
+
 /* Grouped (MoE) scaled GEMM: the rows of the expert-sorted activation are
  * split by expert_offsets (device int32 [E+1], non-decreasing, [0] == 0,
  * [E] == T); rows [off[e], off[e+1]) take the symmetric scaled GEMM above

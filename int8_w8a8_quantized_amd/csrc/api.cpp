@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <cmath>
 #include <mutex>
 #include <string>
 
@@ -197,6 +198,28 @@ w8a8_status w8a8_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t l
   return hip_status(w8a8::launch_quantize_act(x, M, K, ldx, mode, s_in, zp_in, xq, ldq, s_x, zp,
                                               static_cast<hipStream_t>(stream)),
                     "quantize_act launch");
+}
+
+w8a8_status w8a8_rmsnorm_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint16_t* gamma,
+                               float eps, uint16_t* residual, int64_t ldr, uint16_t* y, int64_t ldy, int8_t* xq,
+                               int64_t ldq, float* s_x, void* stream) {
+  w8a8_status st;
+  if ((st = check_dim(M, "M")) != W8A8_OK) return st;
+  if ((st = check_k(K)) != W8A8_OK) return st;
+  W8A8_REQUIRE(std::isfinite(eps) && eps > 0.0f, "eps=%g must be finite and > 0", (double)eps);
+  if (M == 0) return ok();
+  W8A8_REQUIRE(x && gamma && xq && s_x, "x, gamma, xq and s_x must not be NULL");
+  W8A8_REQUIRE(aligned16(x) && aligned16(gamma) && aligned16(xq) && (residual == nullptr || aligned16(residual)) &&
+                   (y == nullptr || aligned16(y)),
+               "x, gamma, xq, residual and y must be 16-byte aligned");
+  W8A8_REQUIRE(ldx >= K && ldx % 8 == 0, "ldx=%lld must be >= K and a multiple of 8", (long long)ldx);
+  W8A8_REQUIRE(ldq >= K && ldq % 16 == 0, "ldq=%lld must be >= K and a multiple of 16", (long long)ldq);
+  if (residual) W8A8_REQUIRE(ldr >= K && ldr % 8 == 0, "ldr=%lld must be >= K and a multiple of 8", (long long)ldr);
+  if (y) W8A8_REQUIRE(ldy >= K && ldy % 8 == 0, "ldy=%lld must be >= K and a multiple of 8", (long long)ldy);
+  if ((st = check_current_device()) != W8A8_OK) return st;
+  return hip_status(w8a8::launch_rmsnorm_quant(x, M, K, ldx, gamma, eps, residual, ldr, y, ldy, xq, ldq, s_x,
+                                               static_cast<hipStream_t>(stream)),
+                    "rmsnorm_quant launch");
 }
 
 w8a8_status w8a8_prepare_colsum(const int8_t* W, int64_t N, int64_t K, int64_t ldw,

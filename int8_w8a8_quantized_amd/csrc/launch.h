@@ -79,6 +79,11 @@ const char* grouped_mm_kernel_name(int64_t K);
 
 // W8A8 FP8 (quant.hip, gemm.hip). mode: 0 per token, 1 per tensor (*s_in),
 // 2 per token in groups of 128 along K (scales group-major [G, M]).
+// RMS normalisation (after the optional residual add, residual updated in
+// place) fused with the per-token symmetric quantiser; y optional.
+hipError_t launch_rmsnorm_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint16_t* gamma,
+                                float eps, uint16_t* residual, int64_t ldr, uint16_t* y, int64_t ldy, int8_t* xq,
+                                int64_t ldq, float* s_x, hipStream_t stream);
 hipError_t launch_quantize_act_fp8(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int mode,
                                    const float* s_in, uint8_t* xq, int64_t ldq, float* s_x, hipStream_t stream);
 // a.A / a.B hold E4M3 codes; out_i32 means a binary32 output; no zero points.

@@ -292,6 +292,175 @@ hipError_t launch_quantize_act_fp8(const uint16_t* x, int64_t M, int64_t K, int6
   return hipGetLastError();
 }
 
+// ---------------------------------------------- RMS normalisation + codes
+// The quantiser fused into the op before it in a decoder layer: the RMS
+// normalisation of the bf16 rows (after the optional residual add) and the
+// per-token symmetric quantisation of its bf16 output, in one pass over the
+// row held in registers. Rounding, per element: h = bf16(x + residual) (the
+// binary32 sum of two bf16 values is exact, or off by less than the bf16
+// rounding's resolution, so rounding it once more to bf16 gives the correctly
+// rounded sum); y = bf16(h * gamma / sqrt(mean(h^2) + eps)) with the mean
+// square, its root and the products in binary64 (every h^2 and h * gamma is
+// exact there), so y is the correctly rounded value except within about
+// 2^-45 of a bf16 rounding boundary (a binary32 evaluation with a binary64
+// fallback near those boundaries measured slower: the fallback code doubled
+// the kernel and its registers); the codes and the scale are the quantiser's own
+// (codes8 on y). HBM traffic per element: 2 B in (+2 B residual in and out),
+// 1 B out (+2 B for y when it is asked for); gamma comes from the caches.
+
+// binary64 -> bf16, round to nearest even: rounding to binary32 toward zero
+// with a sticky bit for any inexactness (round to odd) keeps the second
+// rounding, binary32 -> bf16, correct.
+__device__ __forceinline__ uint32_t f64_to_bf16_bits(double d) {
+  const float f = (float)d;
+  const double back = (double)f;
+  uint32_t u = __float_as_uint(f);
+  if (back != d && d == d) {
+    if (fabs(back) > fabs(d)) u -= 1u;  // rounded away from zero: one binary32 step back toward it
+    u |= 1u;
+  }
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;  // NaN
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+template <int TPR>
+__device__ __forceinline__ double row_sum_f64(double v, double* red) {
+  constexpr int WPR = TPR / 64;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  if (WPR > 1) {
+    const int rb = (threadIdx.x / TPR), wv = (threadIdx.x % TPR) >> 6;
+    if ((threadIdx.x & 63) == 0) red[rb * WPR + wv] = v;
+    __syncthreads();
+    v = red[rb * WPR];
+#pragma unroll
+    for (int i = 1; i < WPR; ++i) v += red[rb * WPR + i];
+  }
+  return v;
+}
+
+template <int TPR, int CH>
+__global__ __launch_bounds__(TPR < 256 ? 256 : TPR) void rmsnorm_quant_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx, const uint16_t* __restrict__ gamma,
+    float eps, uint16_t* __restrict__ res, int64_t ldr, uint16_t* __restrict__ y, int64_t ldy,
+    int8_t* __restrict__ xq, int64_t ldq, float* __restrict__ s_x) {
+  constexpr int BLOCK = TPR < 256 ? 256 : TPR;
+  constexpr int RPB = BLOCK / TPR;  // rows per workgroup
+  constexpr int WPR = TPR / 64;     // waves per row
+  __shared__ double red_d[RPB * WPR];
+  __shared__ float red_f[RPB * WPR];
+  const int sub = threadIdx.x % TPR;
+  const int64_t t = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+  const bool row_ok = t < M;
+  if (WPR == 1 && !row_ok) return;  // nothing below synchronises in that case
+  const int64_t nchunk = K >> 3;
+  const int64_t tr = row_ok ? t : 0;
+  // every load goes out first (x, the residual, gamma): one round trip
+  uint4 v[CH], rv[CH], gv[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int64_t j = (int64_t)c * TPR + sub;
+    const bool in = row_ok && j < nchunk;
+    v[c] = in ? ld16(x + tr * ldx + j * 8) : make_uint4(0, 0, 0, 0);
+    rv[c] = (in && res != nullptr) ? ld16(res + tr * ldr + j * 8) : make_uint4(0, 0, 0, 0);
+    gv[c] = j < nchunk ? ld16(gamma + j * 8) : make_uint4(0, 0, 0, 0);
+  }
+  if (res != nullptr) {  // h = bf16(x + residual), which becomes the residual
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int64_t j = (int64_t)c * TPR + sub;
+      if (!(row_ok && j < nchunk)) continue;
+      const uint4 r = rv[c];
+      const uint32_t a[4] = {v[c].x, v[c].y, v[c].z, v[c].w}, b[4] = {r.x, r.y, r.z, r.w};
+      uint32_t h[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        h[i] = pack_bf16x2(bf16_lo(a[i]) + bf16_lo(b[i]), bf16_hi(a[i]) + bf16_hi(b[i]));
+      v[c] = make_uint4(h[0], h[1], h[2], h[3]);
+      st16(res + tr * ldr + j * 8, v[c]);
+    }
+  }
+  // mean square in binary64
+  double ss = 0.0;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const uint32_t w[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const double lo = (double)bf16_lo(w[i]), hi = (double)bf16_hi(w[i]);
+      ss = __builtin_fma(lo, lo, ss);
+      ss = __builtin_fma(hi, hi, ss);
+    }
+  }
+  ss = row_sum_f64<TPR>(ss, red_d);
+  const double inv = 1.0 / __builtin_sqrt(ss / (double)K + (double)eps);
+  // y = bf16(h * gamma * inv) in binary64 and its absmax
+  auto norm = [&](float hv, float gvv) __attribute__((always_inline)) -> uint32_t {
+    return f64_to_bf16_bits((double)hv * (double)gvv * inv);
+  };
+  float am = 0.0f;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const uint32_t w[4] = {v[c].x, v[c].y, v[c].z, v[c].w}, g[4] = {gv[c].x, gv[c].y, gv[c].z, gv[c].w};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      o[i] = norm(bf16_lo(w[i]), bf16_lo(g[i])) | (norm(bf16_hi(w[i]), bf16_hi(g[i])) << 16);
+    v[c] = make_uint4(o[0], o[1], o[2], o[3]);
+    absmax8(v[c], am);
+  }
+  am = wave_extreme<true>(am);
+  if (WPR > 1) {
+    const int rb = threadIdx.x / TPR, wv = sub >> 6;
+    if ((threadIdx.x & 63) == 0) red_f[rb * WPR + wv] = am;
+    __syncthreads();
+    am = red_f[rb * WPR];
+#pragma unroll
+    for (int i = 1; i < WPR; ++i) am = max_ieee(am, red_f[rb * WPR + i]);
+  }
+  if (!row_ok) return;
+  const RowParams p = row_params<kDynSym>(0.0f, am, nullptr, nullptr);
+  if (sub == 0) s_x[t] = p.s;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int64_t j = (int64_t)c * TPR + sub;
+    if (j >= nchunk) continue;
+    *reinterpret_cast<uint2*>(xq + t * ldq + j * 8) = codes8<kDynSym>(v[c], p);
+    if (y != nullptr) st16(y + t * ldy + j * 8, v[c]);
+  }
+}
+
+hipError_t launch_rmsnorm_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint16_t* gamma,
+                                float eps, uint16_t* residual, int64_t ldr, uint16_t* y, int64_t ldy, int8_t* xq,
+                                int64_t ldq, float* s_x, hipStream_t stream) {
+  // the quantiser's threads-per-row table (wide rows for small batches)
+  const int64_t nchunk = K / 8;
+  int tpr;
+  if (M <= 256)
+    tpr = nchunk <= 64 ? 64 : (nchunk <= 256 ? 256 : (nchunk <= 512 ? 512 : 1024));
+  else
+    tpr = nchunk <= 128 ? 64 : (nchunk <= 2048 ? 256 : 1024);
+  const int ch = (int)((nchunk + tpr - 1) / tpr);  // <= 8 since K <= 65536
+#define W8A8_RN(TPRV, CHV)                                                                                   \
+  hipLaunchKernelGGL((rmsnorm_quant_kernel<TPRV, CHV>), dim3((unsigned)(TPRV < 256 ? (M + 3) / 4 : M)),       \
+                     dim3(TPRV < 256 ? 256 : TPRV), 0, stream, x, M, K, ldx, gamma, eps, residual, ldr, y, ldy, \
+                     xq, ldq, s_x)
+#define W8A8_RN_CH(TPRV)                          \
+  do {                                            \
+    if (ch <= 1) W8A8_RN(TPRV, 1);                \
+    else if (ch <= 2) W8A8_RN(TPRV, 2);           \
+    else if (ch <= 4) W8A8_RN(TPRV, 4);           \
+    else W8A8_RN(TPRV, 8);                        \
+  } while (0)
+  if (tpr == 64) W8A8_RN_CH(64);
+  else if (tpr == 256) W8A8_RN_CH(256);
+  else if (tpr == 512) W8A8_RN_CH(512);
+  else W8A8_RN_CH(1024);
+#undef W8A8_RN_CH
+#undef W8A8_RN
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int mode,
                                const float* s_in, const int32_t* zp_in, int8_t* xq, int64_t ldq,
                                float* s_x, int32_t* zp, hipStream_t stream) {

@@ -69,6 +69,8 @@ _SIGS = {
     "w8a8_moe_route_workspace_size": (ctypes.c_size_t, [_i64, _i64]),
     "w8a8_moe_route": (_i32, [_p, _i64, _i64, _i64, _i32, _p, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]),
     "w8a8_silu_mul_quant": (_i32, [_p, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p]),
+    "w8a8_rmsnorm_quant": (_i32, [_p, _i64, _i64, _i64, _p, ctypes.c_float, _p, _i64, _p, _i64, _p, _i64, _p,
+                                  _p]),
     "w8a8_moe_combine": (_i32, [_p, _i64, _p, _p, _i64, _i32, _i64, _p, _i64, _p]),
     "w8a8_moe_block_workspace_size": (ctypes.c_size_t, [_i64, _i64, _i32, _i64, _i64]),
     "w8a8_moe_block_int8": (_i32, [_p, _i64, _p, _i64, _i64, _i64, _i32, _i64, _i64, _p, _p, _p, _p,
@@ -403,6 +405,27 @@ def silu_mul_quant(h, inter: int, aq=None, s_a=None, act=None, want_act=False):
                                     act.stride(0) if act is not None and T else inter, _stream())
     _raise(st, "w8a8_silu_mul_quant")
     return aq, s_a, act
+
+
+def rmsnorm_quant(x, gamma, eps: float, residual=None, xq=None, s_x=None, y=None, want_y=False):
+    """x bf16 [M, K], gamma bf16 [K]; residual (bf16 [M, K], updated in place
+    to x + residual) optional. Returns (xq int8 [M, K], s_x float [M], y bf16
+    [M, K] or None)."""
+    import torch
+    M, K = x.shape
+    dev = x.device
+    if xq is None:
+        xq = torch.empty((M, K), dtype=torch.int8, device=dev)
+    if s_x is None:
+        s_x = torch.empty(M, dtype=torch.float32, device=dev)
+    if y is None and want_y:
+        y = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    st = load().w8a8_rmsnorm_quant(_ptr(x), M, K, x.stride(0) if M else K, _ptr(gamma), eps, _ptr(residual),
+                                   residual.stride(0) if residual is not None and M else K, _ptr(y),
+                                   y.stride(0) if y is not None and M else K, _ptr(xq), xq.stride(0) if M else K,
+                                   _ptr(s_x), _stream())
+    _raise(st, "w8a8_rmsnorm_quant")
+    return xq, s_x, y
 
 
 def moe_combine(y, pos, topk_w, out=None):

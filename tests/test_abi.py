@@ -16,7 +16,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = W.header_functions()
-    assert len(names) == 25, names
+    assert len(names) == 26, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -231,6 +231,22 @@ def test_moe_calls_reject_before_device_work(L):
     assert smq(h=FAKE + 8) == W.ERR_INVALID_ARG
     assert smq(act=FAKE, ld_act=60) == W.ERR_INVALID_ARG
     assert smq(T=0) == W.OK
+
+    def rnq(M=4, K=64, ldx=64, eps=1e-6, res=None, ldr=0, y=None, ldy=0, ldq=64, x=FAKE, g=FAKE):
+        return L.w8a8_rmsnorm_quant(x, M, K, ldx, g, eps, res, ldr, y, ldy, FAKE, ldq, FAKE, None)
+    assert rnq(K=40, ldx=40, ldq=48) == W.ERR_INVALID_ARG
+    assert rnq(eps=0.0) == W.ERR_INVALID_ARG
+    assert rnq(eps=-1e-6) == W.ERR_INVALID_ARG
+    assert rnq(eps=float("inf")) == W.ERR_INVALID_ARG
+    assert rnq(eps=float("nan")) == W.ERR_INVALID_ARG
+    assert rnq(ldx=60) == W.ERR_INVALID_ARG
+    assert rnq(ldq=72) == W.ERR_INVALID_ARG
+    assert rnq(res=FAKE, ldr=56) == W.ERR_INVALID_ARG
+    assert rnq(y=FAKE, ldy=60) == W.ERR_INVALID_ARG
+    assert rnq(x=FAKE + 8) == W.ERR_INVALID_ARG
+    assert rnq(g=None) == W.ERR_INVALID_ARG
+    assert rnq(res=FAKE + 2, ldr=64) == W.ERR_INVALID_ARG
+    assert rnq(M=0) == W.OK
 
     def comb(tokens=4, k=8, N=64, ldy=64, ldo=64, y=FAKE):
         return L.w8a8_moe_combine(y, ldy, FAKE, FAKE, tokens, k, N, FAKE, ldo, None)
