@@ -40,6 +40,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+HBM_STREAM_GBS = 6450.0      # what a plain streaming read of HBM reaches on this GPU (measured)
+NODE_US = 1.6                # a kernel node of a HIP graph, empty (measured)
 INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA, TOPS
 FP8_PEAK_TFLOPS = 5000.0     # MI355X dense fp8 MFMA, TFLOP/s
 ROTATE_BYTES = 1 << 30       # weight bytes cycled between reuses of one copy, per shape
@@ -86,6 +88,14 @@ def quant_bytes(M, K, asym=False):
 
 def grouped_bytes(E, T, K, N, rows_read):
     return E * N * K + rows_read * K + 4 * T + 4 * E * N + 2 * T * N + 4 * (E + 1)
+
+
+def launch_floor_us(nbytes):
+    """The time no launch of a kernel moving nbytes can beat here: an empty
+    graph node plus the bytes at the plain streaming-read rate. floor_frac =
+    this / the measured time (1.0 = at the floor), beside hbm_frac against
+    the 8 TB/s peak."""
+    return NODE_US + nbytes / (HBM_STREAM_GBS * 1e3)
 
 
 def rmsnorm_quant_bytes(M, K, residual):
@@ -291,7 +301,9 @@ def decode_section(args, torch, W, synth, to_dev, timer, dev):
             kname = W.linear_dyn_sym_kernel_name(M, N, K)
             b = gemm_bytes(M, K, N, bias=True) + quant_bytes(M, K)
             per_shape[f"{M}x{K}x{N}"] = {"kernel": kname, "fused_us": round(us, 3),
-                                         "GBs": round(b / (us * 1e-6) / 1e9, 1)}
+                                         "GBs": round(b / (us * 1e-6) / 1e9, 1),
+                                         "hbm_frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                                         "floor_frac": round(launch_floor_us(b) / us, 4)}
         else:
             g = capture(torch, lambda: [gemm(shape, c) for c in range(R)])
             us = timer.graph_us(g, R)
@@ -302,6 +314,8 @@ def decode_section(args, torch, W, synth, to_dev, timer, dev):
             b = gemm_bytes(M, K, N, bias=True)
             per_shape[f"{M}x{K}x{N}"] = {"kernel": kname, "gemm_us": round(us, 3),
                                          "GBs": round(b / (us * 1e-6) / 1e9, 1),
+                                         "hbm_frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                                         "floor_frac": round(launch_floor_us(b) / us, 4),
                                          "quant_us": round(qus, 3)}
             qname = "quant_kernel (dynamic symmetric)"
             agg = per_kernel.setdefault(qname, dict(launches=0, us=0.0, bytes=0))
