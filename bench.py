@@ -207,6 +207,14 @@ def progress(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def fresh_cache(torch):
+    """Each section starts from an empty allocator cache: the decode
+    section's 4 GiB of weight copies, once freed, otherwise stay cached, and
+    the prefill GEMMs measured 10-20% slower on tensors carved out of them."""
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
 def capture(torch, fn):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
@@ -382,6 +390,7 @@ def main():
     # ---------------------------------------------------------------- decode
     shapes = [(M, K, N) for M in synth.DECODE_M for (K, N) in synth.DECODE_KN]
     dec = decode_section(args, torch, W, synth, to_dev, timer, dev) if "decode" in args.sections else None
+    fresh_cache(torch)
     # ------------------------------------------------------------ prefill TOPS
     prefill = None
     if "prefill" in args.sections:
@@ -416,11 +425,14 @@ def main():
 
     extra = None
     if args.sections & {"static", "moe", "fp8", "rmsnorm"}:
+        fresh_cache(torch)
         extra = extra_sections(torch, np, W, synth, to_dev, timer, dev, args.sections)
         if "fp8" in args.sections:
+            fresh_cache(torch)
             extra["fp8_prefill"] = fp8_section(torch, W, synth, to_dev, timer, dev)
             progress("fp8 section done")
         if "rmsnorm" in args.sections:
+            fresh_cache(torch)
             extra["rmsnorm_quant"] = rmsnorm_section(torch, W, synth, to_dev, timer, dev)
             progress("rmsnorm section done")
 
@@ -468,6 +480,7 @@ def extra_sections(torch, np, W, synth, to_dev, timer, dev, sections):
     if "static" in sections:
         out.update(static_section(torch, np, W, synth, to_dev, timer, dev))
     if "moe" in sections:
+        fresh_cache(torch)
         out.update(moe_section(torch, np, W, synth, to_dev, timer, dev))
     return out
 
