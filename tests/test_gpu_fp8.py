@@ -208,6 +208,7 @@ FP8_CASES = [
     (257, 4096, 384, W.FP8_W_BLOCK128, "gemm_fp8_block_dma_kernel<2, 128>"),
     (2000, 384, 3100, W.FP8_W_BLOCK128, "gemm_fp8_block_dma_kernel<2, 256>"),
     (1800, 256, 3968, W.FP8_W_BLOCK128, "gemm_fp8_block_dma_kernel<2, 256>"),
+    (300, 128, 16384, W.FP8_W_BLOCK128, "gemm_fp8_block_dma_kernel<2, 256>"),
     (130, 272, 260, W.FP8_W_BLOCK128, "gemm_fp8_kernel<128, 128, true>"),
     (7, 400, 130, W.FP8_W_BLOCK128, "gemm_fp8_kernel<128, 128, true>"),
 ]
