@@ -308,7 +308,8 @@ w8a8_status w8a8_linear_dyn_sym(const uint16_t* x, int64_t M, int64_t K, int64_t
  * receives the normalised rows) bf16 [M, K] with strides ldx, ldr, ldy
  * (multiples of 8); gamma bf16 [K]; xq int8 [M, K] (ldq % 16 == 0), s_x
  * float [M]. K % 16 == 0; eps finite and > 0; x, residual, y, gamma and xq
- * 16-byte aligned. residual and y may be x itself. */
+ * 16-byte aligned. residual and y may be x itself, but not each other
+ * (W8A8_ERR_INVALID_ARG). */
 w8a8_status w8a8_rmsnorm_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                                const uint16_t* gamma, float eps, uint16_t* residual, int64_t ldr,
                                uint16_t* y, int64_t ldy, int8_t* xq, int64_t ldq, float* s_x,

@@ -216,6 +216,7 @@ w8a8_status w8a8_rmsnorm_quant(const uint16_t* x, int64_t M, int64_t K, int64_t 
   W8A8_REQUIRE(ldq >= K && ldq % 16 == 0, "ldq=%lld must be >= K and a multiple of 16", (long long)ldq);
   if (residual) W8A8_REQUIRE(ldr >= K && ldr % 8 == 0, "ldr=%lld must be >= K and a multiple of 8", (long long)ldr);
   if (y) W8A8_REQUIRE(ldy >= K && ldy % 8 == 0, "ldy=%lld must be >= K and a multiple of 8", (long long)ldy);
+  W8A8_REQUIRE(y == nullptr || y != residual, "y and residual must be different buffers (y may be x)");
   if ((st = check_current_device()) != W8A8_OK) return st;
   return hip_status(w8a8::launch_rmsnorm_quant(x, M, K, ldx, gamma, eps, residual, ldr, y, ldy, xq, ldq, s_x,
                                                static_cast<hipStream_t>(stream)),

@@ -296,10 +296,10 @@ hipError_t launch_quantize_act_fp8(const uint16_t* x, int64_t M, int64_t K, int6
 // The quantiser fused into the op before it in a decoder layer: the RMS
 // normalisation of the bf16 rows (after the optional residual add) and the
 // per-token symmetric quantisation of its bf16 output, in one pass over the
-// row held in registers. Rounding, per element: h = bf16(x + residual) (the
-// binary32 sum of two bf16 values is exact, or off by less than the bf16
-// rounding's resolution, so rounding it once more to bf16 gives the correctly
-// rounded sum); y = bf16(h * gamma / sqrt(mean(h^2) + eps)) with the mean
+// row held in registers. Rounding, per element: h = bf16(x + residual)
+// (binary32 carries more than twice bf16's 8 significant bits, so rounding
+// the binary32 sum of two bf16 values to bf16 gives the correctly rounded
+// sum: a double rounding through that width is innocuous); y = bf16(h * gamma / sqrt(mean(h^2) + eps)) with the mean
 // square, its root and the products in binary64 (every h^2 and h * gamma is
 // exact there), so y is the correctly rounded value except within about
 // 2^-45 of a bf16 rounding boundary (a binary32 evaluation with a binary64
@@ -341,9 +341,12 @@ __device__ __forceinline__ double row_sum_f64(double v, double* red) {
 
 template <int TPR, int CH>
 __global__ __launch_bounds__(TPR < 256 ? 256 : TPR) void rmsnorm_quant_kernel(
-    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx, const uint16_t* __restrict__ gamma,
-    float eps, uint16_t* __restrict__ res, int64_t ldr, uint16_t* __restrict__ y, int64_t ldy,
-    int8_t* __restrict__ xq, int64_t ldq, float* __restrict__ s_x) {
+    const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint16_t* __restrict__ gamma, float eps,
+    uint16_t* res, int64_t ldr, uint16_t* y, int64_t ldy, int8_t* __restrict__ xq, int64_t ldq,
+    float* __restrict__ s_x) {
+  // x, res and y may be one buffer (the residual and the normalised rows may
+  // overwrite x): each element is read and written by the same thread, all
+  // reads first, so no qualifier promises them apart
   constexpr int BLOCK = TPR < 256 ? 256 : TPR;
   constexpr int RPB = BLOCK / TPR;  // rows per workgroup
   constexpr int WPR = TPR / 64;     // waves per row

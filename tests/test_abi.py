@@ -246,6 +246,7 @@ def test_moe_calls_reject_before_device_work(L):
     assert rnq(x=FAKE + 8) == W.ERR_INVALID_ARG
     assert rnq(g=None) == W.ERR_INVALID_ARG
     assert rnq(res=FAKE + 2, ldr=64) == W.ERR_INVALID_ARG
+    assert rnq(res=FAKE + 4096, ldr=64, y=FAKE + 4096, ldy=64) == W.ERR_INVALID_ARG  # y is the residual
     assert rnq(M=0) == W.OK
 
     def comb(tokens=4, k=8, N=64, ldy=64, ldo=64, y=FAKE):
