@@ -16,7 +16,10 @@ Python loops:
   test_oracle_quant;
 * int_gemm / colsum / corrected_acc: integer sums by Python loops;
 * moe_topk / moe_sort: the ranking and the (expert, token) order by sorting
-  Python tuples (ties broken by the lower expert index).
+  Python tuples (ties broken by the lower expert index);
+* e4m3fn_encode: the nearest OCP E4M3FN value of any binary32 in [-448, 448]
+  by exhaustive search over the codes decoded from their bit fields here,
+  ties to the even code, the sign kept.
 """
 
 from fractions import Fraction
@@ -153,3 +156,28 @@ def test_moe_topk_and_sort_by_tuples(tokens, E, data):
     for t in range(tokens):
         for j in range(k):
             assert pairs[int(pos[t, j])] == (int(ids[t, j]), t)
+
+
+def _e4m3_value(code):
+    """Exact value of a finite E4M3FN code from its fields: sign, 4-bit
+    exponent (bias 7, field 0 subnormal), 3-bit mantissa."""
+    e, m = (code >> 3) & 0xF, code & 7
+    mag = Fraction(m, 8) * Fraction(2) ** -6 if e == 0 else (1 + Fraction(m, 8)) * Fraction(2) ** (e - 7)
+    return -mag if code & 0x80 else mag
+
+
+_E4M3_MAGS = [(_e4m3_value(c), c) for c in range(127)]  # codes 0x00 .. 0x7E (0x7F is NaN)
+
+
+@SETTINGS
+@given(st.floats(min_value=-448.0, max_value=448.0, width=32, allow_nan=False))
+def test_e4m3_encode_is_nearest_even(v):
+    code = int(O.e4m3fn_encode(np.array([v], np.float32))[0])
+    a = abs(Fraction(v))
+    best = min(abs(a - m) for m, _ in _E4M3_MAGS)
+    near = [c for m, c in _E4M3_MAGS if abs(a - m) == best]
+    want = near[0] if len(near) == 1 else next(c for c in near if c % 2 == 0)
+    if np.signbit(np.float32(v)):
+        want |= 0x80
+    assert code == want
+    assert abs(_e4m3_value(code)) == abs(_e4m3_value(want))
