@@ -91,6 +91,25 @@ def test_strided_output():
     _run(d, W.AZP_NONE, ldo=264, out_dtype=W.OUT_I32)
 
 
+@pytest.mark.parametrize("M,K,N,ldo", [(300, 256, 520, 600), (2100, 384, 2100, 2164), (2300, 640, 6100, 6144)])
+def test_strided_output_tiles(M, K, N, ldo):
+    """The MFMA tile path writing into a wider output (row stride ldo > N):
+    every 128 x 128, 256 x 128 and 256 x 256 store form, columns past N
+    left alone."""
+    assert W.scaled_mm_kernel_name(M, N, K).startswith("gemm_i8_dma_kernel")
+    d = _inputs(M, K, N, seed=ldo)
+    _run(d, W.AZP_PER_TOKEN, ldo=ldo, out_dtype=W.OUT_I32)
+    _run(d, W.AZP_NONE, ldo=ldo, bias=True)
+    full = torch.full((M, ldo), -7, dtype=torch.int32, device="cuda:0")
+    note(f"strided tile output padding M={M} K={K} N={N} ldo={ldo}")
+    W.scaled_mm_int8(to_dev(d["xq"]), to_dev(d["w"]), to_dev(d["sx"]), to_dev(d["sw"]), out_dtype=W.OUT_I32,
+                     out=full[:, :N])
+    torch.cuda.synchronize()
+    f = host(full)
+    assert np.all(f[:, N:] == -7), "columns past N were written"
+    assert_equal(f[:, :N], O.int_gemm(d["xq"], d["w"]).astype(np.int32), "strided int32")
+
+
 def test_extreme_values_exact():
     """All -128 against all -128 over K = 14336: the largest sums, still exact."""
     M, K, N = 70, 14336, 40
