@@ -10,6 +10,9 @@ fixed by its seed (the same cases on every run).
   bit-exact.
 * w8a8_grouped_scaled_mm_int8: random expert counts (empty experts
   included), sorted or gathered rows; int32 bit-exact.
+* w8a8_quantize_act_fp8 (every mode), w8a8_linear_dyn_sym (fused and
+  two-launch shapes) and w8a8_rmsnorm_quant (with and without a residual),
+  each to the bar of its own test file.
 """
 
 import numpy as np
@@ -17,7 +20,7 @@ import pytest
 import torch
 
 import oracle as O
-from gpu_util import assert_equal, host, note, to_dev
+from gpu_util import assert_bf16_close, assert_equal, bf16_bits, bf16_f64, host, note, to_dev
 from int8_w8a8_quantized_amd import lib as W
 from int8_w8a8_quantized_amd import synth
 from test_gpu_gemm import _run
@@ -104,3 +107,76 @@ def test_grouped_random(seed):
         if off[e + 1] > off[e]:
             want[off[e]:off[e + 1]] = O.int_gemm(rows[off[e]:off[e + 1]], w[e])
     assert_equal(host(out), want.astype(np.int32), "grouped int32")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_quantize_act_fp8_random(seed):
+    rng = np.random.default_rng(4000 + seed)
+    M = int(rng.integers(1, 400))
+    K = int(rng.integers(1, 100)) * 16
+    mode = int(rng.integers(0, 3))
+    x = rng.standard_normal((M, K)).astype(np.float32) * np.float32(rng.uniform(0.01, 50.0))
+    xb = synth.f32_to_bf16_bits(x)
+    s_in = np.float32(np.abs(x).max() / 300.0 + 1e-6) if mode == W.FP8_ACT_TENSOR else None
+    note(f"random quantize_act_fp8 seed={seed} M={M} K={K} mode={mode}")
+    sd = None if s_in is None else torch.tensor([s_in], dtype=torch.float32, device="cuda:0")
+    q, s = W.quantize_act_fp8(to_dev(xb), mode, s_in=sd)
+    torch.cuda.synchronize()
+    rq, rs = O.quant_fp8(xb, mode, s_in=s_in)
+    assert_equal(host(q), rq, "E4M3 codes")
+    if rs is not None:
+        assert_equal(host(s).view(np.uint32), np.asarray(rs, np.float32).view(np.uint32), "scales")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_linear_dyn_sym_random(seed):
+    """Quantiser + GEMM in one call (one fused kernel on the smallest shapes):
+    codes and scales bit-exact, the output within the bar."""
+    rng = np.random.default_rng(5000 + seed)
+    M = int(rng.choice([rng.integers(1, 3), rng.integers(3, 129)]))
+    K = int(rng.integers(1, 80)) * 128 if rng.random() < 0.7 else int(rng.integers(1, 300)) * 16
+    N = int(rng.integers(1, 5000))
+    x = synth.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32) * np.float32(2.0))
+    w = rng.integers(-127, 128, (N, K), dtype=np.int8)
+    sw = rng.uniform(1e-3, 1e-2, N).astype(np.float32)
+    bias = synth.bias_bits(rng, N)
+    note(f"random linear_dyn_sym seed={seed} M={M} K={K} N={N} kernel={W.linear_dyn_sym_kernel_name(M, N, K)}")
+    out, xq, sx = W.linear_dyn_sym(to_dev(x), to_dev(w), to_dev(sw), bias=to_dev(bias))
+    torch.cuda.synchronize()
+    rq, rs = O.quant_dyn_sym(x)
+    assert_equal(host(xq), rq, "codes")
+    assert_equal(host(sx).view(np.uint32), rs.view(np.uint32), "scales")
+    want, _ = O.scaled_mm(rq, w, rs, sw, bias_bits=bias)
+    assert_bf16_close(bf16_bits(out), want)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_rmsnorm_quant_random(seed):
+    """The residual sum bit-exact; codes and scales bit-exact against the
+    quantiser applied to the device's own normalised rows, which must equal
+    the oracle's wherever no value sits within 2^-40 of a bf16 midpoint."""
+    rng = np.random.default_rng(6000 + seed)
+    M = int(rng.integers(1, 300))
+    K = int(rng.integers(1, 400)) * 16
+    x = synth.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32) * np.float32(rng.uniform(0.1, 10)))
+    g = synth.f32_to_bf16_bits(rng.uniform(0.2, 2.0, K).astype(np.float32))
+    r = synth.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32)) if rng.random() < 0.5 else None
+    eps = float(rng.choice([1e-6, 1e-5]))
+    note(f"random rmsnorm_quant seed={seed} M={M} K={K} residual={r is not None}")
+    rd = None if r is None else to_dev(r)
+    xq, sx, y = W.rmsnorm_quant(to_dev(x), to_dev(g), eps, residual=rd, want_y=True)
+    torch.cuda.synchronize()
+    h_ref, y_ref = O.rmsnorm_bf16(x, g, eps, residual_bits=r)
+    if r is not None:
+        assert_equal(bf16_bits(rd), h_ref, "residual sum")
+    y_dev = bf16_bits(y)
+    diff = y_dev != y_ref
+    if diff.any():  # only the midpoint ambiguity of the binary64 evaluation is allowed
+        h = O.bf16_bits_to_f32(h_ref).astype(np.float64)
+        gg = O.bf16_bits_to_f32(g).astype(np.float64)
+        exact = (h / np.sqrt(np.mean(h * h, axis=1, keepdims=True) + float(np.float32(eps))) * gg[None, :])[diff]
+        mid = (bf16_f64(y_dev[diff]) + bf16_f64(y_ref[diff])) / 2
+        assert np.all(np.abs(exact - mid) <= 2.0 ** -40 * np.abs(exact)), "normalised rows differ"
+    q_ref, s_ref = O.quant_dyn_sym(y_dev)
+    assert_equal(host(xq), q_ref, "codes")
+    assert_equal(host(sx).view(np.uint32), s_ref.view(np.uint32), "scales")
