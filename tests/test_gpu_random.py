@@ -10,6 +10,8 @@ fixed by its seed (the same cases on every run).
   bit-exact.
 * w8a8_grouped_scaled_mm_int8: random expert counts (empty experts
   included), sorted or gathered rows; int32 bit-exact.
+* w8a8_scaled_mm_fp8 (every weight-scale layout, ring and register-staged
+  kernels) to the bounds of test_gpu_fp8;
 * w8a8_quantize_act_fp8 (every mode), w8a8_linear_dyn_sym (fused and
   two-launch shapes) and w8a8_rmsnorm_quant (with and without a residual),
   each to the bar of its own test file.
@@ -180,3 +182,17 @@ def test_rmsnorm_quant_random(seed):
     q_ref, s_ref = O.quant_dyn_sym(y_dev)
     assert_equal(host(xq), q_ref, "codes")
     assert_equal(host(sx).view(np.uint32), s_ref.view(np.uint32), "scales")
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_scaled_mm_fp8_random(seed):
+    """The W8A8 FP8 GEMM on random shapes and scale layouts, to the bounds of
+    test_gpu_fp8 (integer-valued codes: the scale steps' roundings only; full
+    range: plus the measured summation loss)."""
+    from test_gpu_fp8 import _fp8_case, _run_fp8
+    rng = np.random.default_rng(7000 + seed)
+    M = int(rng.integers(1, 600))
+    K = int(rng.integers(1, 30)) * (128 if rng.random() < 0.7 else 16)
+    N = int(rng.integers(1, 1200))
+    w_mode = int(rng.integers(0, 3))
+    _run_fp8(_fp8_case(M, K, N, w_mode, seed, narrow=bool(seed % 2)))
