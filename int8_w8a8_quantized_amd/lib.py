@@ -241,13 +241,16 @@ def _workspace(device, stream: int, nbytes: int):
     """A workspace of at least nbytes kept per (device, stream); the library
     keeps no state in it, so calls ordered on one stream can share it. A
     buffer that a larger request replaces is kept alive (never freed), since
-    a HIP graph captured with it may still write there on replay."""
+    a HIP graph captured with it may still write there on replay; a
+    replacement is at least twice the size it replaces, so the buffers kept
+    alive add up to less than the largest one."""
     import torch
     key = (device.index, stream)
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:
         if ws is not None:
             _ws_retired.append(ws)
+            nbytes = max(nbytes, 2 * ws.numel())
         ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
         _ws_cache[key] = ws
     return ws

@@ -192,6 +192,26 @@ def test_noalloc_scratch_covers_every_workspace():
     assert 0 < worst <= W.NOALLOC_SCRATCH_BYTES
 
 
+def test_workspace_cache_keeps_replaced_buffers():
+    """The binding's per-stream workspace (host tensors stand in for device
+    ones): a request it covers reuses the buffer; a larger one replaces it
+    with one at least twice as large and keeps the old one alive, since a
+    captured graph may still use its address."""
+    import torch
+    dev, stream = torch.device("cpu"), 0x5EED
+    W._ws_cache.pop((dev.index, stream), None)
+    kept = len(W._ws_retired)
+    a = W._workspace(dev, stream, 1000)
+    assert a.numel() == 1000 and W._workspace(dev, stream, 600) is a
+    b = W._workspace(dev, stream, 1200)
+    assert b.numel() == 2000 and W._ws_retired[-1] is a
+    c = W._workspace(dev, stream, 9000)
+    assert c.numel() == 9000 and W._ws_retired[-1] is b
+    assert len(W._ws_retired) == kept + 2
+    W._ws_cache.pop((dev.index, stream))
+    del W._ws_retired[kept:]
+
+
 def test_noalloc_rejects_before_device_work(L):
     def mm(M=4, K=64, N=8, ldx=64, ldw=64, ldo=8, azp=0, out_dtype=0, xq=FAKE, w=FAKE, out=FAKE):
         return L.w8a8_scaled_mm_int8_noalloc(xq, M, K, ldx, w, N, ldw, FAKE, 1, FAKE, 1, None, None, azp,
