@@ -5,7 +5,8 @@ fixed by its seed (the same cases on every run).
 
 * w8a8_scaled_mm_int8 (48 problems): M in [1, 700] (both the decode kernels and the MFMA
   tiles), K a multiple of 16 up to 2064, N up to 1600; int32 bit-exact, bf16
-  within the stated bar.
+  within the stated bar; and 36 more with K a multiple of 128 (or 64) on
+  the main decode kernels and MFMA tiles, up to 2599 x 8192 x 6499.
 * w8a8_quantize_act: every mode on ragged rows; codes, scales, zero points
   bit-exact.
 * w8a8_grouped_scaled_mm_int8: random expert counts (empty experts
@@ -53,6 +54,42 @@ def test_scaled_mm_random(seed):
         zin=int(rng.integers(-128, 128)),
     )
     note(f"random scaled_mm seed={seed} M={M} K={K} N={N} azp={azp} kernel={W.scaled_mm_kernel_name(M, N, K)}")
+    _run(d, azp, per_token=per_token, per_channel=per_channel, out_dtype=W.OUT_I32)
+    _run(d, azp, per_token=per_token, per_channel=per_channel, bias=bias)
+
+
+def _gemm_draw_main(seed):
+    """K a multiple of 128 (of 64 for some large problems), so the draws land
+    on the main kernels: decode (M <= 128, N up to 9000, K up to 8192),
+    middle (M 129-999) and large (M 1000-2599, N 2000-6499) problems."""
+    rng = np.random.default_rng(1500 + seed)
+    cls = seed % 3
+    if cls == 0:
+        M, K, N = int(rng.integers(1, 129)), int(rng.integers(1, 65)) * 128, int(rng.integers(1, 9000))
+    elif cls == 1:
+        M, K, N = int(rng.integers(129, 1000)), int(rng.integers(1, 33)) * 128, int(rng.integers(1, 3000))
+    else:
+        M, K, N = (int(rng.integers(1000, 2600)), int(rng.integers(1, 9)) * (128 if rng.random() < 0.7 else 64),
+                   int(rng.integers(2000, 6500)))
+    return M, K, N, rng
+
+
+@pytest.mark.parametrize("seed", range(36))
+def test_scaled_mm_random_main_kernels(seed):
+    M, K, N, rng = _gemm_draw_main(seed)
+    azp = int(rng.integers(0, 3))
+    per_token, per_channel, bias = bool(rng.integers(0, 2)), bool(rng.integers(0, 2)), bool(rng.integers(0, 2))
+    d = dict(
+        xq=rng.integers(-128, 128, (M, K), dtype=np.int8),
+        w=rng.integers(-128, 128, (N, K), dtype=np.int8),
+        sx=rng.uniform(1e-3, 5e-2, M).astype(np.float32),
+        sw=rng.uniform(1e-3, 1e-2, N).astype(np.float32),
+        zp=rng.integers(-128, 128, M).astype(np.int32),
+        bias=synth.bias_bits(rng, N),
+        zin=int(rng.integers(-128, 128)),
+    )
+    note(f"random scaled_mm (main kernels) seed={seed} M={M} K={K} N={N} azp={azp} "
+         f"kernel={W.scaled_mm_kernel_name(M, N, K)}")
     _run(d, azp, per_token=per_token, per_channel=per_channel, out_dtype=W.OUT_I32)
     _run(d, azp, per_token=per_token, per_channel=per_channel, bias=bias)
 
