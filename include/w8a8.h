@@ -465,8 +465,10 @@ const char* w8a8_scaled_mm_kernel_name(int64_t M, int64_t N, int64_t K);
  * invalid shape). No device is touched. */
 const char* w8a8_linear_dyn_sym_kernel_name(int64_t M, int64_t N, int64_t K);
 
-/* Human-readable name of a status code (static storage). */
-const char* w8a8_status_string(w8a8_status status);
+/* Human-readable name of a status code (static storage); any other value
+ * gives "W8A8_UNKNOWN_STATUS". The code is taken as a plain integer, so a
+ * value outside the enumeration is well defined. */
+const char* w8a8_status_string(int32_t status);
 
 /* Message of the last failed call on this host thread ("" if none). */
 const char* w8a8_last_error(void);

@@ -787,7 +787,7 @@ const char* w8a8_scaled_mm_kernel_name(int64_t M, int64_t N, int64_t K) {
   return (M <= w8a8::kDecodeMaxM) ? w8a8::decode_kernel_name(M, N, K, w8a8::decode_workspace_bytes(M, N, K)) : w8a8::scaled_mm_kernel_name(M, N, K);
 }
 
-const char* w8a8_status_string(w8a8_status s) {
+const char* w8a8_status_string(int32_t s) {
   switch (s) {
     case W8A8_OK: return "W8A8_OK";
     case W8A8_ERR_INVALID_ARG: return "W8A8_ERR_INVALID_ARG";
